@@ -1,0 +1,258 @@
+/*
+ * pagedkv.h -- C ABI of the paged-KV decode library for AMD MI355X (gfx950).
+ *
+ * The operations follow the pages that describe PagedAttention:
+ *  - the KV cache lives in fixed-size physical blocks of B tokens held in one
+ *    pool shared by all requests, reached through a per-request block table
+ *    (ithome article 10417389, section 3 "PagedAttention"; ultralytics glossary
+ *    "PagedAttention", section "How paging works"; optiverse-tech blog
+ *    "paged-kv-cache", section "Block table and non-contiguous allocation");
+ *  - a new token's key/value is written to pool[table[pos / B], pos % B]
+ *    (glossary code example);
+ *  - the attention kernel reads keys and values back block by block through
+ *    the table (glossary, "How paging works"; optiverse, same section);
+ *  - shared blocks are reference counted and copied on write (ithome,
+ *    section 4, "Physical block sharing" and "Copy-on-Write").
+ *
+ * Conventions for every device call
+ *  - All device pointers are caller-owned (torch tensors on ROCm in the Python
+ *    binding).  The library allocates no device memory and keeps no pointer
+ *    after a call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *    and return PKV_OK or a negative pkv_status.  Arguments are validated on
+ *    the host before anything is launched; on error nothing is launched and
+ *    pkv_last_error() describes the failure.
+ *  - Device data is trusted only as far as memory safety: block ids and slots
+ *    outside the pool are skipped by the kernels (never read or written), but
+ *    the result for such entries is unspecified.
+ *  - Device pointers must be 16-byte aligned.
+ *
+ * Pool layout (one layer), num_blocks = N, num_kv_heads = H, block_size = B,
+ * head_dim = D, element type = kv_dtype:
+ *    key pool   [N][H][B][D]   a token's key for one head is a contiguous row
+ *    value pool [N][H][D][B]   within a block, values are dimension-major
+ * The value layout puts the B tokens of one dimension next to each other so
+ * that the P.V product of the decode kernel reads its matrix-core operand with
+ * one 16-byte load per lane.
+ *
+ * fp8 (PKV_FP8_E4M3) is OCP FP8 E4M3FN.  A stored code c of a pool with scale
+ * s stands for e4m3(c) * s; reshape_and_cache encodes x as
+ * round_nearest_even_saturating(fp32(x) / fp32(s)) (NaN -> 0x7F, sign kept).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_E_INVAL = -1,        /* bad argument or shape */
+  PKV_E_NOMEM = -2,        /* block manager: not enough free blocks (state unchanged) */
+  PKV_E_UNSUPPORTED = -3,  /* valid but not built: dtype / head_dim / block_size combination */
+  PKV_E_HIP = -4           /* a HIP runtime call failed */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* One layer's K and V pools (layouts above). */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;     /* 8, 16 or 32 */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t kv_dtype;       /* pkv_dtype */
+  float k_scale;          /* fp8 only; must be 1.0f for f32 / bf16 pools */
+  float v_scale;
+} pkv_cache_desc;
+
+/* ------------------------------------------------------------------ device calls */
+
+/*
+ * reshape_and_cache -- write new tokens' keys and values into their slots.
+ * Glossary code example: key_pool[block_table[pos // B], pos % B] = key.
+ *
+ *   k, v          device [num_tokens][H][D] of in_dtype (f32 for an f32 pool;
+ *                 bf16 for a bf16 pool; bf16 or f32 for an fp8 pool, encoded
+ *                 with the pool's k_scale / v_scale)
+ *   slot_mapping  device int64 [num_tokens]; slot = block * B + position;
+ *                 a negative slot skips the token
+ *   k_pool/v_pool device pools described by *c
+ * Slots of one call must be distinct (two writes to one slot race).
+ * Bytes of the pools outside the written slots are unchanged.
+ */
+int pkv_reshape_and_cache(const void* k, const void* v, int32_t in_dtype,
+                          const int64_t* slot_mapping, int64_t num_tokens,
+                          void* k_pool, void* v_pool, const pkv_cache_desc* c,
+                          void* stream);
+
+/*
+ * copy_blocks -- the copy of copy-on-write (ithome, section 4): for every
+ * (src, dst) pair, block dst of both pools becomes a bit copy of block src
+ * (all heads, all B positions).
+ *   src_dst_pairs device int64 [num_pairs][2]
+ * Pairs must have src != dst, distinct dst, and no dst that is also a src, so
+ * their order does not matter (the Python binding checks this on the host;
+ * the library cannot see device data).  num_pairs == 0 launches nothing.
+ */
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
+                    int64_t num_pairs, const pkv_cache_desc* c, void* stream);
+
+/*
+ * Bytes of workspace pkv_paged_attn_decode needs to split every context into
+ * partitions of `partition_size` tokens (0 bytes when partition_size == 0 or a
+ * single partition covers max_context_len).
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_attn_decode -- one new query per sequence attends over its cached
+ * context through its block table (glossary "How paging works"; optiverse
+ * "Block table and non-contiguous allocation"); query heads share KV heads in
+ * contiguous groups of num_q_heads / num_kv_heads (grouped-query attention,
+ * glossary "Related techniques").
+ *
+ *   q             device [num_seqs][num_q_heads][D] of q_dtype (f32 with an
+ *                 f32 pool, bf16 with bf16 / fp8 pools)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(ctx / B) are never read
+ *   context_lens  device int32 [num_seqs]; tokens 0..ctx-1, including the one
+ *                 being decoded (written by reshape_and_cache beforehand);
+ *                 ctx == 0 gives zeros
+ *   scale         softmax scale applied to q.k (e.g. 1/sqrt(D))
+ *   out           device [num_seqs][num_q_heads][D] of q_dtype
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid
+ *                 without reading device data); larger contexts are cut at it
+ *   partition_size   0 = one pass over each context; otherwise a multiple of
+ *                 B: each context is split into partitions of that many tokens
+ *                 which run in parallel and are merged by a second kernel
+ *   workspace     device buffer of >= pkv_decode_workspace_bytes(...) bytes
+ *                 (may be NULL when that is 0)
+ * The result does not depend on partition_size beyond rounding; for a given
+ * partition_size it depends only on the logical order of the context, not on
+ * where blocks sit in the pool or on what unused slots hold.
+ */
+int pkv_paged_attn_decode(const void* q, int32_t q_dtype,
+                          const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, void* out,
+                          int32_t max_context_len, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode kernel families, for tests and benchmarks that pin one. */
+typedef enum {
+  PKV_IMPL_AUTO = 0,     /* matrix-core kernel where built, else the vector kernel */
+  PKV_IMPL_VECTOR = 1,   /* plain vector-ALU kernel: every dtype, fp32 arithmetic */
+  PKV_IMPL_MFMA = 2      /* bf16 / fp8 pools: QK^T and P.V on MFMA, group size <= 16 */
+} pkv_decode_impl;
+
+/* pkv_paged_attn_decode with an explicit kernel family (PKV_E_UNSUPPORTED if not built). */
+int pkv_paged_attn_decode_ex(const void* q, int32_t q_dtype,
+                             const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, float scale, void* out,
+                             int32_t max_context_len, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             int32_t impl);
+
+/*
+ * The two phases of pkv_paged_attn_decode, for callers that time or schedule
+ * them apart (or merge partitions computed elsewhere).
+ *
+ * pkv_paged_attn_partials -- same arguments as pkv_paged_attn_decode_ex.
+ *   Sequences whose context fits one partition get their output written to
+ *   `out`; the others leave, per (sequence, q head, partition), the running
+ *   max (log2 units), running sum and normalised partial output in
+ *   `workspace` for pkv_paged_attn_merge.
+ * pkv_paged_attn_merge -- combines the partitions of every sequence that has
+ *   more than one: out = sum_p w_p o_p / sum_p w_p with
+ *   w_p = l_p * 2^(m_p - max m), the rescaling of the running softmax
+ *   (FlashAttention-style tiling, glossary "Related techniques").  Arguments
+ *   must match the partials call; nothing is launched when no context was
+ *   split.
+ */
+int pkv_paged_attn_partials(const void* q, int32_t q_dtype,
+                            const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_q_heads, float scale, void* out,
+                            int32_t max_context_len, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            int32_t impl);
+int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                         int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                         void* out, void* stream);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------ host block manager
+ *
+ * Refcounted block allocator (ithome sections 3-4; glossary "How paging works"
+ * and "Sharing blocks between sequences"; optiverse "Block table ...").
+ *  - Blocks are taken from the head of the free list (glossary code example,
+ *    free_blocks.pop(0)), a new one only when the last block is full.
+ *  - fork shares every block of the parent (count + 1).
+ *  - append to a sequence whose last block is shared and partly filled takes a
+ *    new block, reports the (old, new) pair to copy, and drops the old block's
+ *    count; full shared blocks stay shared.
+ *  - free_seq drops one count per block; blocks reaching 0 are appended to the
+ *    tail of the free list in the sequence's logical order.
+ *  - Every operation is all-or-nothing: PKV_E_NOMEM / PKV_E_INVAL leave the
+ *    state unchanged.
+ * Not thread-safe: one owner thread per manager.
+ */
+typedef struct pkv_bm pkv_bm;
+
+typedef struct {
+  int32_t free_blocks, used_blocks;
+  int64_t tokens, slots_allocated, logical_blocks, physical_blocks;
+} pkv_bm_stats_t;
+
+/* free_order: the initial free list, head first (distinct ids in [0, num_blocks);
+ * blocks not listed are held elsewhere); NULL = 0..num_blocks-1.  NULL on error. */
+pkv_bm* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                      int32_t free_count);
+void pkv_bm_destroy(pkv_bm* bm);
+/* admit seq holding num_tokens tokens: ceil(num_tokens / B) blocks */
+int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int64_t num_tokens);
+int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
+/* slot of the next token; *cow_src / *cow_dst = the copy pair or -1 */
+int pkv_bm_append(pkv_bm* bm, int64_t seq, int64_t* slot, int64_t* cow_src, int64_t* cow_dst);
+/* one token for each of n distinct sequences, in the order given (pass ascending ids);
+ * slots[n]; pairs[2 * n] receives *num_pairs (src, dst) pairs */
+int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots,
+                        int64_t* pairs, int32_t* num_pairs);
+/* n tokens for one sequence: slots[n]; at most one copy pair (the first token) */
+int pkv_bm_extend(pkv_bm* bm, int64_t seq, int64_t n, int64_t* slots, int64_t* cow_src,
+                  int64_t* cow_dst);
+int pkv_bm_free_seq(pkv_bm* bm, int64_t seq);
+/* slots of positions start .. start+n-1 (all < the sequence's length) */
+int pkv_bm_slots(pkv_bm* bm, int64_t seq, int64_t start_pos, int64_t n, int64_t* out);
+/* tables [n][max_blocks] (padding -1) and context lengths [n] of the listed sequences */
+int pkv_bm_block_tables(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables,
+                        int32_t max_blocks, int32_t* context_lens);
+int pkv_bm_stats(pkv_bm* bm, pkv_bm_stats_t* out);
+/* reference count of a block (-1 if out of range) */
+int32_t pkv_bm_refcount(pkv_bm* bm, int32_t block);
+/* number of tokens of seq (-1 if unknown) */
+int64_t pkv_bm_seq_len(pkv_bm* bm, int64_t seq);
+/* copy the free list (head first) into out[cap]; returns its length */
+int32_t pkv_bm_free_list(pkv_bm* bm, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

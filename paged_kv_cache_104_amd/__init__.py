@@ -1,0 +1,407 @@
+"""Python binding of libpagedkv: paged-KV decode for AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of ``libpagedkv.so`` (built in-tree by ``build_lib``); PyTorch provides device
+memory and the current stream.  Importing this package without the built
+library raises ImportError -- there is no CPU fallback.
+
+Device calls (see include/pagedkv.h for layouts and error behaviour):
+``reshape_and_cache``, ``copy_blocks``, ``paged_attn_decode``.
+Host block manager: ``BlockManager`` (refcounted free-list allocator with fork
+and copy-on-write).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_E_INVAL, PKV_E_NOMEM, PKV_E_UNSUPPORTED, PKV_E_HIP = 0, -1, -2, -3, -4
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+IMPL_AUTO, IMPL_VECTOR, IMPL_MFMA = 0, 1, 2
+DTYPES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pagedkv error {code}: {msg}")
+        self.code = code
+
+
+class NoMemory(PagedKVError):
+    """The block manager has too few free blocks; its state is unchanged."""
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+class BmStats(ctypes.Structure):
+    _fields_ = [("free_blocks", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
+                ("tokens", ctypes.c_int64), ("slots_allocated", ctypes.c_int64),
+                ("logical_blocks", ctypes.c_int64), ("physical_blocks", ctypes.c_int64)]
+
+
+_i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                              ctypes.c_size_t)
+_pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "pkv_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i64, _vp, _vp,
+                                             ctypes.POINTER(CacheDesc), _vp]),
+    "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i64, ctypes.POINTER(CacheDesc), _vp]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp,
+                                             _i32, _vp, _i32, _i32, _f32, _vp, _i32, _i32, _vp,
+                                             _sz, _vp]),
+    "pkv_paged_attn_decode_ex": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
+                                                _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
+                                                _i32, _vp, _sz, _vp, _i32]),
+    "pkv_paged_attn_partials": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
+                                               _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
+                                               _i32, _vp, _sz, _vp, _i32]),
+    "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                            _vp, _vp]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_add_seq": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pkv_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pkv_bm_append": (ctypes.c_int, [_vp, _i64, _pi64, _pi64, _pi64]),
+    "pkv_bm_append_batch": (ctypes.c_int, [_vp, _pi64, _i32, _pi64, _pi64, _pi32]),
+    "pkv_bm_extend": (ctypes.c_int, [_vp, _i64, _i64, _pi64, _pi64, _pi64]),
+    "pkv_bm_free_seq": (ctypes.c_int, [_vp, _i64]),
+    "pkv_bm_slots": (ctypes.c_int, [_vp, _i64, _i64, _i64, _pi64]),
+    "pkv_bm_block_tables": (ctypes.c_int, [_vp, _pi64, _i32, _pi32, _i32, _pi32]),
+    "pkv_bm_stats": (ctypes.c_int, [_vp, ctypes.POINTER(BmStats)]),
+    "pkv_bm_refcount": (_i32, [_vp, _i32]),
+    "pkv_bm_seq_len": (_i64, [_vp, _i64]),
+    "pkv_bm_free_list": (_i32, [_vp, _pi32, _i32]),
+}
+
+
+def _load():
+    # torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading torch
+    # first makes this library bind to that same runtime instead of bringing a
+    # second copy into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python paged_kv_cache_104_amd/build_lib.py` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} lacks {name}: it is stale, rebuild it with "
+                              "`python paged_kv_cache_104_amd/build_lib.py`")
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != PKV_OK:
+        msg = lib.pkv_last_error().decode(errors="replace")
+        if rc == PKV_E_NOMEM:
+            raise NoMemory(rc, msg)
+        raise PagedKVError(rc, msg)
+
+
+def version() -> str:
+    return lib.pkv_version().decode()
+
+
+# ---------------------------------------------------------------------------- device side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def cache_desc(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+               kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> CacheDesc:
+    return CacheDesc(num_blocks, num_kv_heads, block_size, head_dim, DTYPES[kv_dtype],
+                     k_scale, v_scale)
+
+
+def pool_shapes(desc: CacheDesc) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """(key pool shape [N, H, B, D], value pool shape [N, H, D, B])."""
+    N, H, B, D = desc.num_blocks, desc.num_kv_heads, desc.block_size, desc.head_dim
+    return (N, H, B, D), (N, H, D, B)
+
+
+def alloc_pools(desc: CacheDesc, device="cuda", poison: bool = True):
+    """Allocate one layer's K and V pools (torch tensors); unused slots hold NaN patterns."""
+    torch = _torch()
+    tdt = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}[desc.kv_dtype]
+    ks, vs = pool_shapes(desc)
+    k = torch.empty(ks, dtype=tdt, device=device)
+    v = torch.empty(vs, dtype=tdt, device=device)
+    if poison:
+        if desc.kv_dtype == PKV_FP8_E4M3:
+            k.fill_(0x7F)
+            v.fill_(0x7F)
+        else:
+            k.fill_(float("nan"))
+            v.fill_(float("nan"))
+    return k, v
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+def _check_pool(t, shape, desc: CacheDesc, what: str) -> None:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} shape {tuple(t.shape)} != {tuple(shape)}")
+    if dtype_code(t) != desc.kv_dtype:
+        raise ValueError(f"{what} dtype {t.dtype} does not match the descriptor")
+
+
+def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, desc: CacheDesc, stream=None) -> None:
+    """Write new tokens' K, V ([T, H, D]) to slots ``slot_mapping`` (int64 [T]; <0 skips)."""
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    T = int(slot_mapping.numel())
+    if tuple(k.shape) != (T, desc.num_kv_heads, desc.head_dim) or k.shape != v.shape:
+        raise ValueError(f"k/v must be [{T}, {desc.num_kv_heads}, {desc.head_dim}]")
+    if not (k.is_contiguous() and v.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("k, v and slot_mapping must be contiguous")
+    if slot_mapping.dtype != _torch().int64 or not slot_mapping.is_cuda:
+        raise ValueError("slot_mapping must be a device int64 tensor")
+    _check(lib.pkv_reshape_and_cache(_ptr(k), _ptr(v), dtype_code(k), _ptr(slot_mapping), T,
+                                     _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+                                     _stream(stream)))
+
+
+def check_pairs(pairs: np.ndarray, num_blocks: int) -> np.ndarray:
+    """Host check of copy pairs: in range, src != dst, distinct dst, no dst that is a src."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if ((pairs < 0) | (pairs >= num_blocks)).any():
+        raise ValueError("copy pair block id out of range")
+    src, dst = pairs[:, 0], pairs[:, 1]
+    if (src == dst).any():
+        raise ValueError("copy pair with src == dst")
+    if len(np.unique(dst)) != len(dst):
+        raise ValueError("two copy pairs share a destination")
+    if np.intersect1d(src, dst).size:
+        raise ValueError("a copy destination is also a source")
+    return pairs
+
+
+def copy_blocks(k_pool, v_pool, pairs, desc: CacheDesc, stream=None) -> None:
+    """Copy-on-write copies: block dst of both pools becomes block src.
+
+    ``pairs`` on the host (list / numpy / CPU tensor, [n, 2]) is checked and
+    uploaded; a device int64 tensor is passed as is (the caller vouches for it).
+    """
+    torch = _torch()
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    if isinstance(pairs, torch.Tensor) and pairs.is_cuda:
+        dev = pairs.contiguous()
+        if dev.dtype != torch.int64:
+            raise ValueError("device pairs must be int64")
+    else:
+        host = pairs.cpu().numpy() if isinstance(pairs, torch.Tensor) else pairs
+        host = check_pairs(host, desc.num_blocks)
+        if len(host) == 0:
+            return
+        dev = torch.from_numpy(host).to(k_pool.device, non_blocking=False)
+    n = int(dev.numel() // 2)
+    if n == 0:
+        return
+    _check(lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(dev), n, ctypes.byref(desc),
+                               _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                           max_context_len: int, partition_size: int) -> int:
+    return int(lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                              partition_size))
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                      desc: CacheDesc, max_context_len: int, partition_size: int = 0,
+                      workspace=None, impl: int = IMPL_AUTO, stream=None):
+    """Decode attention: q [S, Hq, D] over each sequence's paged context -> out [S, Hq, D]."""
+    torch = _torch()
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    S, Hq, D = q.shape
+    if D != desc.head_dim or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("q / out shapes or dtypes do not match")
+    if not (q.is_contiguous() and out.is_contiguous() and block_tables.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("q, out, block_tables and context_lens must be contiguous")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else 0
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib.pkv_paged_attn_decode_ex(
+        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+        float(scale), _ptr(out), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+        _stream(stream), int(impl)))
+    return out
+
+
+def paged_attn_partials(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                        desc: CacheDesc, max_context_len: int, partition_size: int, workspace,
+                        impl: int = IMPL_AUTO, stream=None):
+    """First phase of paged_attn_decode (the per-partition kernel); see include/pagedkv.h."""
+    S, Hq, D = q.shape
+    ws_ptr = _ptr(workspace) if workspace is not None else 0
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib.pkv_paged_attn_partials(
+        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+        float(scale), _ptr(out), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+        _stream(stream), int(impl)))
+
+
+def paged_attn_merge(out, context_lens, max_context_len: int, partition_size: int, workspace,
+                     stream=None):
+    """Second phase of paged_attn_decode: merge split contexts into ``out``."""
+    S, Hq, D = out.shape
+    ws_ptr = _ptr(workspace) if workspace is not None else 0
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib.pkv_paged_attn_merge(dtype_code(out), _ptr(context_lens), S, Hq, D,
+                                    int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+                                    _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- host side
+
+def _np_ptr(a: np.ndarray, typ):
+    return a.ctypes.data_as(ctypes.POINTER(typ))
+
+
+class BlockManager:
+    """Refcounted block allocator (C++): free list, block tables, fork, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        if free_order is None:
+            h = lib.pkv_bm_create(num_blocks, block_size, None, 0)
+        else:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            h = lib.pkv_bm_create(num_blocks, block_size, _np_ptr(fo, ctypes.c_int32), len(fo))
+        if not h:
+            raise PagedKVError(PKV_E_INVAL, lib.pkv_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.pkv_bm_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq: int, num_tokens: int) -> None:
+        _check(lib.pkv_bm_add_seq(self._h, seq, num_tokens))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib.pkv_bm_fork(self._h, parent, child))
+
+    def append(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.pkv_bm_append(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
+                                 ctypes.byref(dst)))
+        return slot.value, ((src.value, dst.value) if src.value >= 0 else None)
+
+    def append_batch(self, seqs: Iterable[int]) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        slots = np.empty(len(s), dtype=np.int64)
+        pairs = np.empty((max(1, len(s)), 2), dtype=np.int64)
+        n = ctypes.c_int32()
+        _check(lib.pkv_bm_append_batch(self._h, _np_ptr(s, ctypes.c_int64), len(s),
+                                       _np_ptr(slots, ctypes.c_int64),
+                                       _np_ptr(pairs, ctypes.c_int64), ctypes.byref(n)))
+        return slots, pairs[: n.value].copy()
+
+    def extend(self, seq: int, n: int) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        slots = np.empty(max(1, n), dtype=np.int64)
+        src, dst = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.pkv_bm_extend(self._h, seq, n, _np_ptr(slots, ctypes.c_int64),
+                                 ctypes.byref(src), ctypes.byref(dst)))
+        return slots[:n].copy(), ([(src.value, dst.value)] if src.value >= 0 else [])
+
+    def free_seq(self, seq: int) -> None:
+        _check(lib.pkv_bm_free_seq(self._h, seq))
+
+    def slots(self, seq: int, start: int, n: int) -> np.ndarray:
+        out = np.empty(max(1, n), dtype=np.int64)
+        _check(lib.pkv_bm_slots(self._h, seq, start, n, _np_ptr(out, ctypes.c_int64)))
+        return out[:n].copy()
+
+    def block_tables(self, seqs: Sequence[int], max_blocks: int,
+                     out_tables: Optional[np.ndarray] = None,
+                     out_lens: Optional[np.ndarray] = None):
+        s = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        tables = out_tables if out_tables is not None else np.empty((len(s), max_blocks), np.int32)
+        lens = out_lens if out_lens is not None else np.empty(len(s), np.int32)
+        _check(lib.pkv_bm_block_tables(self._h, _np_ptr(s, ctypes.c_int64), len(s),
+                                       _np_ptr(tables, ctypes.c_int32), max_blocks,
+                                       _np_ptr(lens, ctypes.c_int32)))
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = BmStats()
+        _check(lib.pkv_bm_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in BmStats._fields_}
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pkv_bm_refcount(self._h, block))
+
+    def seq_len(self, seq: int) -> int:
+        return int(lib.pkv_bm_seq_len(self._h, seq))
+
+    def free_list(self) -> List[int]:
+        n = lib.pkv_bm_free_list(self._h, None, 0)
+        out = np.empty(max(1, n), dtype=np.int32)
+        lib.pkv_bm_free_list(self._h, _np_ptr(out, ctypes.c_int32), n)
+        return out[:n].tolist()

@@ -1,0 +1,74 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+Usage: python paged_kv_cache_104_amd/build_lib.py [--jobs N]
+(run it as a script: importing the package would load the library being rebuilt)
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libpagedkv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["errors.cpp", "block_manager.cpp", "cache_ops.hip", "decode.hip"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
+          "-Wno-unused-result"]
+# device code: never emit packed-fp32 instructions (v_pk_*_f32)
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fno-gpu-rdc"]
+
+
+def _obj(src: str) -> str:
+    return os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+
+
+def compile_one(src: str) -> str:
+    path = os.path.join(CSRC, src)
+    out = _obj(src)
+    cmd = [HIPCC] + COMMON
+    if src.endswith(".hip"):
+        cmd += HIP_FLAGS + ["-x", "hip"]
+    else:
+        cmd += ["-x", "c++"]
+    cmd += ["-c", path, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stderr or "").splitlines() if noise not in ln and ln.strip()]
+    if msgs:
+        sys.stderr.write("\n".join(msgs) + "\n")
+    return out
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=4)
+    args = ap.parse_args()
+    build(args.jobs, verbose=True)

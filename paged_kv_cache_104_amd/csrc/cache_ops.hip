@@ -1,0 +1,181 @@
+// Cache operations: the write of new tokens into their (block, slot) and the
+// whole-block copy of copy-on-write.
+//
+// reshape_and_cache follows the ultralytics glossary code example
+// (key_pool[block_table[pos // B], pos % B] = key): slot = block * B + pos.
+// copy_blocks is the copy step of copy-on-write (ithome article 10417389,
+// section 4): the writer's new block receives the whole shared block.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+// One workgroup per token; each thread moves 8 consecutive dimensions of one
+// head: 16 B (bf16) or 32 B (f32) in, a contiguous row segment of the key
+// pool out, and 8 scattered elements of the dimension-major value block.
+template <int KV, typename In>
+__global__ __launch_bounds__(128) void reshape_and_cache_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const int64_t* __restrict__ slots,
+    typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ v_pool,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_slots, float k_scale,
+    float v_scale) {
+  typedef typename KvTraits<KV>::T T;
+  const int64_t tok = blockIdx.x;
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;             // skip (negative) / never write outside
+  const int64_t blk = slot / block_size;
+  const int pos = int(slot - blk * block_size);
+  const int chunks = num_kv_heads * head_dim / 8;
+  const int64_t head_stride = int64_t(block_size) * head_dim;
+  for (int ch = threadIdx.x; ch < chunks; ch += blockDim.x) {
+    const int h = (ch * 8) / head_dim;
+    const int d0 = ch * 8 - h * head_dim;
+    const In* ks = k + tok * num_kv_heads * head_dim + ch * 8;
+    const In* vs = v + tok * num_kv_heads * head_dim + ch * 8;
+    float kf[8], vf[8];
+    if constexpr (sizeof(In) == 2) {
+      const uint4 ku = *reinterpret_cast<const uint4*>(ks);
+      const uint4 vu = *reinterpret_cast<const uint4*>(vs);
+      const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w}, vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kf[2 * i] = bf16_to_f32(kw[i] & 0xffffu);
+        kf[2 * i + 1] = bf16_to_f32(kw[i] >> 16);
+        vf[2 * i] = bf16_to_f32(vw[i] & 0xffffu);
+        vf[2 * i + 1] = bf16_to_f32(vw[i] >> 16);
+      }
+    } else {
+      const float4 k0 = reinterpret_cast<const float4*>(ks)[0];
+      const float4 k1 = reinterpret_cast<const float4*>(ks)[1];
+      const float4 v0 = reinterpret_cast<const float4*>(vs)[0];
+      const float4 v1 = reinterpret_cast<const float4*>(vs)[1];
+      kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
+      kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
+      vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
+      vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+    }
+    T* kd = k_pool + (blk * num_kv_heads + h) * head_stride + int64_t(pos) * head_dim + d0;
+    T* vd = v_pool + (blk * num_kv_heads + h) * head_stride + int64_t(d0) * block_size + pos;
+    if constexpr (KV == KV_FP8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_encode(__fdiv_rn(kf[i], k_scale)) << (8 * i);
+        hi |= e4m3_encode(__fdiv_rn(kf[i + 4], k_scale)) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vd[i * block_size] = uint8_t(e4m3_encode(__fdiv_rn(vf[i], v_scale)));
+    } else if constexpr (KV == KV_BF16) {
+      // bf16 input into a bf16 pool: the bits are copied unchanged
+      const uint4 ku = *reinterpret_cast<const uint4*>(ks);
+      const uint4 vu = *reinterpret_cast<const uint4*>(vs);
+      *reinterpret_cast<uint4*>(kd) = ku;
+      const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vd[(2 * i) * block_size] = uint16_t(vw[i] & 0xffffu);
+        vd[(2 * i + 1) * block_size] = uint16_t(vw[i] >> 16);
+      }
+    } else {
+      reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
+      reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vd[i * block_size] = vf[i];
+    }
+  }
+}
+
+// One workgroup per (pair, pool): 16-byte copies of a whole block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_pool,
+                                                          uint8_t* __restrict__ v_pool,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t block_bytes, int64_t num_blocks) {
+  const int64_t src = pairs[2 * int64_t(blockIdx.x)];
+  const int64_t dst = pairs[2 * int64_t(blockIdx.x) + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const uint4* s = reinterpret_cast<const uint4*>(pool + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(pool + dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int pkv_reshape_and_cache(const void* k, const void* v, int32_t in_dtype,
+                                     const int64_t* slot_mapping, int64_t num_tokens,
+                                     void* k_pool, void* v_pool, const pkv_cache_desc* c,
+                                     void* stream) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(PKV_E_INVAL, "negative num_tokens");
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return fail(PKV_E_INVAL, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(slot_mapping))
+    return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
+  if (num_tokens > 0x7fffffff) return fail(PKV_E_INVAL, "too many tokens for one call");
+  const bool ok = (c->kv_dtype == PKV_F32 && in_dtype == PKV_F32) ||
+                  (c->kv_dtype == PKV_BF16 && in_dtype == PKV_BF16) ||
+                  (c->kv_dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32));
+  if (!ok)
+    return fail(PKV_E_UNSUPPORTED, "%s input into a %s pool", dtype_name(in_dtype),
+                dtype_name(c->kv_dtype));
+  const int64_t num_slots = int64_t(c->num_blocks) * c->block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(num_tokens)), block(128);
+  const int H = c->num_kv_heads, D = c->head_dim, B = c->block_size;
+  if (c->kv_dtype == PKV_F32) {
+    reshape_and_cache_kernel<KV_F32, float><<<grid, block, 0, s>>>(
+        static_cast<const float*>(k), static_cast<const float*>(v), slot_mapping,
+        static_cast<float*>(k_pool), static_cast<float*>(v_pool), H, D, B, num_slots, 1.f, 1.f);
+  } else if (c->kv_dtype == PKV_BF16) {
+    reshape_and_cache_kernel<KV_BF16, uint16_t><<<grid, block, 0, s>>>(
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping,
+        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), H, D, B, num_slots, 1.f,
+        1.f);
+  } else if (in_dtype == PKV_BF16) {
+    reshape_and_cache_kernel<KV_FP8, uint16_t><<<grid, block, 0, s>>>(
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping,
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), H, D, B, num_slots,
+        c->k_scale, c->v_scale);
+  } else {
+    reshape_and_cache_kernel<KV_FP8, float><<<grid, block, 0, s>>>(
+        static_cast<const float*>(k), static_cast<const float*>(v), slot_mapping,
+        static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), H, D, B, num_slots,
+        c->k_scale, c->v_scale);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "reshape_and_cache launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
+                               int64_t num_pairs, const pkv_cache_desc* c, void* stream) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_pairs < 0) return fail(PKV_E_INVAL, "negative num_pairs");
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs) return fail(PKV_E_INVAL, "NULL pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_E_INVAL, "pools must be 16-byte aligned");
+  if (num_pairs > 0x7fffffff) return fail(PKV_E_INVAL, "too many pairs for one call");
+  const int64_t block_bytes =
+      int64_t(c->num_kv_heads) * c->block_size * c->head_dim * elem_bytes(c->kv_dtype);
+  const dim3 grid(static_cast<unsigned>(num_pairs), 2), block(256);
+  copy_blocks_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), src_dst_pairs, block_bytes,
+      c->num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}

@@ -1,0 +1,127 @@
+"""One layer's paged KV cache on the GPU: pools + block manager + decode step.
+
+The serving-engine side of the hot path, reduced to what one decode step
+needs: the C++ block manager decides block tables, slots and copy-on-write
+pairs on the host; the HIP kernels copy blocks, write new tokens and run the
+decode attention on the device.
+
+Allocator scripts are lists of operations:
+``('add', seq, n)``, ``('fork', parent, child)``, ``('extend', seq, n)``,
+``('append_batch', [seqs])``, ``('free', seq)``.  Copy-on-write pairs are
+copied on the device before any later token write, since the last holder of a
+shared block writes into it in place.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+from . import (IMPL_AUTO, BlockManager, CacheDesc, alloc_pools, copy_blocks,
+               decode_workspace_bytes, paged_attn_decode, reshape_and_cache)
+
+
+def to_device(x: np.ndarray, in_dtype: str, device):
+    """Host array in input format (float32, or bf16 bit patterns) -> device tensor."""
+    import torch
+
+    if in_dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device)
+
+
+class PagedKVCache:
+    def __init__(self, desc: CacheDesc, free_order: Optional[Sequence[int]] = None,
+                 device="cuda", poison: bool = True):
+        self.desc = desc
+        self.device = device
+        self.bm = BlockManager(desc.num_blocks, desc.block_size, free_order)
+        self.k_pool, self.v_pool = alloc_pools(desc, device, poison)
+
+    # -- device work ------------------------------------------------------------
+    def write(self, k, v, slots) -> None:
+        import torch
+
+        slot_t = torch.as_tensor(np.ascontiguousarray(slots, dtype=np.int64)).to(self.device)
+        reshape_and_cache(k, v, slot_t, self.k_pool, self.v_pool, self.desc)
+
+    def copy(self, pairs) -> None:
+        if len(pairs):
+            copy_blocks(self.k_pool, self.v_pool, np.asarray(pairs, dtype=np.int64), self.desc)
+
+    # -- allocator script ----------------------------------------------------
+    def run_script(self, ops, kv_input: Callable[[int], tuple], in_dtype: str,
+                   keep: Optional[Callable[[int], bool]] = None) -> None:
+        """Replay ``ops``; ``kv_input(seq)`` gives that sequence's (K, V) by position.
+
+        Token writes of sequences for which ``keep(seq)`` is false are skipped
+        (their blocks are still allocated).
+        """
+        keep = keep or (lambda s: True)
+        bm = self.bm
+
+        def put(seq, positions, slots):
+            if not keep(seq) or len(positions) == 0:
+                return
+            k, v = kv_input(seq)
+            self.write(to_device(k[positions], in_dtype, self.device),
+                       to_device(v[positions], in_dtype, self.device), slots)
+
+        for op in ops:
+            kind = op[0]
+            if kind == "add":
+                _, seq, n = op
+                bm.add_seq(seq, n)
+                if n:
+                    put(seq, np.arange(n), bm.slots(seq, 0, n))
+            elif kind == "fork":
+                bm.fork(op[1], op[2])
+            elif kind == "free":
+                bm.free_seq(op[1])
+            elif kind == "extend":
+                _, seq, n = op
+                start = bm.seq_len(seq)
+                slots, pairs = bm.extend(seq, n)
+                self.copy(pairs)
+                put(seq, np.arange(start, start + n), slots)
+            elif kind == "append_batch":
+                seqs = list(op[1])
+                starts = [bm.seq_len(s) for s in seqs]
+                slots, pairs = bm.append_batch(seqs)
+                self.copy(pairs)
+                for s, p, sl in zip(seqs, starts, slots):
+                    put(s, np.array([p]), np.array([sl]))
+            else:
+                raise ValueError(f"unknown op {kind}")
+
+    # -- decode step ---------------------------------------------------------
+    def append_and_write(self, seqs, k_new, v_new):
+        """Reserve one slot per sequence, copy shared partial blocks, write the new tokens.
+
+        Returns (slots, pairs) as host arrays.
+        """
+        slots, pairs = self.bm.append_batch(seqs)
+        self.copy(pairs)
+        self.write(k_new, v_new, slots)
+        return slots, pairs
+
+    def tables(self, seqs, max_blocks: int):
+        import torch
+
+        t, lens = self.bm.block_tables(seqs, max_blocks)
+        return torch.from_numpy(t).to(self.device), torch.from_numpy(lens).to(self.device)
+
+    def decode(self, q, out, tables, lens, scale: float, max_context_len: int,
+               partition_size: int = 0, workspace=None, impl: int = IMPL_AUTO):
+        return paged_attn_decode(q, self.k_pool, self.v_pool, tables, lens, scale, out, self.desc,
+                                 max_context_len, partition_size, workspace, impl)
+
+    def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
+                  partition_size: int):
+        import torch
+
+        n = decode_workspace_bytes(num_seqs, num_q_heads, self.desc.head_dim, max_context_len,
+                                   partition_size)
+        return torch.empty(max(n, 16), dtype=torch.uint8, device=self.device) if n else None

@@ -335,3 +335,70 @@ def random_small(seed: int, *, S: int, Hq: int, Hkv: int, D: int, B: int,
     return _plain(f"random-{seed}", seed, S, Hq, Hkv, D, B, ctx, kv_dtype, in_dtype,
                   partition_size, pool_blocks=N, free_order=free_order,
                   description="random small parity case")
+
+
+class KVFeeder:
+    """Serves ``wl.seq_kv_input`` for sequences in a known order, drawing ahead on threads.
+
+    numpy's generators release the GIL, so drawing several sequences at once
+    scales with the cores.  ``seq_order`` lists sequence ids in the order they
+    will be asked for; results stay available for a few further requests.
+    """
+
+    def __init__(self, wl: "Workload", seq_order, workers: int = 8, ahead: int = 16,
+                 keep: int = 8):
+        from collections import OrderedDict
+        from concurrent.futures import ThreadPoolExecutor
+
+        self.wl = wl
+        self.index = wl.seq_index()
+        seen, order = set(), []
+        for s in seq_order:
+            s = int(s)
+            if s in self.index and s not in seen:
+                seen.add(s)
+                order.append(self.index[s])
+        self.order = order
+        self.pos = 0
+        self.ahead = ahead
+        self.keep = keep
+        self.ex = ThreadPoolExecutor(max_workers=workers)
+        self.futs: Dict[int, object] = {}
+        self.done: "OrderedDict[int, Tuple[np.ndarray, np.ndarray]]" = OrderedDict()
+
+    def _fill(self):
+        while len(self.futs) < self.ahead and self.pos < len(self.order):
+            i = self.order[self.pos]
+            self.pos += 1
+            if i not in self.futs and i not in self.done:
+                self.futs[i] = self.ex.submit(self.wl.seq_kv_input, i)
+
+    def by_index(self, i: int):
+        if i in self.done:
+            self.done.move_to_end(i)
+            return self.done[i]
+        self._fill()
+        fut = self.futs.pop(i, None)
+        r = fut.result() if fut is not None else self.wl.seq_kv_input(i)
+        self.done[i] = r
+        while len(self.done) > self.keep:
+            self.done.popitem(last=False)
+        self._fill()
+        return r
+
+    def __call__(self, seq: int):
+        return self.by_index(self.index[int(seq)])
+
+    def close(self):
+        self.ex.shutdown(wait=False, cancel_futures=True)
+
+
+def ops_seq_order(ops) -> List[int]:
+    """Sequence ids in the order an allocator script first writes tokens for them."""
+    out = []
+    for op in ops:
+        if op[0] in ("add", "extend"):
+            out.append(int(op[1]))
+        elif op[0] == "append_batch":
+            out.extend(int(s) for s in op[1])
+    return out
