@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+One step is one pass of the whole hot path over the batch:
+  host   C++ block manager: append one token per sequence -> slots, copy pairs,
+         block tables (staged in pinned memory, uploaded asynchronously)
+  device copy_blocks (copy-on-write pairs, when there are any)
+         reshape_and_cache (the batch's new K/V into their slots)
+         paged attention: per-partition kernel + partition merge
+Inputs are resident in HBM before the timed region.  Contexts grow by one
+token per step, as in a real decode loop; the KV bytes of every step are
+counted from the block manager's lengths.
+
+Prints one JSON line.  `value` is the KV-read rate of the whole step
+(algorithmic KV bytes / wall time of the timed steps); the `roofline` object is
+the per-partition attention kernel alone, timed with HIP events on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import gc
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV-read GB/s (fraction of HBM peak) + decode tokens/s"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "8b-gqa-bf16"
+DOMINANT_KERNEL = "decode_mfma_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_104_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(config: str):
+    """HBM bytes per launch from committed counter runs, if taken on the current kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(config)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def build_gpu_state(wl, workers: int):
+    import torch
+
+    import workloads
+    from paged_kv_cache_104_amd.engine import PagedKVCache, to_device
+
+    import paged_kv_cache_104_amd as pkv
+
+    k_scale, v_scale = wl.kv_scales()
+    desc = pkv.cache_desc(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
+                          wl.kv_dtype, k_scale, v_scale)
+    cache = PagedKVCache(desc, wl.free_order, device="cuda", poison=True)
+    feeder = workloads.KVFeeder(wl, workloads.ops_seq_order(wl.setup_ops), workers=workers)
+    last = {int(s): int(c) - 1 for s, c in zip(wl.decode_seqs, wl.ctx_lens)}
+    rows = {}
+
+    def source(seq):
+        k, v = feeder(seq)
+        if seq not in rows:
+            rows[seq] = (k[last[seq]].copy(), v[last[seq]].copy())
+        return k, v
+
+    live = set(last)
+    try:
+        cache.run_script(wl.setup_ops, source, wl.in_dtype, keep=lambda s: s in live)
+        for s in wl.decode_seqs:
+            if int(s) not in rows:
+                source(int(s))
+    finally:
+        feeder.close()
+    seqs = [int(s) for s in wl.decode_seqs]
+    k_new = to_device(np.stack([rows[s][0] for s in seqs]), wl.in_dtype, "cuda")
+    v_new = to_device(np.stack([rows[s][1] for s in seqs]), wl.in_dtype, "cuda")
+    q = to_device(wl.q_input(), wl.in_dtype, "cuda")
+    torch.cuda.synchronize()
+    return cache, desc, seqs, q, k_new, v_new
+
+
+def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers: int):
+    import torch
+
+    import paged_kv_cache_104_amd as pkv
+
+    t_setup = time.perf_counter()
+    cache, desc, seqs, q, k_new, v_new = build_gpu_state(wl, workers)
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.num_seqs} seqs, "
+        f"{int(wl.ctx_lens.sum())} cached tokens, pool {wl.num_blocks} blocks")
+    S, B = len(seqs), wl.block_size
+    total = warmup + steps
+    max_ctx = wl.max_context_len + total
+    max_blocks = -(-max_ctx // B)
+    bytes_per_token = wl.kv_bytes_per_token()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    slots_h = [torch.empty(S, dtype=torch.int64, pin_memory=True) for _ in range(2)]
+    tables_h = [torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    lens_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    uploaded = [torch.cuda.Event() for _ in range(2)]
+    slots_d = torch.empty(S, dtype=torch.int64, device=dev)
+    tables_d = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty(S, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws_bytes = pkv.decode_workspace_bytes(S, wl.num_q_heads, wl.head_dim, max_ctx, partition_size)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    kv_bytes = np.zeros(total)
+    n_pairs = 0
+
+    def step(i):
+        nonlocal n_pairs
+        b = i % 2
+        uploaded[b].synchronize()                     # pinned buffer b is free again
+        slots, pairs = cache.bm.append_batch(seqs)
+        np.copyto(slots_h[b].numpy(), slots)
+        _, lens = cache.bm.block_tables(seqs, max_blocks, out_tables=tables_h[b].numpy(),
+                                        out_lens=lens_h[b].numpy())
+        kv_bytes[i] = float(lens.astype(np.int64).sum()) * bytes_per_token
+        slots_d.copy_(slots_h[b], non_blocking=True)
+        tables_d.copy_(tables_h[b], non_blocking=True)
+        lens_d.copy_(lens_h[b], non_blocking=True)
+        uploaded[b].record(stream)
+        e = ev[i]
+        e[0].record(stream)
+        if len(pairs):
+            n_pairs += len(pairs)
+            pkv.copy_blocks(cache.k_pool, cache.v_pool, pairs, desc)
+        pkv.reshape_and_cache(k_new, v_new, slots_d, cache.k_pool, cache.v_pool, desc)
+        e[1].record(stream)
+        pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, tables_d, lens_d, wl.scale, out,
+                                desc, max_ctx, partition_size, workspace, impl)
+        e[2].record(stream)
+        pkv.paged_attn_merge(out, lens_d, max_ctx, partition_size, workspace)
+        e[3].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()                      # no collector pauses inside the timed steps
+    t0 = time.perf_counter()
+    for i in range(warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gc.enable()
+    timed = range(warmup, total)
+    t_write = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed]) * 1e-3
+    t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed]) * 1e-3
+    t_merge = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in timed]) * 1e-3
+    kvb = kv_bytes[warmup:]
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    return dict(wall=wall, kv_bytes=kvb, t_write=t_write, t_attn=t_attn, t_merge=t_merge,
+                max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the workload's sequences."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import allocator as oalloc
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    from oracle import codec
+
+    k_scale, v_scale = wl.kv_scales()
+    q = wl.q_input()
+    q64 = codec.bf16_to_f64(q) if wl.in_dtype == "bf16" else q.astype(np.float64)
+    done_bytes, done_tokens, spent, n = 0.0, 0, 0.0, 0
+    for i in range(wl.num_seqs):
+        ctx = int(wl.ctx_lens[i])
+        nb = -(-ctx // wl.block_size)
+        a = oalloc.BlockAllocator(nb, wl.block_size)
+        a.add_seq(0, ctx)
+        kp, vp = ocache.new_pools(nb, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.kv_dtype)
+        k, v = wl.seq_kv_input(i)
+        ocache.reshape_and_cache(kp, vp, k, v, a.slots(0, 0, ctx), wl.in_dtype, wl.kv_dtype,
+                                 k_scale, v_scale)
+        tables, lens = a.block_tables([0], nb)
+        t = time.perf_counter()
+        oattn.paged_decode(q64[i:i + 1], kp, vp, tables, lens, wl.scale, wl.kv_dtype,
+                           k_scale, v_scale)
+        spent += time.perf_counter() - t
+        done_bytes += ctx * wl.kv_bytes_per_token()
+        done_tokens += 1
+        n += 1
+        if spent >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": done_bytes / spent / 1e9, "unit": "GB/s",
+        "tokens_per_s": done_tokens / spent, "cores": int(threads), "kind": "oracle",
+        "sample": f"first {n} of {wl.num_seqs} sequences of {wl.name} "
+                  f"({int(sum(wl.ctx_lens[:n]))} cached tokens), decode attention only, "
+                  f"{spent:.1f}s of CPU time, numpy float64 with {threads} BLAS thread(s)",
+    }
+
+
+def copy_calibration(n_bytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling HBM counters (rocprofv3 --pmc)."""
+    import torch
+
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n_bytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 vector, 2 mfma")
+    ap.add_argument("--workers", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this paged-KV build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 10)
+        return 0
+
+    import torch
+
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = workloads.get(args.config)
+    wl.cache_sequences = True          # keep the drawn inputs for the oracle's sample
+    ps = wl.partition_size if args.partition_size is None else args.partition_size
+    r = run_gpu(wl, args.steps, args.warmup, ps, args.impl, args.workers)
+    wall = r["wall"]
+    total_bytes = float(r["kv_bytes"].sum())
+    value = total_bytes / wall / 1e9
+    attn_gbs = float((r["kv_bytes"] / r["t_attn"]).mean()) / 1e9
+    mean_ctx = float(r["kv_bytes"].mean()) / wl.kv_bytes_per_token() / wl.num_seqs
+    traffic = measured_traffic(args.config)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+            "mean_context": round(mean_ctx, 1), "partition_size": ps,
+            "description": wl.description,
+        },
+        "decode_tokens_per_s": round(wl.num_seqs * args.steps / wall, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": {
+            "reshape_and_cache+copy_blocks": round(float(r["t_write"].mean()) * 1e3, 4),
+            "attention_partials": round(float(r["t_attn"].mean()) * 1e3, 4),
+            "attention_merge": round(float(r["t_merge"].mean()) * 1e3, 4),
+        },
+        "roofline": {
+            "kernel": DOMINANT_KERNEL,
+            "bound": "hbm",
+            "achieved": round(attn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(r["kv_bytes"].mean()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -203,16 +203,15 @@ __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a
 // Per-lane registers of one 32-token step.
 template <int KV, int D>
 struct StepRegs {
-  // K rows (MFMA A operand of Q.K^T): two 16-token tiles, D/32 k-steps each
-  uint4 ka[KV == KV_FP8 ? D / 64 : D / 32];
-  uint4 kb[KV == KV_FP8 ? D / 64 : D / 32];
-  // V^T (MFMA A operand of P.V): D/16 tiles of 8 tokens x 1 dimension per lane
-  typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];
+  static constexpr int NK = KV == KV_FP8 ? D / 64 : D / 32;  // 16-byte K loads per tile
+  uint4 ka[NK];   // K rows, tile a (MFMA A operand of Q.K^T)
+  uint4 kb[NK];   // K rows, tile b
+  typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];  // V^T, 8 tokens x 1 dim
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Two fp8 codes (low or high half of w) -> two bf16 (exact: e4m3 fits in bf16).
+// Two fp8 codes (low or high half of w) -> two bf16 (exact: every e4m3 value is a bf16).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t,
@@ -224,6 +223,12 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 w) {
                     fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 // Start dimension of the 8 dimensions lane group r feeds into k-step i of Q.K^T.
 // bf16: one 16-byte load per k-step, the 4 lane groups read 64 contiguous bytes.
 // fp8: one 16-byte load covers two k-steps.
@@ -233,52 +238,76 @@ __device__ __forceinline__ int qk_dim0(int i, int r) {
   else return 32 * i + 8 * r;
 }
 
+// Lane-constant parts of the step addresses.  A step covers tokens tt .. tt+31
+// (tt is a multiple of BS); lane (r, c) reads
+//   K tile a: token ka_tok = 8*(c>>2) + (c&3), tile b: ka_tok + 4, dimensions qk_dim0(., r)
+//   V^T:      tokens 8r .. 8r+7 of dimension 16*j + c
 template <int KV, int D, int BS>
-__device__ __forceinline__ void load_step(StepRegs<KV, D>& R, const DecodeArgs& a,
-                                          const int32_t* table, int kvh, int tt, int t1, int r,
-                                          int c) {
-  typedef typename KvTraits<KV>::T T;
-  const T* kp = static_cast<const T*>(a.k_pool);
-  const T* vp = static_cast<const T*>(a.v_pool);
-  constexpr int64_t head_stride = int64_t(BS) * D;
-  const int64_t kvh_off = int64_t(kvh) * head_stride;
-  const int64_t blk_stride = int64_t(a.num_kv_heads) * head_stride;
-  // K rows: tile a row c holds token 8*(c>>2) + (c&3) of the step, tile b the token 4 later
-  const int ta = 8 * (c >> 2) + (c & 3);
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    const int tok = tt + ta + 4 * tile;
-    const int pb = tok < t1 ? table[tok / BS] : -1;
-    const bool ok = pb >= 0 && pb < a.num_blocks;
-    const T* row = kp + int64_t(pb) * blk_stride + kvh_off + int64_t(tok % BS) * D;
-    uint4* dst = tile == 0 ? R.ka : R.kb;
-    constexpr int NL = KV == KV_FP8 ? D / 64 : D / 32;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int d0 = KV == KV_FP8 ? qk_dim0<KV>(2 * i, r) : qk_dim0<KV>(i, r);
-      dst[i] = ok ? *reinterpret_cast<const uint4*>(row + d0) : make_uint4(0, 0, 0, 0);
-    }
+struct LaneMap {
+  int ka_blk, kb_blk, v_blk;    // which of the step's 32/BS blocks
+  int64_t ka_off, kb_off, v_off;  // element offset inside a (block, head) tile
+  __device__ LaneMap(int r, int c) {
+    const int ta = 8 * (c >> 2) + (c & 3), tb = ta + 4, tv = 8 * r;
+    ka_blk = ta / BS;
+    kb_blk = tb / BS;
+    v_blk = tv / BS;
+    ka_off = int64_t(ta % BS) * D + qk_dim0<KV>(0, r);
+    kb_off = int64_t(tb % BS) * D + qk_dim0<KV>(0, r);
+    v_off = int64_t(c) * BS + (tv % BS);
   }
-  // V^T: lane group r reads tokens 8r .. 8r+7 of the step, dimension 16*j + c
-  const int tv = tt + 8 * r;
-  const int pbv = tv < t1 ? table[tv / BS] : -1;
-  const bool okv = pbv >= 0 && pbv < a.num_blocks;
-  const T* vb = vp + int64_t(pbv) * blk_stride + kvh_off + (tv % BS);
+};
+
+template <int BS>
+__device__ __forceinline__ int pick_block(const int (&pbs)[32 / BS], int which) {
+  int pb = pbs[0];
+#pragma unroll
+  for (int b = 1; b < 32 / BS; ++b) pb = which == b ? pbs[b] : pb;
+  return pb;
+}
+
+// Issue the loads of one step.  Block ids outside the pool (and blocks past the
+// context, whose tokens are masked later) read block 0 instead, so every load is
+// in bounds and no lane branches.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void load_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
+                                          const typename KvTraits<KV>::T* vp,
+                                          const int32_t* table, int nlb, int num_blocks,
+                                          int64_t blk_stride, int tt, const LaneMap<KV, D, BS>& L) {
+  constexpr int NB = 32 / BS;
+  int pbs[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int lb = tt / BS + b;
+    const int pb = lb < nlb ? table[lb] : 0;
+    pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
+  }
+  const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
+  const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
+  const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
+#pragma unroll
+  for (int i = 0; i < StepRegs<KV, D>::NK; ++i) {
+    // bf16: k-step i starts 32*i dimensions further; fp8: load i covers k-steps 2i, 2i+1
+    const int di = KV == KV_FP8 ? 64 * i : 32 * i;
+    R.ka[i] = *reinterpret_cast<const uint4*>(ka + di);
+    R.kb[i] = *reinterpret_cast<const uint4*>(kb + di);
+  }
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) {
-    const T* col = vb + int64_t(16 * j + c) * BS;
-    if constexpr (KV == KV_FP8)
-      R.v[j] = okv ? *reinterpret_cast<const uint2*>(col) : make_uint2(0, 0);
-    else
-      R.v[j] = okv ? *reinterpret_cast<const uint4*>(col) : make_uint4(0, 0, 0, 0);
+    const auto* col = vb + 16 * j * BS;
+    if constexpr (KV == KV_FP8) R.v[j] = *reinterpret_cast<const uint2*>(col);
+    else R.v[j] = *reinterpret_cast<const uint4*>(col);
   }
 }
 
+// Rescaling threshold (log2 units): the running reference max is only raised
+// when a score exceeds it by more than this, so weights stay below 2^8.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int KV, int D>
 __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf16x8_t (&qb)[D / 32],
-                                             floatx4_t (&acc)[D / 16], float& m, float& l,
-                                             float qk_scale_log2, int tt, int t1, int r) {
-  // scores: S^T[token][head] for the two 16-token tiles
+                                             floatx4_t (&acc)[D / 16], floatx4_t& lsum, float& m,
+                                             float sl2, int tt, int t1, int r) {
+  // scores S^T[token][head] of the two 16-token tiles
   floatx4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -296,35 +325,35 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
     sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[i], sa, 0, 0, 0);
     sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[i], sb, 0, 0, 0);
   }
-  // lane (r, c): x[e] = score of head c for token 8r + e of the step
+  // lane (r, c): x[e] = raw score of head c for token 8r + e of the step
   float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
   const bool tail = tt + 32 > t1;
+  if (tail) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    x[e] *= qk_scale_log2;
-    if (tail && tt + 8 * r + e >= t1) x[e] = -INFINITY;
+    for (int e = 0; e < 8; ++e)
+      if (tt + 8 * r + e >= t1) x[e] = -INFINITY;
   }
-  float mx = x[0];
+  float lmax = x[0];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // token tt < t1 is valid, so mx is finite for every column
-  const float m_new = fmaxf(m, mx);
-  const float alpha = exp2f(m - m_new);
+  for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, x[e]);
+  // raise the reference max (and rescale what was summed so far) only when needed
+  if (__builtin_amdgcn_ballot_w64(lmax * sl2 > m + kRescaleLog2)) {
+    float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m, cmax * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+    lsum *= alpha;
+    m = m_new;
+  }
   uint32_t pw[4];
-  float psum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const uint16_t b0 = f32_to_bf16(exp2f(x[e] - m_new));
-    const uint16_t b1 = f32_to_bf16(exp2f(x[e + 1] - m_new));
-    psum += bf16_to_f32(b0) + bf16_to_f32(b1);
-    pw[e / 2] = uint32_t(b0) | (uint32_t(b1) << 16);
-  }
-  l = l * alpha + psum;
-  m = m_new;
+  for (int e = 0; e < 8; e += 2)
+    pw[e / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[e], sl2, -m)),
+                            __builtin_amdgcn_exp2f(fmaf(x[e + 1], sl2, -m)));
   const bf16x8_t pb = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-  // invalid tokens contribute p = 0, but 0 * NaN is NaN: zero their V elements
+  // invalid tokens have p = 0, but 0 * NaN is NaN: zero their V elements
   uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
   if (tail) {
 #pragma unroll
@@ -342,13 +371,16 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
       vw.z &= vmask[2];
       vw.w &= vmask[3];
     }
-    acc[j] *= alpha;
     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vw), pb, acc[j], 0, 0, 0);
   }
+  // running sum of the same bf16 weights: a ones operand sums P^T over the 32 tokens
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), pb, lsum, 0, 0, 0);
 }
 
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
+  typedef typename KvTraits<KV>::T T;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
   const int wid = remap_xcd(blockIdx.x, gridDim.x);
@@ -371,39 +403,45 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   // Q^T as the B operand of Q.K^T: column c = head c of the group (zero beyond the group)
   bf16x8_t qb[D / 32];
   {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (row0 + c) * D;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (row0 + min(c, g - 1)) * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-      const uint4 w = c < g ? *reinterpret_cast<const uint4*>(q + qk_dim0<KV>(i, r))
-                            : make_uint4(0, 0, 0, 0);
-      qb[i] = as_bf16x8(w);
+      const uint4 w = *reinterpret_cast<const uint4*>(q + qk_dim0<KV>(i, r));
+      qb[i] = as_bf16x8(c < g ? w : make_uint4(0, 0, 0, 0));
     }
   }
   const int32_t* table = a.block_tables + int64_t(s) * a.max_blocks;
+  const int nlb = (ctx + BS - 1) / BS;
+  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * D;
+  const T* kp = static_cast<const T*>(a.k_pool) + int64_t(kvh) * BS * D;
+  const T* vp = static_cast<const T*>(a.v_pool) + int64_t(kvh) * BS * D;
+  const LaneMap<KV, D, BS> L(r, c);
   floatx4_t acc[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  const float sl2 = a.qk_scale_log2;
 
-  // software pipeline: the next step's loads are in flight while this one computes
+  // two-stage software pipeline: the next step's loads are in flight while this one computes
   StepRegs<KV, D> bufA, bufB;
   int tt = t0;
-  load_step<KV, D, BS>(bufA, a, table, kvh, tt, t1, r, c);
+  load_step<KV, D, BS>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt, L);
   while (true) {
-    if (tt + 32 < t1) load_step<KV, D, BS>(bufB, a, table, kvh, tt + 32, t1, r, c);
-    compute_step<KV, D>(bufA, qb, acc, m, l, a.qk_scale_log2, tt, t1, r);
+    if (tt + 32 < t1)
+      load_step<KV, D, BS>(bufB, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
+    compute_step<KV, D>(bufA, qb, acc, lsum, m, sl2, tt, t1, r);
     tt += 32;
     if (tt >= t1) break;
-    if (tt + 32 < t1) load_step<KV, D, BS>(bufA, a, table, kvh, tt + 32, t1, r, c);
-    compute_step<KV, D>(bufB, qb, acc, m, l, a.qk_scale_log2, tt, t1, r);
+    if (tt + 32 < t1)
+      load_step<KV, D, BS>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
+    compute_step<KV, D>(bufB, qb, acc, lsum, m, sl2, tt, t1, r);
     tt += 32;
     if (tt >= t1) break;
   }
 
-  // lanes (0..3, c) hold disjoint tokens of head c: total the running sums
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
   if (c >= g) return;
+  const float l = lsum[0];
   const float inv = a.v_scale / l;
   const int64_t row = row0 + c;
   if (nparts == 1) {
@@ -411,8 +449,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     for (int j = 0; j < D / 16; ++j) {
       const int d = 16 * j + 4 * r;
       uint2 w;
-      w.x = uint32_t(f32_to_bf16(acc[j][0] * inv)) | (uint32_t(f32_to_bf16(acc[j][1] * inv)) << 16);
-      w.y = uint32_t(f32_to_bf16(acc[j][2] * inv)) | (uint32_t(f32_to_bf16(acc[j][3] * inv)) << 16);
+      w.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+      w.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
       *reinterpret_cast<uint2*>(out + row * D + d) = w;
     }
   } else {
