@@ -1,0 +1,96 @@
+"""Every workload at its full size, in the launch configuration bench.py times.
+
+For each configuration the GPU side runs the whole allocator script, the decode
+step and the decode attention with the configuration's partition size.  The
+oracle then checks:
+
+* the block tables and context lengths of every sequence (C++ manager vs the
+  oracle allocator), bit for bit;
+* for a seeded sample of sequences (shortest, longest and random ones): every
+  byte of the K and V blocks they use, and their attention outputs within the
+  dtype's tolerance.  The oracle writes only the sampled sequences' tokens (and,
+  for forked samples, their whole family) into full-size pools.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import TOL, GpuState, out_host, torch_mod
+from oracle import allocator as oalloc
+from oracle import attention as oattn
+from oracle import cache as ocache
+from oracle import codec
+from oracle_pipeline import kv_by_seq
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(wl, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    S = wl.num_seqs
+    idx = {int(np.argmin(wl.ctx_lens)), int(np.argmax(wl.ctx_lens))}
+    idx |= set(rng.choice(S, size=min(S, n), replace=False).tolist())
+    return sorted(idx)[: max(n, 2)] if S > 1 else [0]
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_full_config(name):
+    torch = torch_mod()
+    wl = workloads.get(name)
+    if wl.kv_dtype == "fp8":
+        wl.cache_sequences = True      # the scales need every input; keep them for the fill
+    print(f"config {name}: {wl.num_seqs} seqs, {int(wl.ctx_lens.sum())} tokens", flush=True)
+    g = GpuState(wl, workers=16)
+    out = out_host(g.decode())
+    print(f"config {name}: GPU decode done", flush=True)
+
+    # tables of every sequence
+    a = oalloc.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+    events = oalloc.run_ops(a, wl.setup_ops)
+    seqs = [int(s) for s in wl.decode_seqs]
+    starts = [a.lens[s] for s in seqs]
+    slots, pairs = a.append_batch(seqs)
+    tables, lens = a.block_tables(seqs, wl.max_blocks_per_seq)
+    assert np.array_equal(g.tables.cpu().numpy(), tables)
+    assert np.array_equal(g.lens.cpu().numpy(), lens)
+    assert g.slots.tolist() == slots and [tuple(p) for p in g.pairs.tolist()] == pairs
+
+    # sampled sequences: oracle pools holding their tokens (and their families')
+    rows = _sample(wl)
+    if name == "shared-prefix-bf16":
+        keep = {int(s) for r in rows for s in range((r // 4) * 4, (r // 4) * 4 + 4)}
+    else:
+        keep = {seqs[r] for r in rows}
+    k_scale, v_scale = wl.kv_scales()
+    kp, vp = ocache.new_pools(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
+                              wl.kv_dtype)
+    get = kv_by_seq(wl)
+    ev = [e for e in events if e[0] == "copy" or e[1] in keep]
+    ocache.apply_events(kp, vp, ev, get, wl.in_dtype, wl.kv_dtype, k_scale, v_scale)
+    if pairs:
+        ocache.copy_blocks(kp, vp, pairs)
+    for s, p, sl in zip(seqs, starts, slots):
+        if s in keep:
+            k, v = get(s)
+            ocache.reshape_and_cache(kp, vp, k[p:p + 1], v[p:p + 1], [sl], wl.in_dtype,
+                                     wl.kv_dtype, k_scale, v_scale)
+
+    # every block the sampled sequences read, bit for bit
+    used = sorted({int(b) for r in rows for b in tables[r][: -(-int(lens[r]) // wl.block_size)]})
+    idx = torch.tensor(used, dtype=torch.long, device="cuda")
+    gk = g.cache.k_pool.index_select(0, idx).cpu()
+    gv = g.cache.v_pool.index_select(0, idx).cpu()
+    gk = gk.view(torch.int16).numpy().view(np.uint16) if wl.kv_dtype == "bf16" else gk.numpy()
+    gv = gv.view(torch.int16).numpy().view(np.uint16) if wl.kv_dtype == "bf16" else gv.numpy()
+    assert np.array_equal(gk.view(np.uint8), kp[used].view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), vp[used].view(np.uint8))
+
+    # attention of the sampled sequences
+    q = wl.q_input()
+    q64 = codec.bf16_to_f64(q) if wl.in_dtype == "bf16" else q.astype(np.float64)
+    ref = oattn.paged_decode(q64, kp, vp, tables, lens, wl.scale, wl.kv_dtype, k_scale, v_scale,
+                             seqs=rows)
+    err = np.abs(out[rows] - ref[rows]).max()
+    print(f"config {name}: sampled rows {rows}, max abs err {err:.3g}", flush=True)
+    assert err <= TOL[wl.kv_dtype], err
+    assert np.isfinite(out).all()
