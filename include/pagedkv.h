@@ -145,14 +145,23 @@ int pkv_paged_attn_decode(const void* q, int32_t q_dtype,
                           int32_t max_context_len, int32_t partition_size,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Decode kernel families, for tests and benchmarks that pin one. */
+/* Decode kernel families (low byte of `impl`), for tests and benchmarks that pin one,
+ * and hints (high bits). */
 typedef enum {
   PKV_IMPL_AUTO = 0,     /* matrix-core kernel where built, else the vector kernel */
   PKV_IMPL_VECTOR = 1,   /* plain vector-ALU kernel: every dtype, fp32 arithmetic */
-  PKV_IMPL_MFMA = 2      /* bf16 / fp8 pools: QK^T and P.V on MFMA, group size <= 16 */
+  PKV_IMPL_MFMA = 2,     /* bf16 / fp8 pools: QK^T and P.V on MFMA, group size <= 16 */
+  PKV_IMPL_FAMILY_MASK = 0xff,
+  /* Hint: some blocks are shared by several sequences of the batch (forked
+   * samples, beam search).  The MFMA kernel then reads K/V with ordinary
+   * cached loads so the other readers hit in L2 / Infinity Cache; without the
+   * hint it streams them (non-temporal loads), which is faster when every
+   * block is read once.  The result is the same either way. */
+  PKV_IMPL_SHARED_BLOCKS = 0x100
 } pkv_decode_impl;
 
-/* pkv_paged_attn_decode with an explicit kernel family (PKV_E_UNSUPPORTED if not built). */
+/* pkv_paged_attn_decode with an explicit kernel family and hints (PKV_E_UNSUPPORTED if the
+ * family is not built for the pool's dtype). */
 int pkv_paged_attn_decode_ex(const void* q, int32_t q_dtype,
                              const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
                              const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 PKV_OK, PKV_E_INVAL, PKV_E_NOMEM, PKV_E_UNSUPPORTED, PKV_E_HIP = 0, -1, -2, -3, -4
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 IMPL_AUTO, IMPL_VECTOR, IMPL_MFMA = 0, 1, 2
+IMPL_SHARED_BLOCKS = 0x100     # hint: some blocks are shared between sequences
 DTYPES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
 
 

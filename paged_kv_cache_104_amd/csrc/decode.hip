@@ -265,10 +265,33 @@ __device__ __forceinline__ int pick_block(const int (&pbs)[32 / BS], int which) 
   return pb;
 }
 
+// A KV block that no other sequence shares is read once per decode: streaming
+// (non-temporal) loads keep it from displacing useful lines.  Blocks shared by
+// several sequences (forked samples) are read with ordinary loads so that the
+// other readers can hit in L2 / the Infinity Cache.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  u32x4_t v;
+  if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  else v = *static_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool NT>
+__device__ __forceinline__ uint2 ld8(const void* p) {
+  u32x2_t v;
+  if constexpr (NT) v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  else v = *static_cast<const u32x2_t*>(p);
+  return make_uint2(v.x, v.y);
+}
+
 // Issue the loads of one step.  Block ids outside the pool (and blocks past the
 // context, whose tokens are masked later) read block 0 instead, so every load is
 // in bounds and no lane branches.
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool NT>
 __device__ __forceinline__ void load_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
                                           const typename KvTraits<KV>::T* vp,
                                           const int32_t* table, int nlb, int num_blocks,
@@ -288,14 +311,14 @@ __device__ __forceinline__ void load_step(StepRegs<KV, D>& R, const typename KvT
   for (int i = 0; i < StepRegs<KV, D>::NK; ++i) {
     // bf16: k-step i starts 32*i dimensions further; fp8: load i covers k-steps 2i, 2i+1
     const int di = KV == KV_FP8 ? 64 * i : 32 * i;
-    R.ka[i] = *reinterpret_cast<const uint4*>(ka + di);
-    R.kb[i] = *reinterpret_cast<const uint4*>(kb + di);
+    R.ka[i] = ld16<NT>(ka + di);
+    R.kb[i] = ld16<NT>(kb + di);
   }
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) {
     const auto* col = vb + 16 * j * BS;
-    if constexpr (KV == KV_FP8) R.v[j] = *reinterpret_cast<const uint2*>(col);
-    else R.v[j] = *reinterpret_cast<const uint4*>(col);
+    if constexpr (KV == KV_FP8) R.v[j] = ld8<NT>(col);
+    else R.v[j] = ld16<NT>(col);
   }
 }
 
@@ -378,7 +401,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
   lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), pb, lsum, 0, 0, 0);
 }
 
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool NT>
 __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   typedef typename KvTraits<KV>::T T;
   const int lane = threadIdx.x;
@@ -426,15 +449,15 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   // two-stage software pipeline: the next step's loads are in flight while this one computes
   StepRegs<KV, D> bufA, bufB;
   int tt = t0;
-  load_step<KV, D, BS>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt, L);
+  load_step<KV, D, BS, NT>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt, L);
   while (true) {
     if (tt + 32 < t1)
-      load_step<KV, D, BS>(bufB, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
+      load_step<KV, D, BS, NT>(bufB, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
     compute_step<KV, D>(bufA, qb, acc, lsum, m, sl2, tt, t1, r);
     tt += 32;
     if (tt >= t1) break;
     if (tt + 32 < t1)
-      load_step<KV, D, BS>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
+      load_step<KV, D, BS, NT>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
     compute_step<KV, D>(bufB, qb, acc, lsum, m, sl2, tt, t1, r);
     tt += 32;
     if (tt >= t1) break;
@@ -471,26 +494,53 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------------ partition merge
 
 // out = sum_p w_p * o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p): the
-// same rescaling the running softmax applies between tiles.
+// same rescaling the running softmax applies between tiles.  One workgroup per
+// (sequence, q head); its 256 threads split the partitions into 256/D groups.
+constexpr int kMergeThreads = 256;
+
 template <typename QT, int D>
-__global__ __launch_bounds__(D) void merge_partitions_kernel(DecodeArgs a) {
-  const int row = blockIdx.x;  // s * Hq + h
+__global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(DecodeArgs a) {
+  constexpr int PG = kMergeThreads / D;       // partition groups
+  __shared__ float red[kMergeThreads];
+  __shared__ float part_o[PG][D];
+  __shared__ float part_l[PG];
+  const int row = blockIdx.x;                 // s * Hq + h
   const int s = row / a.num_q_heads;
   const int ctx = min(a.context_lens[s], a.max_ctx);
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;  // written directly by the decode kernel
+  if (nparts <= 1) return;                    // written directly by the decode kernel
+  const int tid = threadIdx.x;
   const float* ml = a.ws_ml + int64_t(row) * a.max_parts * 2;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  const int d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int p = tid; p < nparts; p += kMergeThreads) mx = fmaxf(mx, ml[2 * p]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const int d = tid % D, pg = tid / D;
   const float* acc = a.ws_acc + int64_t(row) * a.max_parts * D + d;
   float L = 0.f, o = 0.f;
-  for (int p = 0; p < nparts; ++p) {
+#pragma unroll 4
+  for (int p = pg; p < nparts; p += PG) {
     const float w = ml[2 * p + 1] * exp2f(ml[2 * p] - M);
     L += w;
     o = fmaf(w, acc[int64_t(p) * D], o);
   }
-  store_out(static_cast<QT*>(a.out) + int64_t(row) * D + d, o / L);
+  part_o[pg][d] = o;
+  if (d == 0) part_l[pg] = L;
+  __syncthreads();
+  if (pg == 0) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int g = 0; g < PG; ++g) {
+      ot += part_o[g][d];
+      lt += part_l[g];
+    }
+    store_out(static_cast<QT*>(a.out) + int64_t(row) * D + d, ot / lt);
+  }
 }
 
 // ------------------------------------------------------------------------ host side
@@ -524,21 +574,30 @@ static int dispatch_vector(const DecodeArgs& a, int kv, int qd, dim3 grid, hipSt
 }
 
 template <int D, int BS>
-static int dispatch_mfma(const DecodeArgs& a, int kv, dim3 grid, hipStream_t s) {
+static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, dim3 grid, hipStream_t s) {
   dim3 block(64);
-  if (kv == PKV_BF16) return launch(decode_mfma_kernel<KV_BF16, D, BS>, grid, block, s, a, "decode");
+  if (kv == PKV_BF16)
+    return shared ? launch(decode_mfma_kernel<KV_BF16, D, BS, false>, grid, block, s, a, "decode")
+                  : launch(decode_mfma_kernel<KV_BF16, D, BS, true>, grid, block, s, a, "decode");
   if (kv == PKV_FP8_E4M3)
-    return launch(decode_mfma_kernel<KV_FP8, D, BS>, grid, block, s, a, "decode");
+    return shared ? launch(decode_mfma_kernel<KV_FP8, D, BS, false>, grid, block, s, a, "decode")
+                  : launch(decode_mfma_kernel<KV_FP8, D, BS, true>, grid, block, s, a, "decode");
   return fail(PKV_E_UNSUPPORTED, "the MFMA kernel needs a bf16 or fp8 pool");
 }
 
 template <int D>
-static int dispatch_bs(const DecodeArgs& a, int bs, int kv, int qd, bool mfma, dim3 grid,
-                       hipStream_t s) {
+static int dispatch_bs(const DecodeArgs& a, int bs, int kv, int qd, bool mfma, bool shared,
+                       dim3 grid, hipStream_t s) {
   switch (bs) {
-    case 8: return mfma ? dispatch_mfma<D, 8>(a, kv, grid, s) : dispatch_vector<D, 8>(a, kv, qd, grid, s);
-    case 16: return mfma ? dispatch_mfma<D, 16>(a, kv, grid, s) : dispatch_vector<D, 16>(a, kv, qd, grid, s);
-    case 32: return mfma ? dispatch_mfma<D, 32>(a, kv, grid, s) : dispatch_vector<D, 32>(a, kv, qd, grid, s);
+    case 8:
+      return mfma ? dispatch_mfma<D, 8>(a, kv, shared, grid, s)
+                  : dispatch_vector<D, 8>(a, kv, qd, grid, s);
+    case 16:
+      return mfma ? dispatch_mfma<D, 16>(a, kv, shared, grid, s)
+                  : dispatch_vector<D, 16>(a, kv, qd, grid, s);
+    case 32:
+      return mfma ? dispatch_mfma<D, 32>(a, kv, shared, grid, s)
+                  : dispatch_vector<D, 32>(a, kv, qd, grid, s);
   }
   return fail(PKV_E_UNSUPPORTED, "block_size %d", bs);
 }
@@ -628,30 +687,34 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
 
 static int launch_partials(const DecodeArgs& a, const pkv_cache_desc* c, int32_t q_dtype,
                            int64_t P, int32_t impl, hipStream_t s) {
+  const int family = impl & PKV_IMPL_FAMILY_MASK;
+  const bool shared = (impl & PKV_IMPL_SHARED_BLOCKS) != 0;
+  if (impl & ~(PKV_IMPL_FAMILY_MASK | PKV_IMPL_SHARED_BLOCKS))
+    return fail(PKV_E_INVAL, "unknown impl flags 0x%x", impl);
   bool mfma;
-  if (impl == PKV_IMPL_AUTO) mfma = c->kv_dtype != PKV_F32;
-  else if (impl == PKV_IMPL_VECTOR) mfma = false;
-  else if (impl == PKV_IMPL_MFMA) {
+  if (family == PKV_IMPL_AUTO) mfma = c->kv_dtype != PKV_F32;
+  else if (family == PKV_IMPL_VECTOR) mfma = false;
+  else if (family == PKV_IMPL_MFMA) {
     if (c->kv_dtype == PKV_F32) return fail(PKV_E_UNSUPPORTED, "no MFMA kernel for an f32 pool");
     mfma = true;
   } else {
-    return fail(PKV_E_INVAL, "unknown impl %d", impl);
+    return fail(PKV_E_INVAL, "unknown kernel family %d", family);
   }
   const dim3 grid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads * P));
   return c->head_dim == 64
-             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, grid, s)
-             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, grid, s);
+             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, grid, s)
+             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, grid, s);
 }
 
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
   const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_q_heads));
   if (head_dim == 64)
     return q_dtype == PKV_F32
-               ? launch(merge_partitions_kernel<float, 64>, mgrid, dim3(64), s, a, "merge")
-               : launch(merge_partitions_kernel<uint16_t, 64>, mgrid, dim3(64), s, a, "merge");
+               ? launch(merge_partitions_kernel<float, 64>, mgrid, dim3(kMergeThreads), s, a, "merge")
+               : launch(merge_partitions_kernel<uint16_t, 64>, mgrid, dim3(kMergeThreads), s, a, "merge");
   return q_dtype == PKV_F32
-             ? launch(merge_partitions_kernel<float, 128>, mgrid, dim3(128), s, a, "merge")
-             : launch(merge_partitions_kernel<uint16_t, 128>, mgrid, dim3(128), s, a, "merge");
+             ? launch(merge_partitions_kernel<float, 128>, mgrid, dim3(kMergeThreads), s, a, "merge")
+             : launch(merge_partitions_kernel<uint16_t, 128>, mgrid, dim3(kMergeThreads), s, a, "merge");
 }
 
 extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const void* k_pool,

@@ -17,8 +17,8 @@ from typing import Callable, Optional, Sequence
 
 import numpy as np
 
-from . import (IMPL_AUTO, BlockManager, CacheDesc, alloc_pools, copy_blocks,
-               decode_workspace_bytes, paged_attn_decode, reshape_and_cache)
+from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_pools,
+               copy_blocks, decode_workspace_bytes, paged_attn_decode, reshape_and_cache)
 
 
 def to_device(x: np.ndarray, in_dtype: str, device):
@@ -113,8 +113,16 @@ class PagedKVCache:
         t, lens = self.bm.block_tables(seqs, max_blocks)
         return torch.from_numpy(t).to(self.device), torch.from_numpy(lens).to(self.device)
 
+    def shares_blocks(self) -> bool:
+        """True when some physical block is held by more than one sequence."""
+        st = self.bm.stats()
+        return st["logical_blocks"] > st["physical_blocks"]
+
     def decode(self, q, out, tables, lens, scale: float, max_context_len: int,
-               partition_size: int = 0, workspace=None, impl: int = IMPL_AUTO):
+               partition_size: int = 0, workspace=None, impl: int = IMPL_AUTO,
+               hint_sharing: bool = True):
+        if hint_sharing and self.shares_blocks():
+            impl |= IMPL_SHARED_BLOCKS
         return paged_attn_decode(q, self.k_pool, self.v_pool, tables, lens, scale, out, self.desc,
                                  max_context_len, partition_size, workspace, impl)
 

@@ -213,3 +213,18 @@ def test_partition_sweep_long_context():
         for impl in (1, 2):
             err = np.abs(out_host(g.decode(ps, impl)) - ref).max()
             assert err <= TOL["bf16"], (ps, impl, err)
+
+
+def test_shared_blocks_hint_changes_nothing():
+    """Cached and streaming K/V loads give bit-identical outputs."""
+    import paged_kv_cache_104_amd as pkv
+    from test_gpu_cache_ops import _shared_prefix_small
+
+    torch = torch_mod()
+    g = GpuState(_shared_prefix_small(13))
+    for ps in (0, 32):
+        a = g.decode(ps, pkv.IMPL_MFMA)
+        b = g.decode(ps, pkv.IMPL_MFMA | pkv.IMPL_SHARED_BLOCKS)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    with pytest.raises(pkv.PagedKVError):
+        g.decode(0, 0x200)
