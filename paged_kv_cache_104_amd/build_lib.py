@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-BUILD = os.path.join(ROOT, "_build")
-LIB = os.path.join(HERE, "libpagedkv.so")
+BUILD = os.environ.get("PKV_BUILD_DIR", os.path.join(ROOT, "_build"))
+LIB = os.environ.get("PKV_LIB_OUT", os.path.join(HERE, "libpagedkv.so"))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
@@ -38,7 +38,7 @@ def compile_one(src: str) -> str:
     out = _obj(src)
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += HIP_FLAGS + ["-x", "hip"]
+        cmd += HIP_FLAGS + os.environ.get("PKV_EXTRA_HIPFLAGS", "").split() + ["-x", "hip"]
     else:
         cmd += ["-x", "c++"]
     cmd += ["-c", path, "-o", out]

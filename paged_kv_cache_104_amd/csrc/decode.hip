@@ -401,9 +401,20 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
   lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), pb, lsum, 0, 0, 0);
 }
 
+// Software pipeline depth (32-token steps whose loads are in flight while one
+// computes) and the waves per SIMD the register budget is sized for.  Measured
+// on the 8B-like GQA layer: bf16 steps (16 KB) run best 3 deep at 1 wave/SIMD,
+// fp8 steps (8 KB) 2 deep at 2 waves/SIMD.
+template <int KV>
+struct MfmaTuning {
+  static constexpr int stages = KV == KV_FP8 ? 2 : 3;
+  static constexpr int waves = KV == KV_FP8 ? 2 : 1;
+};
+
 template <int KV, int D, int BS, bool NT>
-__global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(DecodeArgs a) {
   typedef typename KvTraits<KV>::T T;
+  constexpr int NS = MfmaTuning<KV>::stages;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
   const int wid = remap_xcd(blockIdx.x, gridDim.x);
@@ -423,6 +434,21 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
     }
     return;
   }
+  const int32_t* table = a.block_tables + int64_t(s) * a.max_blocks;
+  const int nlb = (ctx + BS - 1) / BS;
+  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * D;
+  const T* kp = static_cast<const T*>(a.k_pool) + int64_t(kvh) * BS * D;
+  const T* vp = static_cast<const T*>(a.v_pool) + int64_t(kvh) * BS * D;
+  const LaneMap<KV, D, BS> L(r, c);
+
+  // start the first steps' loads before anything else
+  StepRegs<KV, D> buf[NS];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (t0 + 32 * i < t1)
+      load_step<KV, D, BS, NT>(buf[i], kp, vp, table, nlb, a.num_blocks, blk_stride, t0 + 32 * i,
+                               L);
+
   // Q^T as the B operand of Q.K^T: column c = head c of the group (zero beyond the group)
   bf16x8_t qb[D / 32];
   {
@@ -433,12 +459,6 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
       qb[i] = as_bf16x8(c < g ? w : make_uint4(0, 0, 0, 0));
     }
   }
-  const int32_t* table = a.block_tables + int64_t(s) * a.max_blocks;
-  const int nlb = (ctx + BS - 1) / BS;
-  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * D;
-  const T* kp = static_cast<const T*>(a.k_pool) + int64_t(kvh) * BS * D;
-  const T* vp = static_cast<const T*>(a.v_pool) + int64_t(kvh) * BS * D;
-  const LaneMap<KV, D, BS> L(r, c);
   floatx4_t acc[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -446,22 +466,22 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(DecodeArgs a) {
   float m = -INFINITY;
   const float sl2 = a.qk_scale_log2;
 
-  // two-stage software pipeline: the next step's loads are in flight while this one computes
-  StepRegs<KV, D> bufA, bufB;
+  // ring of NS register buffers: step k computes from buf[k % NS] while the loads
+  // of steps k+1 .. k+NS-1 are in flight
   int tt = t0;
-  load_step<KV, D, BS, NT>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt, L);
   while (true) {
-    if (tt + 32 < t1)
-      load_step<KV, D, BS, NT>(bufB, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
-    compute_step<KV, D>(bufA, qb, acc, lsum, m, sl2, tt, t1, r);
-    tt += 32;
-    if (tt >= t1) break;
-    if (tt + 32 < t1)
-      load_step<KV, D, BS, NT>(bufA, kp, vp, table, nlb, a.num_blocks, blk_stride, tt + 32, L);
-    compute_step<KV, D>(bufB, qb, acc, lsum, m, sl2, tt, t1, r);
-    tt += 32;
-    if (tt >= t1) break;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int tl = tt + 32 * (NS - 1);
+      if (tl < t1)
+        load_step<KV, D, BS, NT>(buf[(st + NS - 1) % NS], kp, vp, table, nlb, a.num_blocks,
+                                 blk_stride, tl, L);
+      compute_step<KV, D>(buf[st], qb, acc, lsum, m, sl2, tt, t1, r);
+      tt += 32;
+      if (tt >= t1) goto done;
+    }
   }
+done:
 
   if (c >= g) return;
   const float l = lsum[0];

@@ -252,7 +252,7 @@ def gqa8b(kv_dtype: str = "fp8") -> Workload:
     """8B-like GQA layer: 128 seqs, 32 q / 8 KV heads, D=128, ctx U[1024,8192]."""
     ctx = _rng(4, _TAG_META, 0).integers(1024, 8192, size=128, endpoint=True)
     name = "8b-gqa-" + kv_dtype
-    w = _plain(name, 4, 128, 32, 8, 128, 16, ctx, kv_dtype, "bf16", 512,
+    w = _plain(name, 4, 128, 32, 8, 128, 16, ctx, kv_dtype, "bf16", 1024,
                description=f"8B-like GQA layer, {kv_dtype} KV, 128 seqs, 32q/8kv, "
                            "ctx U[1024,8192]")
     return w
