@@ -103,9 +103,11 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
                     int64_t num_pairs, const pkv_cache_desc* c, void* stream);
 
 /*
- * Bytes of workspace pkv_paged_attn_decode needs to split every context into
- * partitions of `partition_size` tokens (0 bytes when partition_size == 0 or a
- * single partition covers max_context_len).
+ * Bytes of device workspace a decode call needs (never 0 for a non-empty
+ * batch): the work queue and work list of the matrix-core kernel, and, when
+ * contexts are split, the per-partition (max, sum, output) rows.  A workspace
+ * serves one call at a time; calls on different streams need their own.  It
+ * needs no initialisation: every call rebuilds what it reads.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
@@ -129,10 +131,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   max_context_len  host-side upper bound of context_lens (sizes the grid
  *                 without reading device data); larger contexts are cut at it
  *   partition_size   0 = one pass over each context; otherwise a multiple of
- *                 B: each context is split into partitions of that many tokens
- *                 which run in parallel and are merged by a second kernel
+ *                 B: a context of ctx tokens is split into max(1, ctx / P)
+ *                 partitions of P tokens, the last one also taking the
+ *                 remainder; they run in parallel and a second kernel merges
+ *                 them
  *   workspace     device buffer of >= pkv_decode_workspace_bytes(...) bytes
- *                 (may be NULL when that is 0)
  * The result does not depend on partition_size beyond rounding; for a given
  * partition_size it depends only on the logical order of the context, not on
  * where blocks sit in the pool or on what unused slots hold.

@@ -278,7 +278,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
-    if need and workspace is None:
+    if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else 0
     ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0

@@ -7,23 +7,28 @@
 // tiled attention (glossary, "Related techniques").  Query heads share KV heads
 // in contiguous groups (grouped-query attention, same section).
 //
-// Work split: one work item = (sequence, KV head, partition of the context).
-// Partitions run in parallel; when a context has more than one, each writes
-// (running max, running sum, normalised output) to the workspace and
-// merge_partitions_kernel combines them.
-//
 // Two kernel families:
-//  * decode_mfma_kernel (bf16 / fp8 pools): one wave64 per work item.  The
-//    context is walked 32 tokens at a time; Q.K^T and P.V of the whole head
-//    group are 16x16x32 bf16 MFMAs (group padded to 16 columns), with P
-//    rounded to bf16.  Every lane issues 16-byte loads; the next 32 tokens are
-//    loaded while the current ones are computed.
+//  * decode_mfma_kernel (bf16 / fp8 pools).  plan_kernel lays the contexts of
+//    all (sequence, KV head) pairs end to end as one stream of 32-token steps
+//    and cuts it into equal contiguous ranges, one per persistent wave64
+//    worker, so every worker has the same amount of KV to read whatever the
+//    context lengths.  A worker walks its range with a ring of register
+//    buffers that keeps the next steps' loads in flight across context
+//    boundaries; Q.K^T and P.V of the whole head group are 16x16x32 bf16 MFMAs
+//    (group padded to 16 columns), with P rounded to bf16.  Each piece of a
+//    context a worker covers ("segment") ends with (running max, running sum,
+//    normalised output); a context covered by one segment writes its output
+//    directly, the others are combined by merge_kernel.
 //  * decode_vector_kernel (any pool dtype): a plain, fp32-arithmetic kernel
-//    with LDS staging; the f32 path and a cross-check of the MFMA kernel.
+//    with LDS staging, one workgroup per (sequence, KV head, partition of
+//    partition_size tokens); the f32 path and a cross-check of the MFMA kernel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -31,6 +36,9 @@
 namespace pkv {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxWorkers = 4096;     // persistent workers (wave64) at most
+constexpr int kProtoPartitions = 0;   // workspace rows are (row, partition)
+constexpr int kProtoSegments = 1;     // workspace rows are (segment, head of group)
 
 struct DecodeArgs {
   const void* q;
@@ -39,8 +47,11 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_ml;         // [S][Hq][P][2]: running max (log2 units), running sum
-  float* ws_acc;        // [S][Hq][P][D]: partition output, normalised
+  int32_t* hdr;         // [0] row protocol, [1] steps in all, [2] steps per worker
+  int4* recs;           // per (sequence, KV head) pair: {first step, first segment, segments, ctx}
+  int32_t* wstart;      // per worker: the pair its range starts in
+  float* ws_ml;         // partial (running max in log2 units, running sum) rows
+  float* ws_acc;        // partial normalised outputs, D floats per row
   int32_t max_blocks;   // row stride of block_tables
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -48,19 +59,25 @@ struct DecodeArgs {
   int32_t group;        // num_q_heads / num_kv_heads
   int32_t num_blocks;   // pool blocks (block ids outside [0, num_blocks) are skipped)
   int32_t max_ctx;      // contexts are cut at this host-known bound
-  int32_t part_tokens;  // partition length (tokens); the whole context when 0
-  int32_t max_parts;    // partitions per (sequence, KV head) in the grid
+  int32_t part_tokens;  // vector kernel: partition length (0 = whole context);
+                        // MFMA kernel: least tokens per worker (0 = balance only)
+  int32_t max_parts;    // vector kernel: partitions of the longest context
+  int32_t workers;      // MFMA kernel: persistent workers launched
   float qk_scale_log2;  // scale * log2(e) * k_scale
   float v_scale;
 };
 
-// Grid position -> work item.  Consecutive workgroups go to different XCDs
-// (round robin over 8); the remap keeps the partitions of one (sequence, KV
-// head) on one XCD so their table rows and query share that XCD's L2.
-__device__ __forceinline__ int remap_xcd(int bid, int nblocks) {
-  const int per = nblocks / 8;
-  if (bid >= per * 8) return bid;  // tail that does not fill all XCDs
-  return (bid % 8) * per + bid / 8;
+// Partitions of a context of ctx tokens for the vector kernel: max(1, ctx / P),
+// the last one taking the remainder; none for an empty context.
+__host__ __device__ __forceinline__ int num_parts(int ctx, int part) {
+  if (ctx <= 0) return 0;
+  if (part <= 0) return 1;
+  const int n = ctx / part;
+  return n > 1 ? n : 1;
+}
+
+__device__ __forceinline__ int part_end(int p, int np, int ctx, int part) {
+  return (part <= 0 || p == np - 1) ? ctx : (p + 1) * part;
 }
 
 template <typename OutT>
@@ -91,18 +108,19 @@ __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a
   const int s = wid / (a.max_parts * a.num_kv_heads);
   const int tid = threadIdx.x;
   const int g = a.group;
+  if (wid == 0 && tid == 0) a.hdr[0] = kProtoPartitions;
   const int ctx = min(a.context_lens[s], a.max_ctx);
-  const int t0 = a.part_tokens ? p * a.part_tokens : 0;
-  const int t1 = a.part_tokens ? min(ctx, t0 + a.part_tokens) : ctx;
-  const int nparts = a.part_tokens ? (ctx + a.part_tokens - 1) / a.part_tokens : 1;
+  const int nparts = num_parts(ctx, a.part_tokens);
   QT* out = static_cast<QT*>(a.out);
-  if (t0 >= t1) {
+  if (p >= nparts) {
     if (p == 0) {  // empty context: zeros
       for (int i = tid; i < g * D; i += kVecThreads)
         store_out(out + (int64_t(s) * a.num_q_heads + kvh * g + i / D) * D + i % D, 0.f);
     }
     return;
   }
+  const int t0 = p * a.part_tokens;
+  const int t1 = part_end(p, nparts, ctx, a.part_tokens);
   const QT* q = static_cast<const QT*>(a.q) + (int64_t(s) * a.num_q_heads + kvh * g) * D;
   for (int i = tid; i < g * D; i += kVecThreads) {
     float x;
@@ -207,6 +225,7 @@ struct StepRegs {
   uint4 ka[NK];   // K rows, tile a (MFMA A operand of Q.K^T)
   uint4 kb[NK];   // K rows, tile b
   typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];  // V^T, 8 tokens x 1 dim
+  uint4 q[D / 32];  // Q^T of the step's head group (MFMA B operand of Q.K^T)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -288,48 +307,14 @@ __device__ __forceinline__ uint2 ld8(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
-// Issue the loads of one step.  Block ids outside the pool (and blocks past the
-// context, whose tokens are masked later) read block 0 instead, so every load is
-// in bounds and no lane branches.
-template <int KV, int D, int BS, bool NT>
-__device__ __forceinline__ void load_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
-                                          const typename KvTraits<KV>::T* vp,
-                                          const int32_t* table, int nlb, int num_blocks,
-                                          int64_t blk_stride, int tt, const LaneMap<KV, D, BS>& L) {
-  constexpr int NB = 32 / BS;
-  int pbs[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int lb = tt / BS + b;
-    const int pb = lb < nlb ? table[lb] : 0;
-    pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
-  }
-  const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
-  const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
-  const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
-#pragma unroll
-  for (int i = 0; i < StepRegs<KV, D>::NK; ++i) {
-    // bf16: k-step i starts 32*i dimensions further; fp8: load i covers k-steps 2i, 2i+1
-    const int di = KV == KV_FP8 ? 64 * i : 32 * i;
-    R.ka[i] = ld16<NT>(ka + di);
-    R.kb[i] = ld16<NT>(kb + di);
-  }
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    const auto* col = vb + 16 * j * BS;
-    if constexpr (KV == KV_FP8) R.v[j] = ld8<NT>(col);
-    else R.v[j] = ld16<NT>(col);
-  }
-}
-
 // Rescaling threshold (log2 units): the running reference max is only raised
 // when a score exceeds it by more than this, so weights stay below 2^8.
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int KV, int D>
-__device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf16x8_t (&qb)[D / 32],
-                                             floatx4_t (&acc)[D / 16], floatx4_t& lsum, float& m,
-                                             float sl2, int tt, int t1, int r) {
+__device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, floatx4_t (&acc)[D / 16],
+                                             floatx4_t& lsum, float& m, float sl2, int tt, int t1,
+                                             int r) {
   // scores S^T[token][head] of the two 16-token tiles
   floatx4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -345,8 +330,8 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
       ka = as_bf16x8(R.ka[i]);
       kb = as_bf16x8(R.kb[i]);
     }
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[i], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[i], sb, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(R.q[i]), sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, as_bf16x8(R.q[i]), sb, 0, 0, 0);
   }
   // lane (r, c): x[e] = raw score of head c for token 8r + e of the step
   float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
@@ -402,137 +387,318 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const bf1
 }
 
 // Software pipeline depth (32-token steps whose loads are in flight while one
-// computes) and the waves per SIMD the register budget is sized for.  Measured
-// on the 8B-like GQA layer: bf16 steps (16 KB) run best 3 deep at 1 wave/SIMD,
-// fp8 steps (8 KB) 2 deep at 2 waves/SIMD.
+// computes) and the waves per SIMD the register budget is sized for.
+#ifndef PKV_BF16_STAGES
+#define PKV_BF16_STAGES 3
+#endif
+#ifndef PKV_BF16_WAVES
+#define PKV_BF16_WAVES 1
+#endif
+#ifndef PKV_FP8_STAGES
+#define PKV_FP8_STAGES 2
+#endif
+#ifndef PKV_FP8_WAVES
+#define PKV_FP8_WAVES 2
+#endif
 template <int KV>
 struct MfmaTuning {
-  static constexpr int stages = KV == KV_FP8 ? 2 : 3;
-  static constexpr int waves = KV == KV_FP8 ? 2 : 1;
+  static constexpr int stages = KV == KV_FP8 ? PKV_FP8_STAGES : PKV_BF16_STAGES;
+  static constexpr int waves = KV == KV_FP8 ? PKV_FP8_WAVES : PKV_BF16_WAVES;
 };
 
+// Physical blocks of the step at tokens tt .. tt+31 of a context of t1 tokens
+// whose table row is `table`; blocks past the context (masked tokens) and ids
+// outside the pool read block 0.
+template <int BS>
+__device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* __restrict__ table,
+                                            int tt, int t1, int num_blocks) {
+  const int nlb = (t1 + BS - 1) / BS;
+#pragma unroll
+  for (int b = 0; b < 32 / BS; ++b) {
+    const int lb = tt / BS + b;
+    const int pb = lb < nlb ? table[lb] : 0;
+    pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
+  }
+}
+
+// Issue the loads of one step: K rows, V^T columns and the query of the pair.
+// Lanes beyond the head group load a real head of the group: their columns
+// are computed and never written.
 template <int KV, int D, int BS, bool NT>
-__global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
+                                           const typename KvTraits<KV>::T* vp,
+                                           const int (&pbs)[32 / BS], int64_t blk_stride,
+                                           const uint16_t* qrow, const LaneMap<KV, D, BS>& L,
+                                           int r) {
+  const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
+  const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
+  const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
+#pragma unroll
+  for (int i = 0; i < StepRegs<KV, D>::NK; ++i) {
+    // bf16: k-step i starts 32*i dimensions further; fp8: load i covers k-steps 2i, 2i+1
+    const int di = KV == KV_FP8 ? 64 * i : 32 * i;
+    R.ka[i] = ld16<NT>(ka + di);
+    R.kb[i] = ld16<NT>(kb + di);
+  }
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const auto* col = vb + 16 * j * BS;
+    if constexpr (KV == KV_FP8) R.v[j] = ld8<NT>(col);
+    else R.v[j] = ld16<NT>(col);
+  }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) R.q[i] = ld16<false>(qrow + qk_dim0<KV>(i, r));
+}
+
+// A position in the step stream: pair j (= sequence * Hkv + KV head), its
+// record, and the step x within the pair.
+struct Cursor {
+  int j, x;
+  int4 rec;  // {first step of the pair, first segment, segments, context length}
+};
+
+__device__ __forceinline__ int pair_steps(const int4& rec) { return (rec.w + 31) >> 5; }
+
+// Move to the next pair that has steps.
+__device__ __forceinline__ void next_pair(Cursor& cu, const int4* __restrict__ recs) {
+  do {
+    ++cu.j;
+    cu.rec = recs[cu.j];
+  } while (cu.rec.w <= 0);
+  cu.x = 0;
+}
+
+template <int D>
+__device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
+                                              const floatx4_t (&acc)[D / 16],
+                                              const floatx4_t& lsum, float m, int r, int c) {
+  const int g = a.group;
+  if (c >= g) return;
+  const int s = cu.j / a.num_kv_heads, kvh = cu.j - s * a.num_kv_heads;
+  const float l = lsum[0];
+  const float inv = a.v_scale / l;
+  if (cu.rec.z == 1) {  // the whole context: write the output
+    uint16_t* out =
+        static_cast<uint16_t*>(a.out) + (int64_t(s) * a.num_q_heads + kvh * g + c) * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      uint2 v;
+      v.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+      v.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
+      *reinterpret_cast<uint2*>(out + 16 * j + 4 * r) = v;
+    }
+  } else {
+    const int64_t seg = cu.rec.y + (w - cu.rec.x / q);
+    const int64_t row = seg * g + c;
+    float* wacc = a.ws_acc + row * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      *reinterpret_cast<float4*>(wacc + 16 * j + 4 * r) =
+          make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+    if (r == 0) {
+      a.ws_ml[row * 2] = m;
+      a.ws_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// Persistent worker w: steps [w*q, min(T, (w+1)*q)) of the stream.  The load
+// cursor runs NS-1 steps ahead of the compute cursor; every iteration issues
+// exactly one step of loads (past the end of the range it repeats the last
+// step), so the count of loads in flight is the same on every path.
+template <int KV, int D, int BS, bool NT>
+__global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
+    DecodeArgs a, const int4* __restrict__ recs, const int32_t* __restrict__ tables) {
   typedef typename KvTraits<KV>::T T;
   constexpr int NS = MfmaTuning<KV>::stages;
+  constexpr int NB = 32 / BS;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int wid = remap_xcd(blockIdx.x, gridDim.x);
-  const int p = wid % a.max_parts;
-  const int kvh = (wid / a.max_parts) % a.num_kv_heads;
-  const int s = wid / (a.max_parts * a.num_kv_heads);
-  const int g = a.group;
-  const int ctx = min(a.context_lens[s], a.max_ctx);
-  const int t0 = a.part_tokens ? p * a.part_tokens : 0;
-  const int t1 = a.part_tokens ? min(ctx, t0 + a.part_tokens) : ctx;
-  const int nparts = a.part_tokens ? (ctx + a.part_tokens - 1) / a.part_tokens : 1;
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  const int64_t row0 = int64_t(s) * a.num_q_heads + kvh * g;  // first q head of the group
-  if (t0 >= t1) {
-    if (p == 0 && c < g) {  // empty context: zeros
-      for (int d = r; d < D; d += 4) out[(row0 + c) * D + d] = 0;
-    }
-    return;
-  }
-  const int32_t* table = a.block_tables + int64_t(s) * a.max_blocks;
-  const int nlb = (ctx + BS - 1) / BS;
-  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * D;
-  const T* kp = static_cast<const T*>(a.k_pool) + int64_t(kvh) * BS * D;
-  const T* vp = static_cast<const T*>(a.v_pool) + int64_t(kvh) * BS * D;
+  const int total = a.hdr[1], q = a.hdr[2];
+  const int w = blockIdx.x;
+  if (int64_t(w) * q >= total) return;
+  int rem = min(total - w * q, q);                 // steps left to compute
+  const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
+  const int64_t head_stride = int64_t(BS) * D;
+  const int64_t blk_stride = int64_t(a.num_kv_heads) * head_stride;
+  const T* k_pool = static_cast<const T*>(a.k_pool);
+  const T* v_pool = static_cast<const T*>(a.v_pool);
   const LaneMap<KV, D, BS> L(r, c);
+  const float sl2 = a.qk_scale_log2;
+  const int g = a.group, hkv = a.num_kv_heads;
+  const int cmin = min(c, g - 1);
 
-  // start the first steps' loads before anything else
-  StepRegs<KV, D> buf[NS];
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (t0 + 32 * i < t1)
-      load_step<KV, D, BS, NT>(buf[i], kp, vp, table, nlb, a.num_blocks, blk_stride, t0 + 32 * i,
-                               L);
+  Cursor cu;                                       // compute cursor
+  cu.j = a.wstart[w];
+  cu.rec = recs[cu.j];
+  cu.x = w * q - cu.rec.x;
+  Cursor la = cu;                                  // load cursor
+  int la_left = rem;                               // steps the load cursor still has to load
+  int la_pbs[NB];
+  int la_s = la.j / hkv;
+  step_blocks<BS>(la_pbs, tables + int64_t(la_s) * a.max_blocks, 32 * la.x, la.rec.w,
+                  a.num_blocks);
 
-  // Q^T as the B operand of Q.K^T: column c = head c of the group (zero beyond the group)
-  bf16x8_t qb[D / 32];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (row0 + min(c, g - 1)) * D;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const uint4 w = *reinterpret_cast<const uint4*>(q + qk_dim0<KV>(i, r));
-      qb[i] = as_bf16x8(c < g ? w : make_uint4(0, 0, 0, 0));
-    }
-  }
   floatx4_t acc[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
-  const float sl2 = a.qk_scale_log2;
+  StepRegs<KV, D> buf[NS];
 
-  // ring of NS register buffers: step k computes from buf[k % NS] while the loads
-  // of steps k+1 .. k+NS-1 are in flight
-  int tt = t0;
+  // issue the load cursor's step into R, then move the cursor on
+#define PKV_ISSUE(R)                                                                           \
+  do {                                                                                         \
+    const int kvh_ = la.j - la_s * hkv;                                                        \
+    issue_step<KV, D, BS, NT>(R, k_pool + int64_t(kvh_) * head_stride,                         \
+                              v_pool + int64_t(kvh_) * head_stride, la_pbs, blk_stride,        \
+                              qbase + (int64_t(la_s) * a.num_q_heads + kvh_ * g + cmin) * D, L, \
+                              r);                                                              \
+    if (la_left > 1) {                                                                         \
+      --la_left;                                                                               \
+      if (++la.x == pair_steps(la.rec)) {                                                      \
+        next_pair(la, recs);                                                                   \
+        la_s = la.j / hkv;                                                                     \
+      }                                                                                        \
+      step_blocks<BS>(la_pbs, tables + int64_t(la_s) * a.max_blocks, 32 * la.x, la.rec.w,     \
+                      a.num_blocks);                                                           \
+    }                                                                                          \
+  } while (0)
+
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) PKV_ISSUE(buf[i]);
   while (true) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const int tl = tt + 32 * (NS - 1);
-      if (tl < t1)
-        load_step<KV, D, BS, NT>(buf[(st + NS - 1) % NS], kp, vp, table, nlb, a.num_blocks,
-                                 blk_stride, tl, L);
-      compute_step<KV, D>(buf[st], qb, acc, lsum, m, sl2, tt, t1, r);
-      tt += 32;
-      if (tt >= t1) goto done;
+      PKV_ISSUE(buf[(st + NS - 1) % NS]);
+      compute_step<KV, D>(buf[st], acc, lsum, m, sl2, 32 * cu.x, cu.rec.w, r);
+      --rem;
+      if (++cu.x == pair_steps(cu.rec) || rem == 0) {
+        write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
+        if (rem == 0) goto done;
+        next_pair(cu, recs);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+      }
     }
   }
 done:
+  return;
+#undef PKV_ISSUE
+}
 
-  if (c >= g) return;
-  const float l = lsum[0];
-  const float inv = a.v_scale / l;
-  const int64_t row = row0 + c;
-  if (nparts == 1) {
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const int d = 16 * j + 4 * r;
-      uint2 w;
-      w.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
-      w.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
-      *reinterpret_cast<uint2*>(out + row * D + d) = w;
-    }
-  } else {
-    float* wacc = a.ws_acc + (row * a.max_parts + p) * D;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const int d = 16 * j + 4 * r;
-      *reinterpret_cast<float4*>(wacc + d) =
-          make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-    }
-    if (r == 0) {
-      a.ws_ml[(row * a.max_parts + p) * 2] = m;
-      a.ws_ml[(row * a.max_parts + p) * 2 + 1] = l;
-    }
+// Lays the steps of every (sequence, KV head) pair end to end, cuts the
+// stream into ranges of q steps (one per worker), and writes per pair its
+// first step, first segment and number of segments, and per worker the pair
+// its range starts in.  Pairs with an empty context get zero outputs.  One
+// workgroup; each thread handles a contiguous run of pairs.
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ void block_scan(int* scan, int t) {
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
   }
 }
 
-// ------------------------------------------------------------------------ partition merge
+template <typename QT, int D>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
+  __shared__ int scan[kPlanThreads];
+  __shared__ int q_sh;
+  const int t = threadIdx.x;
+  const int hkv = a.num_kv_heads, g = a.group;
+  const int np = a.num_seqs * hkv;
+  const int per = (np + kPlanThreads - 1) / kPlanThreads;
+  const int j0 = min(np, t * per), j1 = min(np, j0 + per);
+  int steps = 0;
+  for (int j = j0; j < j1; ++j) steps += (min(a.context_lens[j / hkv], a.max_ctx) + 31) >> 5;
+  scan[t] = steps;
+  block_scan(scan, t);
+  const int total = scan[kPlanThreads - 1];
+  if (t == 0) {
+    const int least = max(1, a.part_tokens >> 5);
+    q_sh = max(least, (total + a.workers - 1) / max(1, a.workers));
+  }
+  __syncthreads();
+  const int q = q_sh;
+  const int first_step = scan[t] - steps;
+  // segments: the workers whose ranges meet the pair
+  int segs = 0, P = first_step;
+  for (int j = j0; j < j1; ++j) {
+    const int n = (min(a.context_lens[j / hkv], a.max_ctx) + 31) >> 5;
+    if (n) segs += (P + n - 1) / q - P / q + 1;
+    P += n;
+  }
+  __syncthreads();
+  scan[t] = segs;
+  block_scan(scan, t);
+  int seg = scan[t] - segs;
+  P = first_step;
+  for (int j = j0; j < j1; ++j) {
+    const int s = j / hkv;
+    const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
+    const int n = (ctx + 31) >> 5;
+    const int ns = n ? (P + n - 1) / q - P / q + 1 : 0;
+    a.recs[j] = make_int4(P, seg, ns, ctx);
+    if (n) {
+      for (int w = (P + q - 1) / q; w <= (P + n - 1) / q; ++w) a.wstart[w] = j;
+    } else {
+      QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + (j - s * hkv) * g) * D;
+      for (int i = 0; i < g * D; ++i) store_out(out + i, 0.f);
+    }
+    P += n;
+    seg += ns;
+  }
+  if (t == kPlanThreads - 1) {
+    a.recs[np] = make_int4(total, seg, 0, 1);   // sentinel: never scanned past
+    a.hdr[0] = kProtoSegments;
+    a.hdr[1] = total;
+    a.hdr[2] = q;
+    a.hdr[3] = hkv;
+    a.hdr[4] = g;
+  }
+}
 
-// out = sum_p w_p * o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p): the
+// ------------------------------------------------------------------------ merge
+
+// out = sum_k w_k * o_k / sum_k w_k with w_k = l_k * 2^(m_k - max_k m_k): the
 // same rescaling the running softmax applies between tiles.  One workgroup per
-// (sequence, q head); its 256 threads split the partitions into 256/D groups.
+// (sequence, q head); its 256 threads split the pieces into 256/D groups.  The
+// pieces are the vector kernel's partitions or the MFMA kernel's segments,
+// whichever wrote the workspace last (its header says which).
 constexpr int kMergeThreads = 256;
 
 template <typename QT, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(DecodeArgs a) {
-  constexpr int PG = kMergeThreads / D;       // partition groups
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  constexpr int PG = kMergeThreads / D;       // piece groups
   __shared__ float red[kMergeThreads];
   __shared__ float part_o[PG][D];
   __shared__ float part_l[PG];
   const int row = blockIdx.x;                 // s * Hq + h
   const int s = row / a.num_q_heads;
-  const int ctx = min(a.context_lens[s], a.max_ctx);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;                    // written directly by the decode kernel
+  int count, stride;
+  int64_t first;
+  if (a.hdr[0] == kProtoSegments) {
+    const int hkv = a.hdr[3], g = a.hdr[4];
+    const int h = row - s * a.num_q_heads;
+    const int4 rec = a.recs[s * hkv + h / g];
+    count = rec.z;
+    first = int64_t(rec.y) * g + (h % g);
+    stride = g;
+  } else {
+    count = num_parts(min(a.context_lens[s], a.max_ctx), a.part_tokens);
+    first = int64_t(row) * a.max_parts;
+    stride = 1;
+  }
+  if (count <= 1) return;                     // written directly by the decode kernel
   const int tid = threadIdx.x;
-  const float* ml = a.ws_ml + int64_t(row) * a.max_parts * 2;
   float mx = -INFINITY;
-  for (int p = tid; p < nparts; p += kMergeThreads) mx = fmaxf(mx, ml[2 * p]);
+  for (int k = tid; k < count; k += kMergeThreads) mx = fmaxf(mx, a.ws_ml[(first + int64_t(k) * stride) * 2]);
   red[tid] = mx;
   __syncthreads();
   for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
@@ -541,13 +707,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(DecodeA
   }
   const float M = red[0];
   const int d = tid % D, pg = tid / D;
-  const float* acc = a.ws_acc + int64_t(row) * a.max_parts * D + d;
   float L = 0.f, o = 0.f;
 #pragma unroll 4
-  for (int p = pg; p < nparts; p += PG) {
-    const float w = ml[2 * p + 1] * exp2f(ml[2 * p] - M);
+  for (int k = pg; k < count; k += PG) {
+    const int64_t i = first + int64_t(k) * stride;
+    const float w = a.ws_ml[i * 2 + 1] * exp2f(a.ws_ml[i * 2] - M);
     L += w;
-    o = fmaf(w, acc[int64_t(p) * D], o);
+    o = fmaf(w, a.ws_acc[i * D + d], o);
   }
   part_o[pg][d] = o;
   if (d == 0) part_l[pg] = L;
@@ -555,9 +721,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(DecodeA
   if (pg == 0) {
     float ot = 0.f, lt = 0.f;
 #pragma unroll
-    for (int g = 0; g < PG; ++g) {
-      ot += part_o[g][d];
-      lt += part_l[g];
+    for (int k = 0; k < PG; ++k) {
+      ot += part_o[k][d];
+      lt += part_l[k];
     }
     store_out(static_cast<QT*>(a.out) + int64_t(row) * D + d, ot / lt);
   }
@@ -567,23 +733,77 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partitions_kernel(DecodeA
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static int64_t parts_for(int32_t max_ctx, int32_t part) {
+static int64_t max_parts_for(int32_t max_ctx, int32_t part) {
   if (part <= 0 || max_ctx <= 0) return 1;
-  return (int64_t(max_ctx) + part - 1) / part;
+  return std::max<int64_t>(1, max_ctx / part);
 }
 
-template <typename K>
+static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Workspace: header | per-pair records | per-worker start pairs | partial rows
+// ((max, sum) then D floats each).  Sized with num_q_heads (>= num_kv_heads) so
+// the size does not depend on the pool; the partial rows cover both the vector
+// kernel's partitions and the MFMA kernel's segments (at most one per pair plus
+// one per worker, each holding a head group).
+struct WsLayout {
+  size_t recs_off, wstart_off, ml_off, acc_off, total;
+  int64_t parts, rows, pairs;
+};
+
+static WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                          int32_t max_ctx, int32_t part) {
+  WsLayout w;
+  w.parts = max_parts_for(max_ctx, part);
+  w.pairs = int64_t(num_seqs) * num_q_heads;
+  w.recs_off = 256;
+  w.wstart_off = w.recs_off + align256(size_t(w.pairs + 1) * sizeof(int4));
+  w.ml_off = w.wstart_off + align256(size_t(kMaxWorkers) * sizeof(int32_t));
+  const int64_t part_rows = w.parts > 1 ? w.pairs * w.parts : 0;
+  const int64_t seg_rows = w.pairs + int64_t(kMaxWorkers) * std::min(num_q_heads, 16);
+  w.rows = std::max(part_rows, seg_rows);
+  w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
+  w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
+  return w;
+}
+
+template <typename K, typename... Extra>
 static int launch(K kernel, dim3 grid, dim3 block, hipStream_t s, const DecodeArgs& a,
-                  const char* what) {
-  kernel<<<grid, block, 0, s>>>(a);
+                  const char* what, Extra... extra) {
+  kernel<<<grid, block, 0, s>>>(a, extra...);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
   return PKV_OK;
 }
 
+// Workers that fit on the current device at once for a one-wave kernel.
+template <typename K>
+static int64_t resident_workers(K kernel) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  const uint64_t key = (uint64_t(reinterpret_cast<uintptr_t>(reinterpret_cast<const void*>(kernel)))
+                        << 8) ^ uint64_t(dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
+                                                   64, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    hipGetLastError();
+    return 1024;
+  }
+  const int64_t n = int64_t(cus) * per_cu;
+  cache[key] = n;
+  return n;
+}
+
 template <int D, int BS>
-static int dispatch_vector(const DecodeArgs& a, int kv, int qd, dim3 grid, hipStream_t s) {
-  dim3 block(kVecThreads);
+static int dispatch_vector(const DecodeArgs& a, int kv, int qd, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads * a.max_parts));
+  const dim3 block(kVecThreads);
   if (kv == PKV_F32 && qd == PKV_F32)
     return launch(decode_vector_kernel<KV_F32, float, D, BS>, grid, block, s, a, "decode");
   if (kv == PKV_BF16 && qd == PKV_BF16)
@@ -593,31 +813,38 @@ static int dispatch_vector(const DecodeArgs& a, int kv, int qd, dim3 grid, hipSt
   return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(qd), dtype_name(kv));
 }
 
+template <int KV, int D, int BS, bool NT>
+static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
+  auto kernel = decode_mfma_kernel<KV, D, BS, NT>;
+  DecodeArgs a = a0;
+  a.workers = int32_t(std::min<int64_t>(kMaxWorkers, resident_workers(kernel)));
+  int rc = launch(plan_kernel<uint16_t, D>, dim3(1), dim3(kPlanThreads), s, a, "plan");
+  if (rc) return rc;
+  return launch(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a, "decode",
+                a.recs, a.block_tables);
+}
+
 template <int D, int BS>
-static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, dim3 grid, hipStream_t s) {
-  dim3 block(64);
+static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, hipStream_t s) {
   if (kv == PKV_BF16)
-    return shared ? launch(decode_mfma_kernel<KV_BF16, D, BS, false>, grid, block, s, a, "decode")
-                  : launch(decode_mfma_kernel<KV_BF16, D, BS, true>, grid, block, s, a, "decode");
+    return shared ? launch_mfma<KV_BF16, D, BS, false>(a, s)
+                  : launch_mfma<KV_BF16, D, BS, true>(a, s);
   if (kv == PKV_FP8_E4M3)
-    return shared ? launch(decode_mfma_kernel<KV_FP8, D, BS, false>, grid, block, s, a, "decode")
-                  : launch(decode_mfma_kernel<KV_FP8, D, BS, true>, grid, block, s, a, "decode");
+    return shared ? launch_mfma<KV_FP8, D, BS, false>(a, s)
+                  : launch_mfma<KV_FP8, D, BS, true>(a, s);
   return fail(PKV_E_UNSUPPORTED, "the MFMA kernel needs a bf16 or fp8 pool");
 }
 
 template <int D>
 static int dispatch_bs(const DecodeArgs& a, int bs, int kv, int qd, bool mfma, bool shared,
-                       dim3 grid, hipStream_t s) {
+                       hipStream_t s) {
   switch (bs) {
     case 8:
-      return mfma ? dispatch_mfma<D, 8>(a, kv, shared, grid, s)
-                  : dispatch_vector<D, 8>(a, kv, qd, grid, s);
+      return mfma ? dispatch_mfma<D, 8>(a, kv, shared, s) : dispatch_vector<D, 8>(a, kv, qd, s);
     case 16:
-      return mfma ? dispatch_mfma<D, 16>(a, kv, shared, grid, s)
-                  : dispatch_vector<D, 16>(a, kv, qd, grid, s);
+      return mfma ? dispatch_mfma<D, 16>(a, kv, shared, s) : dispatch_vector<D, 16>(a, kv, qd, s);
     case 32:
-      return mfma ? dispatch_mfma<D, 32>(a, kv, shared, grid, s)
-                  : dispatch_vector<D, 32>(a, kv, qd, grid, s);
+      return mfma ? dispatch_mfma<D, 32>(a, kv, shared, s) : dispatch_vector<D, 32>(a, kv, qd, s);
   }
   return fail(PKV_E_UNSUPPORTED, "block_size %d", bs);
 }
@@ -629,13 +856,10 @@ using namespace pkv;
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_context_len,
                                              int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  const int64_t P = parts_for(max_context_len, partition_size);
-  if (P <= 1) return 0;
-  const int64_t rows = int64_t(num_seqs) * num_q_heads * P;
-  const size_t ml = size_t(rows) * 2 * sizeof(float);
-  const size_t ml_padded = (ml + 255) & ~size_t(255);
-  return ml_padded + size_t(rows) * head_dim * sizeof(float);
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  return ws_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size).total;
 }
 
 // Validate the arguments of a decode call and fill the kernel arguments.
@@ -644,7 +868,7 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                    int32_t num_q_heads, float scale, void* out, int32_t max_context_len,
                    int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   DecodeArgs* a, int64_t* parts) {
+                   DecodeArgs* a, WsLayout* lay) {
   int rc = check_desc(c);
   if (rc) return rc;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -661,36 +885,37 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   if (int64_t(max_blocks_per_seq) * c->block_size < max_context_len)
     return fail(PKV_E_INVAL, "max_blocks_per_seq %d cannot hold max_context_len %d",
                 max_blocks_per_seq, max_context_len);
+  if (int64_t(num_seqs) * c->num_kv_heads * ((int64_t(max_context_len) + 31) / 32) >= (1 << 30))
+    return fail(PKV_E_INVAL, "batch too large for one call");
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
     return fail(PKV_E_INVAL, "q_dtype must be f32 or bf16");
   if ((c->kv_dtype == PKV_F32) != (q_dtype == PKV_F32))
     return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(q_dtype),
                 dtype_name(c->kv_dtype));
-  const int64_t P = parts_for(max_context_len, partition_size);
-  *parts = P;
+  *lay = ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim, max_context_len,
+                   partition_size);
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return fail(PKV_E_INVAL, "NULL pointer");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
-  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, c->head_dim,
-                                                 max_context_len, partition_size);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
-  const int64_t items = int64_t(num_seqs) * c->num_kv_heads * P;
-  if (items > 0x7fffffff) return fail(PKV_E_INVAL, "grid too large");
+  if (!workspace || workspace_bytes < lay->total || !aligned16(workspace))
+    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", lay->total,
+                workspace_bytes);
+  if (lay->rows > 0x7fffffff || lay->pairs > 0x7fffffff)
+    return fail(PKV_E_INVAL, "batch too large for one call");
+  char* ws = static_cast<char*>(workspace);
   a->q = q;
   a->k_pool = k_pool;
   a->v_pool = v_pool;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
   a->out = out;
-  const int64_t rows = int64_t(num_seqs) * num_q_heads * P;
-  a->ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a->ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                              ((size_t(rows) * 2 * sizeof(float) + 255) &
-                                               ~size_t(255)))
-                   : nullptr;
+  a->hdr = reinterpret_cast<int32_t*>(ws);
+  a->recs = reinterpret_cast<int4*>(ws + lay->recs_off);
+  a->wstart = reinterpret_cast<int32_t*>(ws + lay->wstart_off);
+  a->ws_ml = reinterpret_cast<float*>(ws + lay->ml_off);
+  a->ws_acc = reinterpret_cast<float*>(ws + lay->acc_off);
   a->max_blocks = max_blocks_per_seq;
   a->num_seqs = num_seqs;
   a->num_q_heads = num_q_heads;
@@ -698,15 +923,18 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   a->group = group;
   a->num_blocks = c->num_blocks;
   a->max_ctx = max_context_len;
-  a->part_tokens = P > 1 ? partition_size : 0;
-  a->max_parts = int32_t(P);
+  a->part_tokens = partition_size;
+  a->max_parts = int32_t(lay->parts);
+  a->workers = 0;
   a->qk_scale_log2 = scale * kLog2e * (c->kv_dtype == PKV_FP8_E4M3 ? c->k_scale : 1.f);
   a->v_scale = c->kv_dtype == PKV_FP8_E4M3 ? c->v_scale : 1.f;
   return PKV_OK;
 }
 
-static int launch_partials(const DecodeArgs& a, const pkv_cache_desc* c, int32_t q_dtype,
-                           int64_t P, int32_t impl, hipStream_t s) {
+// Launches the per-partition / per-segment kernels; *merge tells whether the
+// merge kernel has pieces to combine.
+static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_t q_dtype,
+                           const WsLayout& lay, int32_t impl, hipStream_t s, bool* merge) {
   const int family = impl & PKV_IMPL_FAMILY_MASK;
   const bool shared = (impl & PKV_IMPL_SHARED_BLOCKS) != 0;
   if (impl & ~(PKV_IMPL_FAMILY_MASK | PKV_IMPL_SHARED_BLOCKS))
@@ -720,21 +948,23 @@ static int launch_partials(const DecodeArgs& a, const pkv_cache_desc* c, int32_t
   } else {
     return fail(PKV_E_INVAL, "unknown kernel family %d", family);
   }
-  const dim3 grid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads * P));
+  DecodeArgs a = a0;
+  if (!mfma && lay.parts <= 1) a.part_tokens = 0;   // the vector kernel does not split
+  *merge = mfma || lay.parts > 1;
   return c->head_dim == 64
-             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, grid, s)
-             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, grid, s);
+             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, s)
+             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, s);
 }
 
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
   const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_q_heads));
+  const dim3 block(kMergeThreads);
   if (head_dim == 64)
     return q_dtype == PKV_F32
-               ? launch(merge_partitions_kernel<float, 64>, mgrid, dim3(kMergeThreads), s, a, "merge")
-               : launch(merge_partitions_kernel<uint16_t, 64>, mgrid, dim3(kMergeThreads), s, a, "merge");
-  return q_dtype == PKV_F32
-             ? launch(merge_partitions_kernel<float, 128>, mgrid, dim3(kMergeThreads), s, a, "merge")
-             : launch(merge_partitions_kernel<uint16_t, 128>, mgrid, dim3(kMergeThreads), s, a, "merge");
+               ? launch(merge_kernel<float, 64>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 64>, mgrid, block, s, a, "merge");
+  return q_dtype == PKV_F32 ? launch(merge_kernel<float, 128>, mgrid, block, s, a, "merge")
+                            : launch(merge_kernel<uint16_t, 128>, mgrid, block, s, a, "merge");
 }
 
 extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const void* k_pool,
@@ -747,12 +977,13 @@ extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const voi
                                        int32_t impl) {
   clear_error();
   DecodeArgs a;
-  int64_t P = 1;
+  WsLayout lay;
   int rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
                    num_seqs, num_q_heads, scale, out, max_context_len, partition_size, workspace,
-                   workspace_bytes, &a, &P);
+                   workspace_bytes, &a, &lay);
   if (rc || num_seqs == 0) return rc;
-  return launch_partials(a, c, q_dtype, P, impl, static_cast<hipStream_t>(stream));
+  bool merge = false;
+  return launch_partials(a, c, q_dtype, lay, impl, static_cast<hipStream_t>(stream), &merge);
 }
 
 extern "C" int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens,
@@ -766,26 +997,26 @@ extern "C" int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_E_UNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return fail(PKV_E_INVAL, "bad q_dtype");
-  const int64_t P = parts_for(max_context_len, partition_size);
-  if (P <= 1 || num_seqs == 0) return PKV_OK;  // nothing was split
-  const size_t need =
-      pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace))
-    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (num_seqs == 0) return PKV_OK;
+  const WsLayout lay = ws_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < lay.total || !aligned16(workspace))
+    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", lay.total,
+                workspace_bytes);
   if (!context_lens || !out || !aligned16(out)) return fail(PKV_E_INVAL, "bad pointer");
   if (int64_t(num_seqs) * num_q_heads > 0x7fffffff) return fail(PKV_E_INVAL, "grid too large");
   DecodeArgs a = {};
-  const int64_t rows = int64_t(num_seqs) * num_q_heads * P;
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_ml = static_cast<float*>(const_cast<void*>(workspace));
-  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
-                                      ((size_t(rows) * 2 * sizeof(float) + 255) & ~size_t(255)));
+  a.hdr = reinterpret_cast<int32_t*>(ws);
+  a.recs = reinterpret_cast<int4*>(ws + lay.recs_off);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.ws_acc = reinterpret_cast<float*>(ws + lay.acc_off);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.max_ctx = max_context_len;
-  a.part_tokens = partition_size;
-  a.max_parts = int32_t(P);
+  a.part_tokens = lay.parts > 1 ? partition_size : 0;
+  a.max_parts = int32_t(lay.parts);
   return launch_merge(a, head_dim, q_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -799,15 +1030,18 @@ extern "C" int pkv_paged_attn_decode_ex(const void* q, int32_t q_dtype, const vo
                                         int32_t impl) {
   clear_error();
   DecodeArgs a;
-  int64_t P = 1;
+  WsLayout lay;
   int rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
                    num_seqs, num_q_heads, scale, out, max_context_len, partition_size, workspace,
-                   workspace_bytes, &a, &P);
+                   workspace_bytes, &a, &lay);
   if (rc || num_seqs == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = launch_partials(a, c, q_dtype, P, impl, s);
-  if (rc || P <= 1) return rc;
-  return launch_merge(a, c->head_dim, q_dtype, s);
+  bool merge = false;
+  rc = launch_partials(a, c, q_dtype, lay, impl, s, &merge);
+  if (rc || !merge) return rc;
+  DecodeArgs m = a;
+  if (lay.parts <= 1) m.part_tokens = 0;
+  return launch_merge(m, c->head_dim, q_dtype, s);
 }
 
 extern "C" int pkv_paged_attn_decode(const void* q, int32_t q_dtype, const void* k_pool,

@@ -29,11 +29,17 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_size():
     import paged_kv_cache_104_amd as pkv
 
-    assert pkv.decode_workspace_bytes(4, 8, 128, 1000, 0) == 0
-    assert pkv.decode_workspace_bytes(4, 8, 128, 512, 512) == 0
-    n = pkv.decode_workspace_bytes(4, 8, 128, 1000, 512)
-    rows = 4 * 8 * 2
-    assert n >= rows * (128 + 2) * 4
+    # header + one 16-byte record per (seq, head) + worker starts + partial rows; the
+    # partial rows hold the MFMA kernel's segments (one per pair plus one per worker
+    # and head of a group) or the vector kernel's partitions, whichever is larger
+    one = pkv.decode_workspace_bytes(4, 8, 128, 1000, 0)
+    assert one >= 256 + 4 * 8 * 16 + (4 * 8) * (128 + 2) * 4
+    assert pkv.decode_workspace_bytes(4, 8, 128, 1000, 512) == one       # 1000 // 512 = 1 part
+    assert pkv.decode_workspace_bytes(4, 8, 128, 1024, 512) == one       # fits the segment rows
+    # many partitions: partition rows of (max, sum) and D floats dominate
+    rows = 64 * 8 * 1000
+    assert pkv.decode_workspace_bytes(64, 8, 128, 16000, 16) >= rows * (128 + 2) * 4
+    assert pkv.decode_workspace_bytes(0, 8, 128, 1024, 512) == 0
 
 
 def _desc(**kw):
