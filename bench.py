@@ -3,17 +3,17 @@
 
 One step is one pass of the whole hot path over the batch:
   host   C++ block manager: append one token per sequence -> slots, copy pairs,
-         block tables (staged in pinned memory, uploaded asynchronously)
+         block tables (staged in pinned memory, one packed upload)
   device copy_blocks (copy-on-write pairs, when there are any)
          reshape_and_cache (the batch's new K/V into their slots)
-         paged attention: per-partition kernel + partition merge
+         paged attention: decode kernel + merge of split contexts
 Inputs are resident in HBM before the timed region.  Contexts grow by one
 token per step, as in a real decode loop; the KV bytes of every step are
 counted from the block manager's lengths.
 
 Prints one JSON line.  `value` is the KV-read rate of the whole step
 (algorithmic KV bytes / wall time of the timed steps); the `roofline` object is
-the per-partition attention kernel alone, timed with HIP events on its stream.
+the decode attention kernel alone, timed with HIP events on its stream.
 """
 from __future__ import annotations
 
@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "8b-gqa-bf16"
 DOMINANT_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DIAG_STEPS = 10        # untimed steps after the timed ones, with every kernel bracketed
 
 
 def kernel_source_hash() -> str:
@@ -111,7 +112,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.num_seqs} seqs, "
         f"{int(wl.ctx_lens.sum())} cached tokens, pool {wl.num_blocks} blocks")
     S, B = len(seqs), wl.block_size
-    total = warmup + steps
+    total = warmup + steps + DIAG_STEPS
     max_ctx = wl.max_context_len + total
     max_blocks = -(-max_ctx // B)
     bytes_per_token = wl.kv_bytes_per_token()
@@ -128,6 +129,9 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         return (buf[:8 * S].view(torch.int64), buf[o_lens:o_lens + 4 * S].view(torch.int32),
                 buf[o_tab:o_tab + 4 * S * max_blocks].view(torch.int32).view(S, max_blocks))
 
+    # Host staging is double-buffered: the host fills one pinned buffer while the
+    # stream still copies from the other.  (A separate copy stream gains a few
+    # microseconds per step but stalls the host for milliseconds once, early on.)
     pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     host_views = [views(b) for b in pinned]
     packed_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -136,18 +140,26 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     out = torch.empty_like(q)
     ws_bytes = pkv.decode_workspace_bytes(S, wl.num_q_heads, wl.head_dim, max_ctx, partition_size)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
+    # Timed steps record one event pair, around the decode kernel; the diagnostic
+    # steps after them also time the cache write and the merge.  Every event is
+    # recorded once here so none is created inside the timed loop.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    for e in [x for row in ev for x in row] + uploaded:
+        e.record(stream)
+    torch.cuda.synchronize()
     st = cache.bm.stats()
     shared = st["logical_blocks"] > st["physical_blocks"]
     if shared:                         # forked samples share blocks: keep them cached
         impl |= pkv.IMPL_SHARED_BLOCKS
     kv_bytes = np.zeros(total)
+    host_s = np.zeros(total)
     n_pairs = 0
 
-    def step(i):
+    def step(i, all_events=False):
         nonlocal n_pairs
         b = i % 2
         uploaded[b].synchronize()                     # pinned buffer b is free again
+        h0 = time.perf_counter()
         slots, pairs = cache.bm.append_batch(seqs)
         sh, lh, th = host_views[b]
         np.copyto(sh.numpy(), slots)
@@ -157,7 +169,8 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         packed_d.copy_(pinned[b], non_blocking=True)
         uploaded[b].record(stream)
         e = ev[i]
-        e[0].record(stream)
+        if all_events:
+            e[0].record(stream)
         if len(pairs):
             n_pairs += len(pairs)
             pkv.copy_blocks(cache.k_pool, cache.v_pool, pairs, desc)
@@ -166,8 +179,10 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, tables_d, lens_d, wl.scale, out,
                                 desc, max_ctx, partition_size, workspace, impl)
         e[2].record(stream)
-        pkv.paged_attn_merge(out, lens_d, max_ctx, partition_size, workspace)
-        e[3].record(stream)
+        pkv.paged_attn_merge(out, lens_d, wl.num_kv_heads, max_ctx, partition_size, workspace)
+        if all_events:
+            e[3].record(stream)
+        host_s[i] = time.perf_counter() - h0
 
     for i in range(warmup):
         step(i)
@@ -175,16 +190,21 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     gc.collect()
     gc.disable()                      # no collector pauses inside the timed steps
     t0 = time.perf_counter()
-    for i in range(warmup, total):
+    for i in range(warmup, warmup + steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for i in range(warmup + steps, total):
+        step(i, all_events=True)
+    torch.cuda.synchronize()
     gc.enable()
-    timed = range(warmup, total)
-    t_write = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed]) * 1e-3
+    timed = range(warmup, warmup + steps)
+    diag = range(warmup + steps, total)
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed]) * 1e-3
-    t_merge = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in timed]) * 1e-3
-    kvb = kv_bytes[warmup:]
+    t_write = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in diag]) * 1e-3
+    t_merge = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in diag]) * 1e-3
+    t_attn_diag = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in diag]) * 1e-3
+    kvb = kv_bytes[warmup:warmup + steps]
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     # bytes of distinct blocks (a block shared by several sequences counted once), last step
     tables, lens = cache.bm.block_tables(seqs, max_blocks)
@@ -196,6 +216,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
             fill[b] = max(fill.get(b, 0), min(B, int(n) - j * B))
     unique_bytes = float(sum(fill.values())) * bytes_per_token
     return dict(wall=wall, kv_bytes=kvb, t_write=t_write, t_attn=t_attn, t_merge=t_merge,
+                t_attn_diag=t_attn_diag, host_s=host_s[warmup:warmup + steps],
                 max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs, shared=shared,
                 unique_ratio=unique_bytes / float(kvb[-1]))
 
@@ -317,10 +338,12 @@ def main() -> int:
         "decode_tokens_per_s": round(wl.num_seqs * args.steps / wall, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {
+            "decode_attention": round(float(r["t_attn"].mean()) * 1e3, 4),
             "reshape_and_cache+copy_blocks": round(float(r["t_write"].mean()) * 1e3, 4),
-            "attention_partials": round(float(r["t_attn"].mean()) * 1e3, 4),
-            "attention_merge": round(float(r["t_merge"].mean()) * 1e3, 4),
+            "merge": round(float(r["t_merge"].mean()) * 1e3, 4),
+            "decode_attention_diag": round(float(r["t_attn_diag"].mean()) * 1e3, 4),
         },
+        "host_ms_per_step": round(float(r["host_s"].mean()) * 1e3, 4),
         "roofline": {
             "kernel": DOMINANT_KERNEL,
             "bound": "hbm",

@@ -103,11 +103,13 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
                     int64_t num_pairs, const pkv_cache_desc* c, void* stream);
 
 /*
- * Bytes of device workspace a decode call needs (never 0 for a non-empty
- * batch): the work queue and work list of the matrix-core kernel, and, when
- * contexts are split, the per-partition (max, sum, output) rows.  A workspace
- * serves one call at a time; calls on different streams need their own.  It
- * needs no initialisation: every call rebuilds what it reads.
+ * Bytes of device workspace a decode call needs (0 only for an empty batch or
+ * invalid sizes): a header, one record per (sequence, head) and the
+ * (max, sum, output) rows of split contexts -- the matrix-core kernel's two
+ * slots per persistent worker (at most 4096 workers, 16 heads per group) or
+ * the vector kernel's partitions, whichever is larger.  A workspace serves one
+ * call at a time; calls on different streams need their own.  It needs no
+ * initialisation: every call writes what it later reads.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
@@ -130,15 +132,18 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   out           device [num_seqs][num_q_heads][D] of q_dtype
  *   max_context_len  host-side upper bound of context_lens (sizes the grid
  *                 without reading device data); larger contexts are cut at it
- *   partition_size   0 = one pass over each context; otherwise a multiple of
- *                 B: a context of ctx tokens is split into max(1, ctx / P)
- *                 partitions of P tokens, the last one also taking the
- *                 remainder; they run in parallel and a second kernel merges
- *                 them
+ *   partition_size   0 or a multiple of B.  Vector kernel: 0 = one pass over
+ *                 each context, else a context of ctx tokens is split into
+ *                 max(1, ctx / P) partitions of P tokens, the last one also
+ *                 taking the remainder, run in parallel and merged.  MFMA
+ *                 kernel: the batch's steps are shared out evenly over the
+ *                 persistent workers, each taking at least P tokens (0 = no
+ *                 lower bound); contexts that cross a worker boundary are
+ *                 merged.
  *   workspace     device buffer of >= pkv_decode_workspace_bytes(...) bytes
- * The result does not depend on partition_size beyond rounding; for a given
- * partition_size it depends only on the logical order of the context, not on
- * where blocks sit in the pool or on what unused slots hold.
+ * The result does not depend on the split beyond rounding; for given context
+ * lengths and partition_size it depends only on the logical order of each
+ * context, not on where blocks sit in the pool or on what unused slots hold.
  */
 int pkv_paged_attn_decode(const void* q, int32_t q_dtype,
                           const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
@@ -176,19 +181,22 @@ int pkv_paged_attn_decode_ex(const void* q, int32_t q_dtype,
 
 /*
  * The two phases of pkv_paged_attn_decode, for callers that time or schedule
- * them apart (or merge partitions computed elsewhere).
+ * them apart.
  *
  * pkv_paged_attn_partials -- same arguments as pkv_paged_attn_decode_ex.
- *   Sequences whose context fits one partition get their output written to
- *   `out`; the others leave, per (sequence, q head, partition), the running
- *   max (log2 units), running sum and normalised partial output in
- *   `workspace` for pkv_paged_attn_merge.
- * pkv_paged_attn_merge -- combines the partitions of every sequence that has
- *   more than one: out = sum_p w_p o_p / sum_p w_p with
- *   w_p = l_p * 2^(m_p - max m), the rescaling of the running softmax
- *   (FlashAttention-style tiling, glossary "Related techniques").  Arguments
- *   must match the partials call; nothing is launched when no context was
- *   split.
+ *   A context computed in one piece gets its output written to `out`; the
+ *   others leave, per piece and q head, the running max (log2 units), running
+ *   sum and normalised partial output in `workspace` for pkv_paged_attn_merge.
+ *   The vector kernel's pieces are the partitions of partition_size tokens;
+ *   the MFMA kernel's pieces are the parts of a context that fall to different
+ *   persistent workers (each worker takes an equal share of all 32-token steps
+ *   of the batch, and at least partition_size tokens when that is non-zero).
+ * pkv_paged_attn_merge -- combines the pieces of every context that has more
+ *   than one, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max m)
+ *   (the rescaling of the running softmax, FlashAttention-style tiling,
+ *   glossary "Related techniques"), and writes zeros for empty contexts.
+ *   Arguments must match the partials call; the workspace header says which
+ *   kernel family wrote the pieces.
  */
 int pkv_paged_attn_partials(const void* q, int32_t q_dtype,
                             const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
@@ -199,9 +207,9 @@ int pkv_paged_attn_partials(const void* q, int32_t q_dtype,
                             void* workspace, size_t workspace_bytes, void* stream,
                             int32_t impl);
 int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t num_seqs,
-                         int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                         int32_t partition_size, const void* workspace, size_t workspace_bytes,
-                         void* out, void* stream);
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t partition_size, const void* workspace,
+                         size_t workspace_bytes, void* out, void* stream);
 
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);

@@ -69,8 +69,8 @@ _SIGNATURES = {
     "pkv_paged_attn_partials": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
                                                _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
                                                _i32, _vp, _sz, _vp, _i32]),
-    "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
-                                            _vp, _vp]),
+    "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _vp, _sz, _vp, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
@@ -304,13 +304,14 @@ def paged_attn_partials(q, k_pool, v_pool, block_tables, context_lens, scale: fl
         _stream(stream), int(impl)))
 
 
-def paged_attn_merge(out, context_lens, max_context_len: int, partition_size: int, workspace,
-                     stream=None):
+def paged_attn_merge(out, context_lens, num_kv_heads: int, max_context_len: int,
+                     partition_size: int, workspace, stream=None):
     """Second phase of paged_attn_decode: merge split contexts into ``out``."""
     S, Hq, D = out.shape
     ws_ptr = _ptr(workspace) if workspace is not None else 0
     ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
-    _check(lib.pkv_paged_attn_merge(dtype_code(out), _ptr(context_lens), S, Hq, D,
+    _check(lib.pkv_paged_attn_merge(dtype_code(out), _ptr(context_lens), S, Hq,
+                                    int(num_kv_heads), D,
                                     int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
                                     _ptr(out), _stream(stream)))
 

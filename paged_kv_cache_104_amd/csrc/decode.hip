@@ -8,17 +8,18 @@
 // in contiguous groups (grouped-query attention, same section).
 //
 // Two kernel families:
-//  * decode_mfma_kernel (bf16 / fp8 pools).  plan_kernel lays the contexts of
-//    all (sequence, KV head) pairs end to end as one stream of 32-token steps
-//    and cuts it into equal contiguous ranges, one per persistent wave64
-//    worker, so every worker has the same amount of KV to read whatever the
-//    context lengths.  A worker walks its range with a ring of register
-//    buffers that keeps the next steps' loads in flight across context
-//    boundaries; Q.K^T and P.V of the whole head group are 16x16x32 bf16 MFMAs
-//    (group padded to 16 columns), with P rounded to bf16.  Each piece of a
-//    context a worker covers ("segment") ends with (running max, running sum,
-//    normalised output); a context covered by one segment writes its output
-//    directly, the others are combined by merge_kernel.
+//  * decode_mfma_kernel (bf16 / fp8 pools).  The contexts of all (sequence,
+//    KV head) pairs are laid end to end as one stream of 32-token steps, cut
+//    into equal contiguous ranges, one per persistent wave64 worker, so every
+//    worker reads the same amount of KV whatever the context lengths.  Each
+//    worker finds its own range from the context lengths (a wave-wide prefix
+//    sum) and walks it with a ring of register buffers that keeps the next
+//    steps' loads in flight across context boundaries; Q.K^T and P.V of the
+//    whole head group are 16x16x32 bf16 MFMAs (group padded to 16 columns),
+//    with P rounded to bf16.  Each piece of a context a worker covers
+//    ("segment") ends with (running max, running sum, normalised output); a
+//    context covered by one segment writes its output directly, the others
+//    are combined by merge_kernel.
 //  * decode_vector_kernel (any pool dtype): a plain, fp32-arithmetic kernel
 //    with LDS staging, one workgroup per (sequence, KV head, partition of
 //    partition_size tokens); the f32 path and a cross-check of the MFMA kernel.
@@ -47,9 +48,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  int32_t* hdr;         // [0] row protocol, [1] steps in all, [2] steps per worker
-  int4* recs;           // per (sequence, KV head) pair: {first step, first segment, segments, ctx}
-  int32_t* wstart;      // per worker: the pair its range starts in
+  int32_t* hdr;         // [0] which kernel wrote the partial rows
+  int2* recs;           // per (sequence, KV head) pair: {first worker, workers} (MFMA kernel)
   float* ws_ml;         // partial (running max in log2 units, running sum) rows
   float* ws_acc;        // partial normalised outputs, D floats per row
   int32_t max_blocks;   // row stride of block_tables
@@ -450,36 +450,112 @@ __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename Kv
   for (int i = 0; i < D / 32; ++i) R.q[i] = ld16<false>(qrow + qk_dim0<KV>(i, r));
 }
 
-// A position in the step stream: pair j (= sequence * Hkv + KV head), its
-// record, and the step x within the pair.
+// A position in the step stream: pair (sequence s, KV head kvh), the pair's
+// first step P in the stream, its steps n and context length ctx, and the
+// step x within the pair.  The stream orders pairs by sequence, then KV head.
 struct Cursor {
-  int j, x;
-  int4 rec;  // {first step of the pair, first segment, segments, context length}
+  int s, kvh, x, P, n, ctx;
 };
 
-__device__ __forceinline__ int pair_steps(const int4& rec) { return (rec.w + 31) >> 5; }
+__device__ __forceinline__ int clamp_ctx(int len, int max_ctx) { return max(0, min(len, max_ctx)); }
+__device__ __forceinline__ int ctx_steps(int ctx) { return (ctx + 31) >> 5; }
 
-// Move to the next pair that has steps.
-__device__ __forceinline__ void next_pair(Cursor& cu, const int4* __restrict__ recs) {
-  do {
-    ++cu.j;
-    cu.rec = recs[cu.j];
-  } while (cu.rec.w <= 0);
+// Move to the next pair that has steps; the caller knows there is one.
+__device__ __forceinline__ void next_pair(Cursor& cu, const int32_t* __restrict__ lens, int hkv,
+                                          int max_ctx) {
+  cu.P += cu.n;
   cu.x = 0;
+  if (++cu.kvh < hkv) return;
+  cu.kvh = 0;
+  do {
+    ++cu.s;
+    cu.ctx = clamp_ctx(lens[cu.s], max_ctx);
+  } while (cu.ctx == 0);
+  cu.n = ctx_steps(cu.ctx);
 }
 
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Every worker derives the split itself from the context lengths (the wave's
+// results are made uniform so the cursor lives in scalar registers): the
+// stream's length `total`, the steps per worker `q` (equal for all, at least
+// part_tokens / 32) and the cursor at its own first step w * q.  False when
+// worker w has no steps.
+__device__ __forceinline__ bool find_start(const DecodeArgs& a, const int32_t* __restrict__ lens,
+                                           int w, int lane, int& total, int& q, Cursor& cu) {
+  const int S = a.num_seqs, hkv = a.num_kv_heads;
+  int sum = 0;
+  for (int s0 = 0; s0 < S; s0 += 256) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + 64 * u + lane;
+      v[u] = s < S ? lens[s] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sum += ctx_steps(clamp_ctx(v[u], a.max_ctx));
+  }
+  total = __builtin_amdgcn_readfirstlane(wave_sum(sum)) * hkv;
+  q = max(max(1, a.part_tokens >> 5), (total + a.workers - 1) / a.workers);
+  if (int64_t(w) * q >= total) return false;
+  const int target = w * q;
+  int base = 0;  // steps of one KV head of the sequences before the chunk
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    const int n = s < S ? ctx_steps(clamp_ctx(lens[s], a.max_ctx)) : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    const uint64_t hit = __ballot(hkv * (base + incl) > target);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const int ns = __builtin_amdgcn_readfirstlane(__shfl(n, l));
+      const int first = hkv * (base + __builtin_amdgcn_readfirstlane(__shfl(incl, l)) - ns);
+      cu.s = s0 + l;
+      cu.kvh = (target - first) / ns;
+      cu.x = target - first - cu.kvh * ns;
+      cu.n = ns;
+      cu.P = first + cu.kvh * ns;
+      cu.ctx = clamp_ctx(lens[cu.s], a.max_ctx);
+      return true;
+    }
+    base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  }
+  return false;
+}
+
+// End of a worker's share of a pair.  A pair that lies inside the worker's
+// range [lo, lo + q) writes its output; otherwise the share is a partial
+// segment, stored in the worker's slot 0 (the pair began before the range)
+// or slot 1 (it goes on past the range).  The worker that holds a pair's
+// first step also records {first worker, workers} of the pair for the merge.
 template <int D>
 __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
                                               const floatx4_t (&acc)[D / 16],
                                               const floatx4_t& lsum, float m, int r, int c) {
   const int g = a.group;
+  const int lo = w * q;
+  const bool head = cu.P >= lo;                  // the pair starts in this range
+  const bool whole = head && cu.P + cu.n <= lo + q;
+  const int64_t pair = int64_t(cu.s) * a.num_kv_heads + cu.kvh;
+  if (head && r == 0 && c == 0) a.recs[pair] = make_int2(w, (cu.P + cu.n - 1) / q - w + 1);
   if (c >= g) return;
-  const int s = cu.j / a.num_kv_heads, kvh = cu.j - s * a.num_kv_heads;
   const float l = lsum[0];
   const float inv = a.v_scale / l;
-  if (cu.rec.z == 1) {  // the whole context: write the output
-    uint16_t* out =
-        static_cast<uint16_t*>(a.out) + (int64_t(s) * a.num_q_heads + kvh * g + c) * D;
+  if (whole) {
+    uint16_t* out = static_cast<uint16_t*>(a.out) +
+                    (int64_t(cu.s) * a.num_q_heads + cu.kvh * g + c) * D;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
       uint2 v;
@@ -488,8 +564,7 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
       *reinterpret_cast<uint2*>(out + 16 * j + 4 * r) = v;
     }
   } else {
-    const int64_t seg = cu.rec.y + (w - cu.rec.x / q);
-    const int64_t row = seg * g + c;
+    const int64_t row = int64_t(2 * w + (head ? 1 : 0)) * g + c;
     float* wacc = a.ws_acc + row * D;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
@@ -502,21 +577,26 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
   }
 }
 
-// Persistent worker w: steps [w*q, min(T, (w+1)*q)) of the stream.  The load
-// cursor runs NS-1 steps ahead of the compute cursor; every iteration issues
-// exactly one step of loads (past the end of the range it repeats the last
-// step), so the count of loads in flight is the same on every path.
+// Persistent worker w: steps [w*q, min(total, (w+1)*q)) of the stream.  The
+// load cursor runs NS-1 steps ahead of the compute cursor; every iteration
+// issues exactly one step of loads (past the end of the range it repeats the
+// last step), so the count of loads in flight is the same on every path.
+// Context lengths and block tables come in as separate restrict arguments:
+// the kernel's stores cannot alias them, so their uniform loads stay scalar
+// and never wait on the vector-load counter.
 template <int KV, int D, int BS, bool NT>
 __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
-    DecodeArgs a, const int4* __restrict__ recs, const int32_t* __restrict__ tables) {
+    DecodeArgs a, const int32_t* __restrict__ lens, const int32_t* __restrict__ tables) {
   typedef typename KvTraits<KV>::T T;
   constexpr int NS = MfmaTuning<KV>::stages;
   constexpr int NB = 32 / BS;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
-  const int total = a.hdr[1], q = a.hdr[2];
   const int w = blockIdx.x;
-  if (int64_t(w) * q >= total) return;
+  if (w == 0 && lane == 0) a.hdr[0] = kProtoSegments;
+  int total, q;
+  Cursor cu;                                       // compute cursor
+  if (!find_start(a, lens, w, lane, total, q, cu)) return;
   int rem = min(total - w * q, q);                 // steps left to compute
   const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
   const int64_t head_stride = int64_t(BS) * D;
@@ -525,18 +605,13 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   const T* v_pool = static_cast<const T*>(a.v_pool);
   const LaneMap<KV, D, BS> L(r, c);
   const float sl2 = a.qk_scale_log2;
-  const int g = a.group, hkv = a.num_kv_heads;
+  const int g = a.group, hkv = a.num_kv_heads, max_ctx = a.max_ctx;
   const int cmin = min(c, g - 1);
 
-  Cursor cu;                                       // compute cursor
-  cu.j = a.wstart[w];
-  cu.rec = recs[cu.j];
-  cu.x = w * q - cu.rec.x;
   Cursor la = cu;                                  // load cursor
   int la_left = rem;                               // steps the load cursor still has to load
   int la_pbs[NB];
-  int la_s = la.j / hkv;
-  step_blocks<BS>(la_pbs, tables + int64_t(la_s) * a.max_blocks, 32 * la.x, la.rec.w,
+  step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,
                   a.num_blocks);
 
   floatx4_t acc[D / 16];
@@ -549,18 +624,14 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
   do {                                                                                         \
-    const int kvh_ = la.j - la_s * hkv;                                                        \
-    issue_step<KV, D, BS, NT>(R, k_pool + int64_t(kvh_) * head_stride,                         \
-                              v_pool + int64_t(kvh_) * head_stride, la_pbs, blk_stride,        \
-                              qbase + (int64_t(la_s) * a.num_q_heads + kvh_ * g + cmin) * D, L, \
-                              r);                                                              \
+    issue_step<KV, D, BS, NT>(R, k_pool + int64_t(la.kvh) * head_stride,                       \
+                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride,      \
+                              qbase + (int64_t(la.s) * a.num_q_heads + la.kvh * g + cmin) * D, \
+                              L, r);                                                           \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
-      if (++la.x == pair_steps(la.rec)) {                                                      \
-        next_pair(la, recs);                                                                   \
-        la_s = la.j / hkv;                                                                     \
-      }                                                                                        \
-      step_blocks<BS>(la_pbs, tables + int64_t(la_s) * a.max_blocks, 32 * la.x, la.rec.w,     \
+      if (++la.x == la.n) next_pair(la, lens, hkv, max_ctx);                                   \
+      step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,       \
                       a.num_blocks);                                                           \
     }                                                                                          \
   } while (0)
@@ -571,12 +642,12 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       PKV_ISSUE(buf[(st + NS - 1) % NS]);
-      compute_step<KV, D>(buf[st], acc, lsum, m, sl2, 32 * cu.x, cu.rec.w, r);
+      compute_step<KV, D>(buf[st], acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
       --rem;
-      if (++cu.x == pair_steps(cu.rec) || rem == 0) {
+      if (++cu.x == cu.n || rem == 0) {
         write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
         if (rem == 0) goto done;
-        next_pair(cu, recs);
+        next_pair(cu, lens, hkv, max_ctx);
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -589,143 +660,58 @@ done:
 #undef PKV_ISSUE
 }
 
-// Lays the steps of every (sequence, KV head) pair end to end, cuts the
-// stream into ranges of q steps (one per worker), and writes per pair its
-// first step, first segment and number of segments, and per worker the pair
-// its range starts in.  Pairs with an empty context get zero outputs.  One
-// workgroup; each thread handles a contiguous run of pairs.
-constexpr int kPlanThreads = 1024;
-
-__device__ __forceinline__ void block_scan(int* scan, int t) {
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
-}
-
-template <typename QT, int D>
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
-  __shared__ int scan[kPlanThreads];
-  __shared__ int q_sh;
-  const int t = threadIdx.x;
-  const int hkv = a.num_kv_heads, g = a.group;
-  const int np = a.num_seqs * hkv;
-  const int per = (np + kPlanThreads - 1) / kPlanThreads;
-  const int j0 = min(np, t * per), j1 = min(np, j0 + per);
-  int steps = 0;
-  for (int j = j0; j < j1; ++j) steps += (min(a.context_lens[j / hkv], a.max_ctx) + 31) >> 5;
-  scan[t] = steps;
-  block_scan(scan, t);
-  const int total = scan[kPlanThreads - 1];
-  if (t == 0) {
-    const int least = max(1, a.part_tokens >> 5);
-    q_sh = max(least, (total + a.workers - 1) / max(1, a.workers));
-  }
-  __syncthreads();
-  const int q = q_sh;
-  const int first_step = scan[t] - steps;
-  // segments: the workers whose ranges meet the pair
-  int segs = 0, P = first_step;
-  for (int j = j0; j < j1; ++j) {
-    const int n = (min(a.context_lens[j / hkv], a.max_ctx) + 31) >> 5;
-    if (n) segs += (P + n - 1) / q - P / q + 1;
-    P += n;
-  }
-  __syncthreads();
-  scan[t] = segs;
-  block_scan(scan, t);
-  int seg = scan[t] - segs;
-  P = first_step;
-  for (int j = j0; j < j1; ++j) {
-    const int s = j / hkv;
-    const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
-    const int n = (ctx + 31) >> 5;
-    const int ns = n ? (P + n - 1) / q - P / q + 1 : 0;
-    a.recs[j] = make_int4(P, seg, ns, ctx);
-    if (n) {
-      for (int w = (P + q - 1) / q; w <= (P + n - 1) / q; ++w) a.wstart[w] = j;
-    } else {
-      QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + (j - s * hkv) * g) * D;
-      for (int i = 0; i < g * D; ++i) store_out(out + i, 0.f);
-    }
-    P += n;
-    seg += ns;
-  }
-  if (t == kPlanThreads - 1) {
-    a.recs[np] = make_int4(total, seg, 0, 1);   // sentinel: never scanned past
-    a.hdr[0] = kProtoSegments;
-    a.hdr[1] = total;
-    a.hdr[2] = q;
-    a.hdr[3] = hkv;
-    a.hdr[4] = g;
-  }
-}
-
 // ------------------------------------------------------------------------ merge
 
 // out = sum_k w_k * o_k / sum_k w_k with w_k = l_k * 2^(m_k - max_k m_k): the
 // same rescaling the running softmax applies between tiles.  One workgroup per
-// (sequence, q head); its 256 threads split the pieces into 256/D groups.  The
-// pieces are the vector kernel's partitions or the MFMA kernel's segments,
-// whichever wrote the workspace last (its header says which).
+// (sequence, KV head) pair covers the pair's head group.  The pieces are the
+// vector kernel's partitions or the MFMA kernel's segments, whichever wrote
+// the workspace last (its header says which).  Empty contexts get zeros here.
 constexpr int kMergeThreads = 256;
 
 template <typename QT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  constexpr int PG = kMergeThreads / D;       // piece groups
-  __shared__ float red[kMergeThreads];
-  __shared__ float part_o[PG][D];
-  __shared__ float part_l[PG];
-  const int row = blockIdx.x;                 // s * Hq + h
-  const int s = row / a.num_q_heads;
-  int count, stride;
-  int64_t first;
-  if (a.hdr[0] == kProtoSegments) {
-    const int hkv = a.hdr[3], g = a.hdr[4];
-    const int h = row - s * a.num_q_heads;
-    const int4 rec = a.recs[s * hkv + h / g];
-    count = rec.z;
-    first = int64_t(rec.y) * g + (h % g);
-    stride = g;
+  const int pair = blockIdx.x;
+  const int hkv = a.num_kv_heads, g = a.group;
+  const int s = pair / hkv, kvh = pair - s * hkv;
+  const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
+  const int64_t row0 = int64_t(s) * a.num_q_heads + kvh * g;   // first q head of the group
+  QT* out = static_cast<QT*>(a.out) + row0 * D;
+  const int tid = threadIdx.x;
+  if (ctx == 0) {
+    for (int i = tid; i < g * D; i += kMergeThreads) store_out(out + i, 0.f);
+    return;
+  }
+  const bool segments = a.hdr[0] == kProtoSegments;
+  int count, w0 = 0;
+  if (segments) {
+    const int2 rec = a.recs[pair];
+    w0 = rec.x;
+    count = rec.y;
   } else {
-    count = num_parts(min(a.context_lens[s], a.max_ctx), a.part_tokens);
-    first = int64_t(row) * a.max_parts;
-    stride = 1;
+    count = num_parts(ctx, a.part_tokens);
   }
   if (count <= 1) return;                     // written directly by the decode kernel
-  const int tid = threadIdx.x;
-  float mx = -INFINITY;
-  for (int k = tid; k < count; k += kMergeThreads) mx = fmaxf(mx, a.ws_ml[(first + int64_t(k) * stride) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const int d = tid % D, pg = tid / D;
-  float L = 0.f, o = 0.f;
-#pragma unroll 4
-  for (int k = pg; k < count; k += PG) {
-    const int64_t i = first + int64_t(k) * stride;
-    const float w = a.ws_ml[i * 2 + 1] * exp2f(a.ws_ml[i * 2] - M);
-    L += w;
-    o = fmaf(w, a.ws_acc[i * D + d], o);
-  }
-  part_o[pg][d] = o;
-  if (d == 0) part_l[pg] = L;
-  __syncthreads();
-  if (pg == 0) {
-    float ot = 0.f, lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < PG; ++k) {
-      ot += part_o[k][d];
-      lt += part_l[k];
+  for (int i = tid; i < g * D; i += kMergeThreads) {
+    const int h = i / D, d = i - h * D;
+    // piece k of head h: segment (worker w0 + k; slot 1 for the first, 0 after)
+    // or partition k of the row
+    const int64_t base = segments ? int64_t(2 * w0 + 1) * g + h : (row0 + h) * a.max_parts;
+    const int64_t step = segments ? 2 * int64_t(g) : 1;
+    const int64_t fix = segments ? -int64_t(g) : 0;  // pieces after the first use slot 0
+    float mx = -INFINITY;
+    for (int k = 0; k < count; ++k) {
+      const int64_t pc = base + k * step + (k ? fix : 0);
+      mx = fmaxf(mx, a.ws_ml[pc * 2]);
     }
-    store_out(static_cast<QT*>(a.out) + int64_t(row) * D + d, ot / lt);
+    float L = 0.f, o = 0.f;
+    for (int k = 0; k < count; ++k) {
+      const int64_t pc = base + k * step + (k ? fix : 0);
+      const float wk = a.ws_ml[pc * 2 + 1] * exp2f(a.ws_ml[pc * 2] - mx);
+      L += wk;
+      o = fmaf(wk, a.ws_acc[pc * D + d], o);
+    }
+    store_out(out + i, o / L);
   }
 }
 
@@ -740,13 +726,13 @@ static int64_t max_parts_for(int32_t max_ctx, int32_t part) {
 
 static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-// Workspace: header | per-pair records | per-worker start pairs | partial rows
-// ((max, sum) then D floats each).  Sized with num_q_heads (>= num_kv_heads) so
-// the size does not depend on the pool; the partial rows cover both the vector
-// kernel's partitions and the MFMA kernel's segments (at most one per pair plus
-// one per worker, each holding a head group).
+// Workspace: header | per-pair records | partial rows ((max, sum) then D
+// floats each).  Sized with num_q_heads (>= num_kv_heads) so the size does not
+// depend on the pool; the partial rows cover both the vector kernel's
+// partitions and the MFMA kernel's segments (two slots per worker, each
+// holding a head group of at most 16 heads).
 struct WsLayout {
-  size_t recs_off, wstart_off, ml_off, acc_off, total;
+  size_t recs_off, ml_off, acc_off, total;
   int64_t parts, rows, pairs;
 };
 
@@ -756,10 +742,9 @@ static WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
   w.parts = max_parts_for(max_ctx, part);
   w.pairs = int64_t(num_seqs) * num_q_heads;
   w.recs_off = 256;
-  w.wstart_off = w.recs_off + align256(size_t(w.pairs + 1) * sizeof(int4));
-  w.ml_off = w.wstart_off + align256(size_t(kMaxWorkers) * sizeof(int32_t));
+  w.ml_off = w.recs_off + align256(size_t(w.pairs) * sizeof(int2));
   const int64_t part_rows = w.parts > 1 ? w.pairs * w.parts : 0;
-  const int64_t seg_rows = w.pairs + int64_t(kMaxWorkers) * std::min(num_q_heads, 16);
+  const int64_t seg_rows = 2 * int64_t(kMaxWorkers) * std::min<int64_t>(num_q_heads, kMaxGroup);
   w.rows = std::max(part_rows, seg_rows);
   w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
   w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
@@ -818,10 +803,8 @@ static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
   auto kernel = decode_mfma_kernel<KV, D, BS, NT>;
   DecodeArgs a = a0;
   a.workers = int32_t(std::min<int64_t>(kMaxWorkers, resident_workers(kernel)));
-  int rc = launch(plan_kernel<uint16_t, D>, dim3(1), dim3(kPlanThreads), s, a, "plan");
-  if (rc) return rc;
   return launch(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a, "decode",
-                a.recs, a.block_tables);
+                a.context_lens, a.block_tables);
 }
 
 template <int D, int BS>
@@ -912,8 +895,7 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   a->context_lens = context_lens;
   a->out = out;
   a->hdr = reinterpret_cast<int32_t*>(ws);
-  a->recs = reinterpret_cast<int4*>(ws + lay->recs_off);
-  a->wstart = reinterpret_cast<int32_t*>(ws + lay->wstart_off);
+  a->recs = reinterpret_cast<int2*>(ws + lay->recs_off);
   a->ws_ml = reinterpret_cast<float*>(ws + lay->ml_off);
   a->ws_acc = reinterpret_cast<float*>(ws + lay->acc_off);
   a->max_blocks = max_blocks_per_seq;
@@ -957,7 +939,7 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
 }
 
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
-  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_q_heads));
+  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
   const dim3 block(kMergeThreads);
   if (head_dim == 64)
     return q_dtype == PKV_F32
@@ -987,13 +969,17 @@ extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const voi
 }
 
 extern "C" int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens,
-                                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                    int32_t max_context_len, int32_t partition_size,
-                                    const void* workspace, size_t workspace_bytes, void* out,
-                                    void* stream) {
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_context_len,
+                                    int32_t partition_size, const void* workspace,
+                                    size_t workspace_bytes, void* out, void* stream) {
   clear_error();
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size < 0)
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      partition_size < 0)
     return fail(PKV_E_INVAL, "negative size");
+  if (num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > kMaxGroup)
+    return fail(PKV_E_INVAL, "num_q_heads %d is not a multiple (at most %d) of num_kv_heads %d",
+                num_q_heads, kMaxGroup, num_kv_heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_E_UNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return fail(PKV_E_INVAL, "bad q_dtype");
@@ -1009,11 +995,13 @@ extern "C" int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens
   a.context_lens = context_lens;
   a.out = out;
   a.hdr = reinterpret_cast<int32_t*>(ws);
-  a.recs = reinterpret_cast<int4*>(ws + lay.recs_off);
+  a.recs = reinterpret_cast<int2*>(ws + lay.recs_off);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   a.ws_acc = reinterpret_cast<float*>(ws + lay.acc_off);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
   a.max_ctx = max_context_len;
   a.part_tokens = lay.parts > 1 ? partition_size : 0;
   a.max_parts = int32_t(lay.parts);
