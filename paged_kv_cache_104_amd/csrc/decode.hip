@@ -421,15 +421,25 @@ __device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* 
   }
 }
 
+// 16 bytes of the query through a buffer descriptor over the whole q tensor.
+// An offset at or past the descriptor's size reads zeros without touching
+// memory, which gives the padding columns of the head group a zero query
+// with the same instruction (no branch, so every step issues the same loads).
+__device__ __forceinline__ uint4 ld16_q(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+}
+
 // Issue the loads of one step: K rows, V^T columns and the query of the pair.
-// Lanes beyond the head group load a real head of the group: their columns
-// are computed and never written.
+// Only lanes of real heads read the query (the group is padded to 16 MFMA
+// columns); the padding columns get a zero query, and their results are
+// computed and never written.
 template <int KV, int D, int BS, bool NT>
 __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
                                            const typename KvTraits<KV>::T* vp,
                                            const int (&pbs)[32 / BS], int64_t blk_stride,
-                                           const uint16_t* qrow, const LaneMap<KV, D, BS>& L,
-                                           int r) {
+                                           __amdgpu_buffer_rsrc_t qrsrc, uint32_t qoff,
+                                           bool qlane, uint32_t qoob,
+                                           const LaneMap<KV, D, BS>& L, int r) {
   const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
   const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
   const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
@@ -447,7 +457,8 @@ __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename Kv
     else R.v[j] = ld16<NT>(col);
   }
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) R.q[i] = ld16<false>(qrow + qk_dim0<KV>(i, r));
+  for (int i = 0; i < D / 32; ++i)
+    R.q[i] = ld16_q(qrsrc, qlane ? qoff + 2u * uint32_t(qk_dim0<KV>(i, r)) : qoob);
 }
 
 // A position in the step stream: pair (sequence s, KV head kvh), the pair's
@@ -606,7 +617,11 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   const LaneMap<KV, D, BS> L(r, c);
   const float sl2 = a.qk_scale_log2;
   const int g = a.group, hkv = a.num_kv_heads, max_ctx = a.max_ctx;
-  const int cmin = min(c, g - 1);
+  const bool qlane = c < g;
+  // q is [num_seqs][num_q_heads][D] bf16; its size fits 31 bits (checked on the host)
+  const uint32_t qbytes = uint32_t(a.num_seqs) * uint32_t(a.num_q_heads) * uint32_t(D) * 2u;
+  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(qbase), 0, int(qbytes), 0x00020000);
 
   Cursor la = cu;                                  // load cursor
   int la_left = rem;                               // steps the load cursor still has to load
@@ -626,8 +641,8 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   do {                                                                                         \
     issue_step<KV, D, BS, NT>(R, k_pool + int64_t(la.kvh) * head_stride,                       \
                               v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride,      \
-                              qbase + (int64_t(la.s) * a.num_q_heads + la.kvh * g + cmin) * D, \
-                              L, r);                                                           \
+                              qrsrc, uint32_t((la.s * a.num_q_heads + la.kvh * g + c) * D * 2), \
+                              qlane, qbytes, L, r);                                            \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
       if (++la.x == la.n) next_pair(la, lens, hkv, max_ctx);                                   \
@@ -664,54 +679,74 @@ done:
 
 // out = sum_k w_k * o_k / sum_k w_k with w_k = l_k * 2^(m_k - max_k m_k): the
 // same rescaling the running softmax applies between tiles.  One workgroup per
-// (sequence, KV head) pair covers the pair's head group.  The pieces are the
-// vector kernel's partitions or the MFMA kernel's segments, whichever wrote
-// the workspace last (its header says which).  Empty contexts get zeros here.
+// (sequence, q head); its threads split the pieces into kMergeThreads / D
+// groups that accumulate independently.  The pieces are the vector kernel's
+// partitions or the MFMA kernel's segments, whichever wrote the workspace last
+// (its header says which).  Empty contexts get zeros here.
 constexpr int kMergeThreads = 256;
 
 template <typename QT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  const int pair = blockIdx.x;
-  const int hkv = a.num_kv_heads, g = a.group;
-  const int s = pair / hkv, kvh = pair - s * hkv;
+  constexpr int PG = kMergeThreads / D;       // piece groups
+  __shared__ float red[kMergeThreads];
+  __shared__ float part_o[PG][D];
+  __shared__ float part_l[PG];
+  const int row = blockIdx.x;                 // s * Hq + h
+  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
+  const int g = a.group, kvh = h / g, hg = h - kvh * g;
   const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
-  const int64_t row0 = int64_t(s) * a.num_q_heads + kvh * g;   // first q head of the group
-  QT* out = static_cast<QT*>(a.out) + row0 * D;
+  QT* out = static_cast<QT*>(a.out) + int64_t(row) * D;
   const int tid = threadIdx.x;
   if (ctx == 0) {
-    for (int i = tid; i < g * D; i += kMergeThreads) store_out(out + i, 0.f);
+    if (tid < D) store_out(out + tid, 0.f);
     return;
   }
-  const bool segments = a.hdr[0] == kProtoSegments;
-  int count, w0 = 0;
-  if (segments) {
-    const int2 rec = a.recs[pair];
-    w0 = rec.x;
+  // piece k is row first + k * stride (+ fix for k > 0)
+  int count;
+  int64_t first, stride, fix = 0;
+  if (a.hdr[0] == kProtoSegments) {
+    // segments of workers w0 .. w0+count-1: slot 1 of the first, slot 0 after
+    const int2 rec = a.recs[int64_t(s) * a.num_kv_heads + kvh];
     count = rec.y;
+    first = int64_t(2 * rec.x + 1) * g + hg;
+    stride = 2 * int64_t(g);
+    fix = -int64_t(g);
   } else {
     count = num_parts(ctx, a.part_tokens);
+    first = int64_t(row) * a.max_parts;
+    stride = 1;
   }
   if (count <= 1) return;                     // written directly by the decode kernel
-  for (int i = tid; i < g * D; i += kMergeThreads) {
-    const int h = i / D, d = i - h * D;
-    // piece k of head h: segment (worker w0 + k; slot 1 for the first, 0 after)
-    // or partition k of the row
-    const int64_t base = segments ? int64_t(2 * w0 + 1) * g + h : (row0 + h) * a.max_parts;
-    const int64_t step = segments ? 2 * int64_t(g) : 1;
-    const int64_t fix = segments ? -int64_t(g) : 0;  // pieces after the first use slot 0
-    float mx = -INFINITY;
-    for (int k = 0; k < count; ++k) {
-      const int64_t pc = base + k * step + (k ? fix : 0);
-      mx = fmaxf(mx, a.ws_ml[pc * 2]);
+  float mx = -INFINITY;
+  for (int k = tid; k < count; k += kMergeThreads)
+    mx = fmaxf(mx, a.ws_ml[(first + k * stride + (k ? fix : 0)) * 2]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const int d = tid % D, pg = tid / D;
+  float L = 0.f, o = 0.f;
+#pragma unroll 4
+  for (int k = pg; k < count; k += PG) {
+    const int64_t pc = first + k * stride + (k ? fix : 0);
+    const float wk = a.ws_ml[pc * 2 + 1] * exp2f(a.ws_ml[pc * 2] - M);
+    L += wk;
+    o = fmaf(wk, a.ws_acc[pc * D + d], o);
+  }
+  part_o[pg][d] = o;
+  if (d == 0) part_l[pg] = L;
+  __syncthreads();
+  if (pg == 0) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < PG; ++k) {
+      ot += part_o[k][d];
+      lt += part_l[k];
     }
-    float L = 0.f, o = 0.f;
-    for (int k = 0; k < count; ++k) {
-      const int64_t pc = base + k * step + (k ? fix : 0);
-      const float wk = a.ws_ml[pc * 2 + 1] * exp2f(a.ws_ml[pc * 2] - mx);
-      L += wk;
-      o = fmaf(wk, a.ws_acc[pc * D + d], o);
-    }
-    store_out(out + i, o / L);
+    store_out(out + d, ot / lt);
   }
 }
 
@@ -868,7 +903,8 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   if (int64_t(max_blocks_per_seq) * c->block_size < max_context_len)
     return fail(PKV_E_INVAL, "max_blocks_per_seq %d cannot hold max_context_len %d",
                 max_blocks_per_seq, max_context_len);
-  if (int64_t(num_seqs) * c->num_kv_heads * ((int64_t(max_context_len) + 31) / 32) >= (1 << 30))
+  if (int64_t(num_seqs) * c->num_kv_heads * ((int64_t(max_context_len) + 31) / 32) >= (1 << 30) ||
+      int64_t(num_seqs) * num_q_heads * c->head_dim * 4 >= (int64_t(1) << 31))
     return fail(PKV_E_INVAL, "batch too large for one call");
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
     return fail(PKV_E_INVAL, "q_dtype must be f32 or bf16");
@@ -939,7 +975,7 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
 }
 
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
-  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
+  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_q_heads));
   const dim3 block(kMergeThreads);
   if (head_dim == 64)
     return q_dtype == PKV_F32
