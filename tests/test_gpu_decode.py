@@ -228,3 +228,50 @@ def test_shared_blocks_hint_changes_nothing():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     with pytest.raises(pkv.PagedKVError):
         g.decode(0, 0x200)
+
+
+def test_workspace_contents_never_matter():
+    """Whatever the workspace held before (zeros, 0xFF, random bytes, the previous call's
+    partial rows, another batch's), the output is bit-identical: every call writes what it
+    later reads."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = workloads.random_small(304, S=6, Hq=8, Hkv=2, D=128, B=16, max_ctx=3000, min_ctx=700,
+                                kv_dtype="bf16", in_dtype="bf16")
+    g = GpuState(wl)
+    st = oracle_run(wl)
+    ref = oracle_decode(st)
+    S, Hq, D = g.q.shape
+    n = pkv.decode_workspace_bytes(S, Hq, D, wl.max_context_len, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    outs = []
+    for fill in ("zeros", "ones", "random", "reuse", "reuse"):
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(0xFF)
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, (n,), generator=gen, dtype=torch.uint8))
+        out = torch.empty_like(g.q)
+        g.cache.decode(g.q, out, g.tables, g.lens, wl.scale, wl.max_context_len, 0, ws,
+                       impl=pkv.IMPL_MFMA)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert np.abs(out_host(outs[0]) - ref).max() <= TOL["bf16"]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    # a different batch (the first half of the sequences) on the same workspace, then the
+    # full batch again
+    half = S // 2
+    out_h = torch.empty_like(g.q[:half])
+    g.cache.decode(g.q[:half].contiguous(), out_h, g.tables[:half].contiguous(),
+                   g.lens[:half].contiguous(), wl.scale, wl.max_context_len, 0, ws,
+                   impl=pkv.IMPL_MFMA)
+    out = torch.empty_like(g.q)
+    g.cache.decode(g.q, out, g.tables, g.lens, wl.scale, wl.max_context_len, 0, ws,
+                   impl=pkv.IMPL_MFMA)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), outs[0].view(torch.int16))
+    assert np.abs(out_host(out_h) - ref[:half]).max() <= TOL["bf16"]

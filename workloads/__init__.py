@@ -248,14 +248,26 @@ def mha13b_bf16_churn() -> Workload:
                               "(median 600, sigma 0.8, clip [16,4096]), churned pool")
 
 
-def gqa8b(kv_dtype: str = "fp8") -> Workload:
-    """8B-like GQA layer: 128 seqs, 32 q / 8 KV heads, D=128, ctx U[1024,8192]."""
+def gqa8b(kv_dtype: str = "fp8", block_size: int = 16) -> Workload:
+    """8B-like GQA layer: 128 seqs, 32 q / 8 KV heads, D=128, ctx U[1024,8192].
+
+    ``block_size`` other than 16 gives the block-size sweep's variants: the same
+    contexts and the same drawn K/V, in a pool of the other block size.
+    """
     ctx = _rng(4, _TAG_META, 0).integers(1024, 8192, size=128, endpoint=True)
-    name = "8b-gqa-" + kv_dtype
-    w = _plain(name, 4, 128, 32, 8, 128, 16, ctx, kv_dtype, "bf16", 1024,
+    name = "8b-gqa-" + kv_dtype + ("" if block_size == 16 else f"-b{block_size}")
+    w = _plain(name, 4, 128, 32, 8, 128, block_size, ctx, kv_dtype, "bf16", 1024,
                description=f"8B-like GQA layer, {kv_dtype} KV, 128 seqs, 32q/8kv, "
-                           "ctx U[1024,8192]")
+                           f"ctx U[1024,8192], {block_size}-token blocks")
     return w
+
+
+def mqa_bf16() -> Workload:
+    """Multi-query layer: 128 seqs, 16 q heads sharing one KV head, D=128, ctx U[1024,8192]."""
+    ctx = _rng(4, _TAG_META, 0).integers(1024, 8192, size=128, endpoint=True)
+    return _plain("mqa-16q-bf16", 7, 128, 16, 1, 128, 16, ctx, "bf16", "bf16", 0,
+                  description="multi-query layer, bf16 KV, 128 seqs, 16 q heads / 1 KV head, "
+                              "ctx U[1024,8192]")
 
 
 def shared_prefix_bf16() -> Workload:
@@ -314,6 +326,9 @@ CONFIGS: Dict[str, Callable[[], Workload]] = {
     "13b-mha-bf16-churn": mha13b_bf16_churn,
     "8b-gqa-fp8": lambda: gqa8b("fp8"),
     "8b-gqa-bf16": lambda: gqa8b("bf16"),
+    "8b-gqa-bf16-b8": lambda: gqa8b("bf16", 8),
+    "8b-gqa-bf16-b32": lambda: gqa8b("bf16", 32),
+    "mqa-16q-bf16": mqa_bf16,
     "shared-prefix-bf16": shared_prefix_bf16,
     "long-32k-bf16": long_context_bf16,
 }
