@@ -64,13 +64,17 @@ class BlockAllocator:
     def blocks_needed(self, n_tokens: int) -> int:
         return -(-n_tokens // self.block_size)
 
+    def available(self) -> int:
+        """Blocks an allocation may take (the free list here)."""
+        return len(self.free)
+
     # -- operations ----------------------------------------------------------
     def add_seq(self, seq: int, n_tokens: int) -> List[int]:
         """Admit a sequence holding ``n_tokens`` tokens; returns its block table."""
         if seq in self.tables or n_tokens < 0:
             raise ValueError("bad add_seq")
         need = self.blocks_needed(n_tokens)
-        if need > len(self.free):
+        if need > self.available():
             raise NoMemory(seq)
         self.tables[seq] = [self._pop() for _ in range(need)]
         self.lens[seq] = n_tokens
@@ -93,11 +97,11 @@ class BlockAllocator:
         table = self.tables[seq]
         pair = None
         if pos % self.block_size == 0:                   # last block full (or none yet)
-            if not self.free:
+            if not self.available():
                 raise NoMemory(seq)
             table.append(self._pop())
         elif self.ref[table[-1]] > 1:                    # shared, partly filled: copy on write
-            if not self.free:
+            if not self.available():
                 raise NoMemory(seq)
             old = table[-1]
             new = self._pop()
@@ -127,7 +131,7 @@ class BlockAllocator:
             if self.ref[last] - drop.get(last, 0) > 1:
                 need += 1
                 drop[last] = drop.get(last, 0) + 1
-        if need > len(self.free):
+        if need > self.available():
             raise NoMemory(seqs)
         slots, pairs = [], []
         for s in seqs:
@@ -146,7 +150,7 @@ class BlockAllocator:
         need = self.blocks_needed(max(0, n - have))
         if n > 0 and have > 0 and self.ref[self.tables[seq][-1]] > 1:
             need += 1
-        if need > len(self.free):
+        if need > self.available():
             raise NoMemory(seq)
         slots, pairs = [], []
         for _ in range(n):
