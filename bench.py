@@ -75,18 +75,19 @@ def build_gpu_state(wl, workers: int):
     k_scale, v_scale = wl.kv_scales()
     desc = pkv.cache_desc(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
                           wl.kv_dtype, k_scale, v_scale)
-    cache = PagedKVCache(desc, wl.free_order, device="cuda", poison=True)
+    cache = PagedKVCache(desc, wl.free_order, device="cuda", poison=True,
+                         prefix_caching=wl.prefix_caching)
     feeder = workloads.KVFeeder(wl, workloads.ops_seq_order(wl.setup_ops), workers=workers)
     last = {int(s): int(c) - 1 for s, c in zip(wl.decode_seqs, wl.ctx_lens)}
     rows = {}
 
     def source(seq):
         k, v = feeder(seq)
-        if seq not in rows:
+        if seq in last and seq not in rows:
             rows[seq] = (k[last[seq]].copy(), v[last[seq]].copy())
         return k, v
 
-    live = set(last)
+    live = wl.data_seqs()
     try:
         cache.run_script(wl.setup_ops, source, wl.in_dtype, keep=lambda s: s in live)
         for s in wl.decode_seqs:
@@ -215,7 +216,9 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
             b = int(row[j])
             fill[b] = max(fill.get(b, 0), min(B, int(n) - j * B))
     unique_bytes = float(sum(fill.values())) * bytes_per_token
+    cache_stats = cache.bm.cache_stats() if wl.prefix_caching else None
     return dict(wall=wall, kv_bytes=kvb, t_write=t_write, t_attn=t_attn, t_merge=t_merge,
+                cache_stats=cache_stats,
                 t_attn_diag=t_attn_diag, host_s=host_s[warmup:warmup + steps],
                 max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs, shared=shared,
                 unique_ratio=unique_bytes / float(kvb[-1]))
@@ -333,6 +336,7 @@ def main() -> int:
             "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
             "mean_context": round(mean_ctx, 1), "partition_size": ps,
             "kv_loads": "cached (shared blocks)" if r["shared"] else "streaming",
+            "prefix_cache": r["cache_stats"],
             "description": wl.description,
         },
         "decode_tokens_per_s": round(wl.num_seqs * args.steps / wall, 1),

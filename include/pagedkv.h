@@ -271,6 +271,54 @@ int64_t pkv_bm_seq_len(pkv_bm* bm, int64_t seq);
 /* copy the free list (head first) into out[cap]; returns its length */
 int32_t pkv_bm_free_list(pkv_bm* bm, int32_t* out, int32_t cap);
 
+/* ------------------------------------------------------------------ prefix caching
+ *
+ * Full blocks found again by their tokens and every token before them (review of
+ * the vLLM paper, the paragraphs on prefix caching; glossary "Sharing blocks
+ * between sequences"), so a request whose prompt starts with full blocks an
+ * earlier request computed reuses them (multi-turn dialogue, shared system
+ * prompts).
+ *  - Keys are exact token prefixes (a trie, no hashing: two prefixes never
+ *    collide).  Only full blocks have keys; a lookup takes the longest run of
+ *    cached full blocks from the start of the prompt.
+ *  - A cached block whose count falls to zero keeps its key and becomes
+ *    evictable; a lookup that finds it revives it.  Blocks come from the free
+ *    list first, then from the evictable block released longest ago, which
+ *    loses its key.  A released sequence's cached blocks join the evictable
+ *    queue last block first (a prefix outlives the blocks that extend it); its
+ *    uncached blocks return to the free list's tail in logical order.
+ *  - A block that fills takes its key unless another block already holds it.
+ *  - Only sequences admitted with their tokens (pkv_bm_add_seq_tokens) take
+ *    part; sequences admitted by count never hit and never register.  Forks
+ *    inherit their parent's tokens.
+ * Token ids are int32 host arrays owned by the caller.
+ *
+ * pkv_bm_set_prefix_caching -- turn caching on (1) or off (0); only while the
+ *   manager holds no sequence (PKV_E_INVAL otherwise).  Off returns the
+ *   evictable blocks to the free list in queue order.
+ * pkv_bm_lookup -- tokens a prompt would find cached (a multiple of B), no change.
+ * pkv_bm_add_seq_tokens -- admit a sequence with its n tokens; *cached_tokens
+ *   receives how many leading tokens were found cached (their KV is already in
+ *   the pool; the caller writes tokens [*cached_tokens, n) only).
+ *   All-or-nothing; PKV_E_NOMEM counts cached blocks it would revive.
+ * pkv_bm_append_batch_tokens / pkv_bm_extend_tokens -- pkv_bm_append_batch /
+ *   pkv_bm_extend with the new tokens' ids, so blocks they fill get keys.
+ * pkv_bm_cache_stats -- out[0] cached blocks, out[1] evictable blocks,
+ *   out[2] prompt tokens found cached, out[3] prompt tokens looked up.
+ * pkv_bm_evictable_list -- the evictable queue, released longest ago first
+ *   (returns its length; copies at most cap entries).
+ */
+int pkv_bm_set_prefix_caching(pkv_bm* bm, int32_t enable);
+int pkv_bm_lookup(pkv_bm* bm, const int32_t* tokens, int64_t n, int64_t* cached_tokens);
+int pkv_bm_add_seq_tokens(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                          int64_t* cached_tokens);
+int pkv_bm_append_batch_tokens(pkv_bm* bm, const int64_t* seqs, const int32_t* tokens, int32_t n,
+                               int64_t* slots, int64_t* pairs, int32_t* num_pairs);
+int pkv_bm_extend_tokens(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                         int64_t* slots, int64_t* cow_src, int64_t* cow_dst);
+int pkv_bm_cache_stats(pkv_bm* bm, int64_t* out);
+int32_t pkv_bm_evictable_list(pkv_bm* bm, int32_t* out, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

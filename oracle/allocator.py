@@ -242,6 +242,19 @@ def run_ops(alloc: BlockAllocator, ops) -> List[tuple]:
                 events.append(("copy", pairs))
             for s, p, sl in zip(seqs, starts, slots):
                 events.append(("write", s, [p], [sl]))
+        elif kind == "add_tokens":                  # prefix caching: cached tokens are not written
+            _, seq, toks = op
+            _, cached = alloc.add_seq_tokens(seq, toks)
+            n = len(toks)
+            if n > cached:
+                events.append(("write", seq, list(range(cached, n)), alloc.slots(seq, cached, n - cached)))
+        elif kind == "extend_tokens":
+            _, seq, toks = op
+            start = alloc.lens[seq]
+            slots, pairs = alloc.extend_tokens(seq, toks)
+            if pairs:
+                events.append(("copy", pairs))
+            events.append(("write", seq, list(range(start, start + len(toks))), slots))
         else:
             raise ValueError(kind)
     return events

@@ -87,6 +87,13 @@ _SIGNATURES = {
     "pkv_bm_refcount": (_i32, [_vp, _i32]),
     "pkv_bm_seq_len": (_i64, [_vp, _i64]),
     "pkv_bm_free_list": (_i32, [_vp, _pi32, _i32]),
+    "pkv_bm_set_prefix_caching": (ctypes.c_int, [_vp, _i32]),
+    "pkv_bm_lookup": (ctypes.c_int, [_vp, _pi32, _i64, _pi64]),
+    "pkv_bm_add_seq_tokens": (ctypes.c_int, [_vp, _i64, _pi32, _i64, _pi64]),
+    "pkv_bm_append_batch_tokens": (ctypes.c_int, [_vp, _pi64, _pi32, _i32, _pi64, _pi64, _pi32]),
+    "pkv_bm_extend_tokens": (ctypes.c_int, [_vp, _i64, _pi32, _i64, _pi64, _pi64, _pi64]),
+    "pkv_bm_cache_stats": (ctypes.c_int, [_vp, _pi64]),
+    "pkv_bm_evictable_list": (_i32, [_vp, _pi32, _i32]),
 }
 
 
@@ -406,4 +413,62 @@ class BlockManager:
         n = lib.pkv_bm_free_list(self._h, None, 0)
         out = np.empty(max(1, n), dtype=np.int32)
         lib.pkv_bm_free_list(self._h, _np_ptr(out, ctypes.c_int32), n)
+        return out[:n].tolist()
+
+    # -- prefix caching ------------------------------------------------------
+    def set_prefix_caching(self, enable: bool = True) -> None:
+        _check(lib.pkv_bm_set_prefix_caching(self._h, 1 if enable else 0))
+
+    @staticmethod
+    def _tokens(tokens) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.int32))
+
+    def lookup(self, tokens) -> int:
+        t = self._tokens(tokens)
+        out = ctypes.c_int64()
+        _check(lib.pkv_bm_lookup(self._h, _np_ptr(t, ctypes.c_int32), len(t), ctypes.byref(out)))
+        return out.value
+
+    def add_seq_tokens(self, seq: int, tokens) -> int:
+        """Admit a sequence with its tokens; returns how many leading tokens were cached."""
+        t = self._tokens(tokens)
+        out = ctypes.c_int64()
+        _check(lib.pkv_bm_add_seq_tokens(self._h, seq, _np_ptr(t, ctypes.c_int32), len(t),
+                                         ctypes.byref(out)))
+        return out.value
+
+    def append_batch_tokens(self, seqs: Iterable[int], tokens) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        t = self._tokens(tokens)
+        if len(t) != len(s):
+            raise ValueError("one token per sequence")
+        slots = np.empty(len(s), dtype=np.int64)
+        pairs = np.empty((max(1, len(s)), 2), dtype=np.int64)
+        n = ctypes.c_int32()
+        _check(lib.pkv_bm_append_batch_tokens(self._h, _np_ptr(s, ctypes.c_int64),
+                                              _np_ptr(t, ctypes.c_int32), len(s),
+                                              _np_ptr(slots, ctypes.c_int64),
+                                              _np_ptr(pairs, ctypes.c_int64), ctypes.byref(n)))
+        return slots, pairs[: n.value].copy()
+
+    def extend_tokens(self, seq: int, tokens) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        t = self._tokens(tokens)
+        n = len(t)
+        slots = np.empty(max(1, n), dtype=np.int64)
+        src, dst = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.pkv_bm_extend_tokens(self._h, seq, _np_ptr(t, ctypes.c_int32), n,
+                                        _np_ptr(slots, ctypes.c_int64), ctypes.byref(src),
+                                        ctypes.byref(dst)))
+        return slots[:n].copy(), ([(src.value, dst.value)] if src.value >= 0 else [])
+
+    def cache_stats(self) -> dict:
+        out = np.zeros(4, dtype=np.int64)
+        _check(lib.pkv_bm_cache_stats(self._h, _np_ptr(out, ctypes.c_int64)))
+        return {"cached_blocks": int(out[0]), "evictable_blocks": int(out[1]),
+                "hit_tokens": int(out[2]), "query_tokens": int(out[3])}
+
+    def evictable_list(self) -> List[int]:
+        n = lib.pkv_bm_evictable_list(self._h, None, 0)
+        out = np.empty(max(1, n), dtype=np.int32)
+        lib.pkv_bm_evictable_list(self._h, _np_ptr(out, ctypes.c_int32), n)
         return out[:n].tolist()

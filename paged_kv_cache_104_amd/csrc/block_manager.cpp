@@ -12,10 +12,26 @@
 //   - freeing a sequence drops one count per block; blocks at zero go to the
 //     tail of the free list, in the sequence's logical order.
 // Every operation checks first and then mutates, so failures change nothing.
+//
+// Prefix caching (optional; review of the vLLM paper, the paragraphs on prefix
+// caching; glossary "Sharing blocks between sequences"): a full block is known
+// by its own tokens and every token before it, and a request whose prompt
+// starts with cached full blocks reuses them.  The keys live in a trie with
+// one node per full block's token prefix (a node's identity is exactly that
+// prefix, so no two prefixes collide); a node names the block that caches it,
+// if any.  Lookups take the longest cached run of full blocks from the start.
+// A cached block whose count falls to zero stays findable and becomes
+// evictable; blocks come from the free list first, then from the evictable
+// block released longest ago, which loses its key.  A released sequence's
+// cached blocks join the evictable queue last block first; its uncached blocks
+// return to the free list as above.  A block that fills takes its key unless
+// another block already holds it.
 #include <algorithm>
 #include <cstring>
 #include <deque>
+#include <list>
 #include <new>
+#include <string>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -24,9 +40,22 @@
 
 namespace {
 
+// One full block's token prefix: its tokens (the key in the parent's map) under
+// the node of the prefix before it.
+struct Node {
+  Node* parent = nullptr;
+  std::string key;
+  std::unordered_map<std::string, Node*> children;
+  int32_t block = -1;   // the block caching this prefix, or -1
+  int64_t users = 0;    // sequence paths through it, children, and its block
+};
+
 struct Seq {
   std::vector<int32_t> blocks;
   int64_t len = 0;
+  bool tracked = false;          // admitted with its tokens (prefix caching)
+  std::vector<int32_t> tokens;   // tracked sequences only
+  std::vector<Node*> path;       // trie node of each full block (tracked only)
 };
 
 }  // namespace
@@ -38,11 +67,112 @@ struct pkv_bm {
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
 
+  // prefix caching
+  bool caching = false;
+  Node root;
+  std::vector<Node*> node_of;                         // block -> node it caches
+  std::list<int32_t> evictable;                       // released longest ago first
+  std::vector<std::list<int32_t>::iterator> ev_pos;   // valid while ev_in[b]
+  std::vector<char> ev_in;
+  int64_t hit_tokens = 0, query_tokens = 0, cached_blocks = 0;
+
+  ~pkv_bm() { drop_children(&root); }
+
+  static void drop_children(Node* n) {
+    for (auto& kv : n->children) {
+      drop_children(kv.second);
+      delete kv.second;
+    }
+    n->children.clear();
+  }
+
+  int64_t available() const { return int64_t(free_list.size()) + int64_t(evictable.size()); }
+
+  void release(Node* n) {
+    while (n != &root && --n->users == 0) {
+      Node* p = n->parent;
+      p->children.erase(n->key);
+      delete n;
+      n = p;
+    }
+  }
+
+  Node* child_of(Node* p, const int32_t* toks) {
+    std::string k(reinterpret_cast<const char*>(toks), sizeof(int32_t) * size_t(block_size));
+    auto it = p->children.find(k);
+    if (it != p->children.end()) return it->second;
+    Node* c = new Node();
+    c->parent = p;
+    c->key = std::move(k);
+    p->children.emplace(c->key, c);
+    p->users += 1;
+    return c;
+  }
+
+  Node* find_child(Node* p, const int32_t* toks) const {
+    std::string k(reinterpret_cast<const char*>(toks), sizeof(int32_t) * size_t(block_size));
+    auto it = p->children.find(k);
+    return it == p->children.end() ? nullptr : it->second;
+  }
+
+  void uncache(int32_t b) {
+    Node* n = node_of[b];
+    n->block = -1;
+    node_of[b] = nullptr;
+    cached_blocks -= 1;
+    release(n);
+  }
+
+  // A block for a new use: the free list's head, else the evictable block
+  // released longest ago (which loses its key).  The caller has checked that
+  // one is available.
   int32_t pop_free() {
-    int32_t b = free_list.front();
-    free_list.pop_front();
+    int32_t b;
+    if (!free_list.empty()) {
+      b = free_list.front();
+      free_list.pop_front();
+    } else {
+      b = evictable.front();
+      evictable.pop_front();
+      ev_in[b] = 0;
+      uncache(b);
+    }
     ref[b] = 1;
     return b;
+  }
+
+  // Full block i of a tracked sequence: extend its trie path, and let the block
+  // take the key if neither the key nor the block is taken.
+  void register_block(Seq& s, int64_t i) {
+    Node* p = i == 0 ? &root : s.path[i - 1];
+    Node* n = child_of(p, s.tokens.data() + i * block_size);
+    n->users += 1;
+    s.path.push_back(n);
+    const int32_t b = s.blocks[i];
+    if (n->block < 0 && !node_of[b]) {
+      n->block = b;
+      node_of[b] = n;
+      n->users += 1;
+      cached_blocks += 1;
+    }
+  }
+
+  void note_tokens(Seq& s, const int32_t* toks, int64_t n) {
+    if (!s.tracked) return;
+    s.tokens.insert(s.tokens.end(), toks, toks + n);
+    const int64_t full = int64_t(s.tokens.size()) / block_size;
+    for (int64_t i = int64_t(s.path.size()); i < full; ++i) register_block(s, i);
+  }
+
+  // cached blocks of the longest run of full blocks from the start of toks
+  void lookup(const int32_t* toks, int64_t n, std::vector<int32_t>* hits) const {
+    const Node* p = &root;
+    for (int64_t i = 0; i < n / block_size; ++i) {
+      const Node* c = find_child(const_cast<Node*>(p), toks + i * block_size);
+      if (!c || c->block < 0) break;
+      hits->push_back(c->block);
+      p = c;
+    }
   }
 
   int64_t slot_of(const Seq& s, int64_t pos) const {
@@ -127,9 +257,9 @@ int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int64_t num_tokens) {
   if (num_tokens < 0) return fail(PKV_E_INVAL, "negative num_tokens");
   if (bm->seqs.count(seq)) return fail(PKV_E_INVAL, "sequence %lld exists", (long long)seq);
   const int64_t need = (num_tokens + bm->block_size - 1) / bm->block_size;
-  if (need > int64_t(bm->free_list.size()))
-    return fail(PKV_E_NOMEM, "add_seq needs %lld blocks, %zu free", (long long)need,
-                bm->free_list.size());
+  if (need > bm->available())
+    return fail(PKV_E_NOMEM, "add_seq needs %lld blocks, %lld available", (long long)need,
+                (long long)bm->available());
   Seq s;
   s.blocks.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->pop_free());
@@ -145,6 +275,7 @@ int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
   if (bm->seqs.count(child)) return fail(PKV_E_INVAL, "child %lld exists", (long long)child);
   Seq s = it->second;
   for (int32_t b : s.blocks) bm->ref[b] += 1;
+  for (Node* n : s.path) n->users += 1;
   bm->seqs.emplace(child, std::move(s));
   return PKV_OK;
 }
@@ -153,8 +284,8 @@ int pkv_bm_append(pkv_bm* bm, int64_t seq, int64_t* slot, int64_t* cow_src, int6
   if (!bm || !slot || !cow_src || !cow_dst) return fail(PKV_E_INVAL, "NULL argument");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
-  if (bm->needs_block(it->second) && bm->free_list.empty())
-    return fail(PKV_E_NOMEM, "append needs a block, none free");
+  if (bm->needs_block(it->second) && bm->available() == 0)
+    return fail(PKV_E_NOMEM, "append needs a block, none available");
   *slot = bm->append_one(it->second, cow_src, cow_dst);
   return PKV_OK;
 }
@@ -189,9 +320,9 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* slo
       dropped[last] = drop + 1;
     }
   }
-  if (need > int64_t(bm->free_list.size()))
-    return fail(PKV_E_NOMEM, "append_batch needs %lld blocks, %zu free", (long long)need,
-                bm->free_list.size());
+  if (need > bm->available())
+    return fail(PKV_E_NOMEM, "append_batch needs %lld blocks, %lld available", (long long)need,
+                (long long)bm->available());
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
     int64_t src, dst;
@@ -217,9 +348,9 @@ int pkv_bm_extend(pkv_bm* bm, int64_t seq, int64_t n, int64_t* slots, int64_t* c
   const int64_t rest = n > have ? n - have : 0;
   int64_t need = (rest + bm->block_size - 1) / bm->block_size;
   if (n > 0 && have > 0 && bm->ref[s.blocks.back()] > 1) ++need;
-  if (need > int64_t(bm->free_list.size()))
-    return fail(PKV_E_NOMEM, "extend needs %lld blocks, %zu free", (long long)need,
-                bm->free_list.size());
+  if (need > bm->available())
+    return fail(PKV_E_NOMEM, "extend needs %lld blocks, %lld available", (long long)need,
+                (long long)bm->available());
   *cow_src = *cow_dst = -1;
   for (int64_t i = 0; i < n; ++i) {
     int64_t src, dst;
@@ -236,10 +367,21 @@ int pkv_bm_free_seq(pkv_bm* bm, int64_t seq) {
   if (!bm) return fail(PKV_E_INVAL, "NULL manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
+  std::vector<int32_t> zero;
   for (int32_t b : it->second.blocks) {
     bm->ref[b] -= 1;
-    if (bm->ref[b] == 0) bm->free_list.push_back(b);
+    if (bm->ref[b] == 0) zero.push_back(b);
   }
+  for (int32_t b : zero)
+    if (!bm->caching || !bm->node_of[b]) bm->free_list.push_back(b);
+  if (bm->caching) {
+    for (auto r = zero.rbegin(); r != zero.rend(); ++r) {
+      if (!bm->node_of[*r]) continue;
+      bm->ev_pos[*r] = bm->evictable.insert(bm->evictable.end(), *r);
+      bm->ev_in[*r] = 1;
+    }
+  }
+  for (Node* n : it->second.path) bm->release(n);
   bm->seqs.erase(it);
   return PKV_OK;
 }
@@ -309,6 +451,111 @@ int32_t pkv_bm_free_list(pkv_bm* bm, int32_t* out, int32_t cap) {
   const int32_t n = int32_t(bm->free_list.size());
   for (int32_t i = 0; i < n && i < cap; ++i) out[i] = bm->free_list[i];
   return n;
+}
+
+// ------------------------------------------------------------------ prefix caching
+
+int pkv_bm_set_prefix_caching(pkv_bm* bm, int32_t enable) {
+  if (!bm) return fail(PKV_E_INVAL, "NULL manager");
+  if (!bm->seqs.empty()) return fail(PKV_E_INVAL, "prefix caching changes only with no sequences");
+  if (enable && !bm->caching) {
+    bm->node_of.assign(bm->num_blocks, nullptr);
+    bm->ev_pos.assign(bm->num_blocks, bm->evictable.end());
+    bm->ev_in.assign(bm->num_blocks, 0);
+  } else if (!enable && bm->caching) {
+    // evictable blocks go back to the free list in queue order, without keys
+    for (int32_t b : bm->evictable) {
+      bm->ev_in[b] = 0;
+      bm->uncache(b);
+      bm->free_list.push_back(b);
+    }
+    bm->evictable.clear();
+  }
+  bm->caching = enable != 0;
+  return PKV_OK;
+}
+
+int pkv_bm_lookup(pkv_bm* bm, const int32_t* tokens, int64_t n, int64_t* cached_tokens) {
+  if (!bm || n < 0 || (n > 0 && !tokens) || !cached_tokens)
+    return fail(PKV_E_INVAL, "bad lookup arguments");
+  std::vector<int32_t> hits;
+  if (bm->caching) bm->lookup(tokens, n, &hits);
+  *cached_tokens = int64_t(hits.size()) * bm->block_size;
+  return PKV_OK;
+}
+
+int pkv_bm_add_seq_tokens(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                          int64_t* cached_tokens) {
+  if (!bm || n < 0 || (n > 0 && !tokens) || !cached_tokens)
+    return fail(PKV_E_INVAL, "bad add_seq_tokens arguments");
+  if (!bm->caching) return fail(PKV_E_INVAL, "prefix caching is off");
+  if (bm->seqs.count(seq)) return fail(PKV_E_INVAL, "sequence %lld exists", (long long)seq);
+  std::vector<int32_t> hits;
+  bm->lookup(tokens, n, &hits);
+  const int64_t need = (n + bm->block_size - 1) / bm->block_size - int64_t(hits.size());
+  int64_t revived = 0;
+  for (int32_t b : hits) revived += bm->ref[b] == 0;
+  if (need > bm->available() - revived)
+    return fail(PKV_E_NOMEM, "add_seq_tokens needs %lld blocks, %lld available", (long long)need,
+                (long long)(bm->available() - revived));
+  for (int32_t b : hits) {
+    if (bm->ref[b] == 0) {
+      bm->evictable.erase(bm->ev_pos[b]);
+      bm->ev_in[b] = 0;
+    }
+    bm->ref[b] += 1;
+  }
+  Seq s;
+  s.tracked = true;
+  s.blocks = hits;
+  s.blocks.reserve(hits.size() + need);
+  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->pop_free());
+  s.len = n;
+  Seq& live = bm->seqs.emplace(seq, std::move(s)).first->second;
+  bm->note_tokens(live, tokens, n);
+  bm->query_tokens += n;
+  bm->hit_tokens += int64_t(hits.size()) * bm->block_size;
+  *cached_tokens = int64_t(hits.size()) * bm->block_size;
+  return PKV_OK;
+}
+
+int pkv_bm_append_batch_tokens(pkv_bm* bm, const int64_t* seqs, const int32_t* tokens, int32_t n,
+                               int64_t* slots, int64_t* pairs, int32_t* num_pairs) {
+  if (!bm || (n > 0 && !tokens)) return fail(PKV_E_INVAL, "bad append_batch_tokens arguments");
+  if (!bm->caching) return fail(PKV_E_INVAL, "prefix caching is off");
+  const int rc = pkv_bm_append_batch(bm, seqs, n, slots, pairs, num_pairs);
+  if (rc) return rc;
+  for (int32_t i = 0; i < n; ++i) bm->note_tokens(bm->seqs.find(seqs[i])->second, tokens + i, 1);
+  return PKV_OK;
+}
+
+int pkv_bm_extend_tokens(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                         int64_t* slots, int64_t* cow_src, int64_t* cow_dst) {
+  if (!bm || n < 0 || (n > 0 && !tokens)) return fail(PKV_E_INVAL, "bad extend_tokens arguments");
+  if (!bm->caching) return fail(PKV_E_INVAL, "prefix caching is off");
+  const int rc = pkv_bm_extend(bm, seq, n, slots, cow_src, cow_dst);
+  if (rc) return rc;
+  bm->note_tokens(bm->seqs.find(seq)->second, tokens, n);
+  return PKV_OK;
+}
+
+int pkv_bm_cache_stats(pkv_bm* bm, int64_t* out) {
+  if (!bm || !out) return fail(PKV_E_INVAL, "NULL argument");
+  out[0] = bm->cached_blocks;
+  out[1] = int64_t(bm->evictable.size());
+  out[2] = bm->hit_tokens;
+  out[3] = bm->query_tokens;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_evictable_list(pkv_bm* bm, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  int32_t i = 0;
+  for (int32_t b : bm->evictable) {
+    if (i < cap) out[i] = b;
+    ++i;
+  }
+  return i;
 }
 
 }  // extern "C"

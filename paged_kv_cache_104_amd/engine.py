@@ -7,9 +7,11 @@ decode attention on the device.
 
 Allocator scripts are lists of operations:
 ``('add', seq, n)``, ``('fork', parent, child)``, ``('extend', seq, n)``,
-``('append_batch', [seqs])``, ``('free', seq)``.  Copy-on-write pairs are
-copied on the device before any later token write, since the last holder of a
-shared block writes into it in place.
+``('append_batch', [seqs])``, ``('free', seq)``, and with prefix caching
+``('add_tokens', seq, token_ids)`` and ``('extend_tokens', seq, token_ids)``
+(tokens found cached are not written again).  Copy-on-write pairs are copied
+on the device before any later token write, since the last holder of a shared
+block writes into it in place.
 """
 from __future__ import annotations
 
@@ -34,10 +36,12 @@ def to_device(x: np.ndarray, in_dtype: str, device):
 
 class PagedKVCache:
     def __init__(self, desc: CacheDesc, free_order: Optional[Sequence[int]] = None,
-                 device="cuda", poison: bool = True):
+                 device="cuda", poison: bool = True, prefix_caching: bool = False):
         self.desc = desc
         self.device = device
         self.bm = BlockManager(desc.num_blocks, desc.block_size, free_order)
+        if prefix_caching:
+            self.bm.set_prefix_caching(True)
         self.k_pool, self.v_pool = alloc_pools(desc, device, poison)
 
     # -- device work ------------------------------------------------------------
@@ -93,6 +97,18 @@ class PagedKVCache:
                 self.copy(pairs)
                 for s, p, sl in zip(seqs, starts, slots):
                     put(s, np.array([p]), np.array([sl]))
+            elif kind == "add_tokens":
+                _, seq, toks = op
+                n = len(toks)
+                cached = bm.add_seq_tokens(seq, toks)
+                if n > cached:
+                    put(seq, np.arange(cached, n), bm.slots(seq, cached, n - cached))
+            elif kind == "extend_tokens":
+                _, seq, toks = op
+                start = bm.seq_len(seq)
+                slots, pairs = bm.extend_tokens(seq, toks)
+                self.copy(pairs)
+                put(seq, np.arange(start, start + len(toks)), slots)
             else:
                 raise ValueError(f"unknown op {kind}")
 

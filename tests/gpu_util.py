@@ -35,17 +35,18 @@ class GpuState:
         self.pkv = pkv
         self.desc = desc_of(wl, pkv)
         fo = wl.free_order if free_order is None else free_order
-        self.cache = PagedKVCache(self.desc, fo, device="cuda", poison=poison)
+        self.cache = PagedKVCache(self.desc, fo, device="cuda", poison=poison,
+                                  prefix_caching=wl.prefix_caching)
         feeder = workloads.KVFeeder(wl, workloads.ops_seq_order(wl.setup_ops)
                                     + [int(s) for s in wl.decode_seqs], workers=workers)
-        live = set(int(s) for s in wl.decode_seqs)
+        live = wl.data_seqs()
         kp = keep if keep is not None else (lambda s: True)
         last = {int(s): int(c) - 1 for s, c in zip(wl.decode_seqs, wl.ctx_lens)}
         new_rows = {}
 
         def source(seq):
             k, v = feeder(seq)
-            if seq not in new_rows:
+            if seq in last and seq not in new_rows:
                 new_rows[seq] = (k[last[seq]].copy(), v[last[seq]].copy())
             return k, v
 

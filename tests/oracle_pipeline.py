@@ -12,6 +12,7 @@ import numpy as np
 
 from oracle import allocator as oalloc
 from oracle import attention as oattn
+from oracle import prefix_cache as oprefix
 from oracle import cache as ocache
 from oracle import codec
 
@@ -39,13 +40,21 @@ def kv_by_seq(wl):
     index = wl.seq_index()
 
     def get(seq):
-        return wl.seq_kv_input(index[int(seq)])
+        seq = int(seq)
+        if seq not in index:
+            return wl.extra_kv_input(seq)
+        return wl.seq_kv_input(index[seq])
     return get
+
+
+def new_allocator(wl):
+    cls = oprefix.PrefixCachingAllocator if wl.prefix_caching else oalloc.BlockAllocator
+    return cls(wl.num_blocks, wl.block_size, wl.free_order)
 
 
 def run(wl, fill: bool = True) -> OracleState:
     """Replay the allocator script, then the decode step's append; optionally fill pools."""
-    alloc = oalloc.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+    alloc = new_allocator(wl)
     # the churn dummies own no data: their writes are dropped
     events = oalloc.run_ops(alloc, wl.setup_ops)
     seqs = [int(s) for s in wl.decode_seqs]
@@ -59,7 +68,7 @@ def run(wl, fill: bool = True) -> OracleState:
         st.k_pool, st.v_pool = ocache.new_pools(wl.num_blocks, wl.num_kv_heads, wl.block_size,
                                                 wl.head_dim, wl.kv_dtype)
         get = kv_by_seq(wl)
-        live = set(seqs)
+        live = wl.data_seqs()
         ev = [e for e in events if e[0] == "copy" or e[1] in live]
         ocache.apply_events(st.k_pool, st.v_pool, ev, get, wl.in_dtype, wl.kv_dtype,
                             k_scale, v_scale)

@@ -20,7 +20,7 @@ from oracle import allocator as oalloc
 from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import codec
-from oracle_pipeline import kv_by_seq
+from oracle_pipeline import kv_by_seq, new_allocator
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_full_config(name):
     print(f"config {name}: GPU decode done", flush=True)
 
     # tables of every sequence
-    a = oalloc.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+    a = new_allocator(wl)
     events = oalloc.run_ops(a, wl.setup_ops)
     seqs = [int(s) for s in wl.decode_seqs]
     starts = [a.lens[s] for s in seqs]
@@ -59,6 +59,8 @@ def test_full_config(name):
     rows = _sample(wl)
     if name == "shared-prefix-bf16":
         keep = {int(s) for r in rows for s in range((r // 4) * 4, (r // 4) * 4 + 4)}
+    elif wl.prefix_caching:
+        keep = wl.data_seqs()          # cached blocks were written by other requests
     else:
         keep = {seqs[r] for r in rows}
     k_scale, v_scale = wl.kv_scales()

@@ -82,6 +82,10 @@ class Workload:
     _scales: Optional[Tuple[float, float]] = None
     _cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = dataclasses.field(default_factory=dict)
     cache_sequences: bool = False
+    # sequences outside the decode batch whose tokens are written (and may be reused
+    # through prefix caching after they end): seq id -> segments, as _segments
+    extra_segments: Dict[int, List[Tuple[int, int, int]]] = dataclasses.field(default_factory=dict)
+    prefix_caching: bool = False
 
     # ---- shapes --------------------------------------------------------------
     @property
@@ -130,6 +134,14 @@ class Workload:
             vs.append(v[first:first + n])
         return np.concatenate(ks), np.concatenate(vs)
 
+    def _segments_kv(self, segs) -> Tuple[np.ndarray, np.ndarray]:
+        ks, vs = [], []
+        for stream, first, n in segs:
+            k, v = self._stream_rows(stream, first + n)
+            ks.append(k[first:first + n])
+            vs.append(v[first:first + n])
+        return np.concatenate(ks), np.concatenate(vs)
+
     def seq_kv_input(self, i: int) -> Tuple[np.ndarray, np.ndarray]:
         """K, V of batch entry ``i`` in the input format of reshape_and_cache."""
         if i in self._cache:
@@ -140,6 +152,17 @@ class Workload:
         if self.cache_sequences:
             self._cache[i] = (k, v)
         return k, v
+
+    def extra_kv_input(self, seq: int) -> Tuple[np.ndarray, np.ndarray]:
+        """K, V (input format) of a sequence outside the decode batch."""
+        k, v = self._segments_kv(self.extra_segments[int(seq)])
+        if self.in_dtype == "bf16":
+            k, v = to_bf16_bits(k), to_bf16_bits(v)
+        return k, v
+
+    def data_seqs(self) -> set:
+        """Sequences whose tokens are written: the decode batch and the extra sequences."""
+        return {int(s) for s in self.decode_seqs} | set(self.extra_segments)
 
     def kv_scales(self) -> Tuple[float, float]:
         """fp8 per-tensor scales: amax(|K|)/448 and amax(|V|)/448 over all inputs, in fp32.
@@ -270,6 +293,69 @@ def mqa_bf16() -> Workload:
                               "ctx U[1024,8192]")
 
 
+def chat_prefix_cache_bf16() -> Workload:
+    """Chat serving with prefix caching: 8 system prompts, 128 users on their second turn
+    (the first turn ran, finished and was released earlier), 64 users on their first turn.
+
+    Token ids decide what the block manager finds cached; the K/V draws follow the
+    same structure (one random stream per system prompt, question and reply), so equal
+    token prefixes have equal K/V, as a model would give.
+    """
+    seed, B = 8, 16
+    rng = _rng(seed, _TAG_META, 0)
+    vocab = 32000
+    n_sys, users, fresh = 8, 128, 64
+    sys_len = rng.integers(1000, 2000, size=n_sys, endpoint=True)
+    sys_tok = [rng.integers(0, vocab, size=int(n)) for n in sys_len]
+    q1_len = rng.integers(32, 256, size=users, endpoint=True)
+    r1_len = rng.integers(32, 256, size=users, endpoint=True)
+    q2_len = rng.integers(16, 128, size=users, endpoint=True)
+    qf_len = rng.integers(32, 256, size=fresh, endpoint=True)
+    tok = lambda n: rng.integers(0, vocab, size=int(n))
+    q1 = [tok(n) for n in q1_len]
+    r1 = [tok(n) for n in r1_len]
+    q2 = [tok(n) for n in q2_len]
+    qf = [tok(n) for n in qf_len]
+    ops: List[Op] = []
+    extra: Dict[int, List[Tuple[int, int, int]]] = {}
+    for u in range(users):                               # first turns: ran and ended
+        k = u % n_sys
+        sid = 1_000_000 + u
+        ops.append(("add_tokens", sid, np.concatenate([sys_tok[k], q1[u]])))
+        ops.append(("extend_tokens", sid, r1[u]))
+        ops.append(("free", sid))
+        extra[sid] = [(20_000 + k, 0, int(sys_len[k])), (30_000 + u, 0, int(q1_len[u])),
+                      (40_000 + u, 0, int(r1_len[u]))]
+    segs: List[List[Tuple[int, int, int]]] = []
+    ctx = []
+    for u in range(users):                               # second turns: the decode batch
+        k = u % n_sys
+        prompt = np.concatenate([sys_tok[k], q1[u], r1[u], q2[u]])
+        ops.append(("add_tokens", u, prompt))
+        segs.append([(20_000 + k, 0, int(sys_len[k])), (30_000 + u, 0, int(q1_len[u])),
+                     (40_000 + u, 0, int(r1_len[u])), (50_000 + u, 0, int(q2_len[u]) + 1)])
+        ctx.append(len(prompt) + 1)
+    for v in range(fresh):                               # new users
+        k = (3 * v) % n_sys
+        prompt = np.concatenate([sys_tok[k], qf[v]])
+        ops.append(("add_tokens", users + v, prompt))
+        segs.append([(20_000 + k, 0, int(sys_len[k])), (60_000 + v, 0, int(qf_len[v]) + 1)])
+        ctx.append(len(prompt) + 1)
+    ctx = np.asarray(ctx, dtype=np.int64)
+    ids = np.arange(users + fresh, dtype=np.int64)
+    N = int(math.ceil(1.25 * sum(blocks_for(c, B) for c in ctx)))
+    free_order = _rng(seed, _TAG_META, 1).permutation(N).astype(np.int32)
+    return Workload(
+        name="chat-prefix-cache-bf16", seed=seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=B, num_blocks=N, kv_dtype="bf16", in_dtype="bf16",
+        scale=1.0 / math.sqrt(128), partition_size=0, free_order=free_order,
+        setup_ops=ops, decode_seqs=ids, ctx_lens=ctx, _segments=lambda i: segs[i],
+        extra_segments=extra, prefix_caching=True,
+        description="chat with prefix caching: 8 system prompts U[1000,2000] tokens, 128 "
+                    "second-turn users (first turn released and cached), 64 first-turn "
+                    "users, 32q/8kv, bf16")
+
+
 def shared_prefix_bf16() -> Workload:
     """64 prompts x 4 samples sharing a 1032-token prefix, tails U{0..512}, bf16, 32q/8kv.
 
@@ -330,6 +416,7 @@ CONFIGS: Dict[str, Callable[[], Workload]] = {
     "8b-gqa-bf16-b32": lambda: gqa8b("bf16", 32),
     "mqa-16q-bf16": mqa_bf16,
     "shared-prefix-bf16": shared_prefix_bf16,
+    "chat-prefix-cache-bf16": chat_prefix_cache_bf16,
     "long-32k-bf16": long_context_bf16,
 }
 
@@ -402,7 +489,10 @@ class KVFeeder:
         return r
 
     def __call__(self, seq: int):
-        return self.by_index(self.index[int(seq)])
+        seq = int(seq)
+        if seq not in self.index:
+            return self.wl.extra_kv_input(seq)
+        return self.by_index(self.index[seq])
 
     def close(self):
         self.ex.shutdown(wait=False, cancel_futures=True)
@@ -412,7 +502,7 @@ def ops_seq_order(ops) -> List[int]:
     """Sequence ids in the order an allocator script first writes tokens for them."""
     out = []
     for op in ops:
-        if op[0] in ("add", "extend"):
+        if op[0] in ("add", "extend", "add_tokens", "extend_tokens"):
             out.append(int(op[1]))
         elif op[0] == "append_batch":
             out.extend(int(s) for s in op[1])
