@@ -97,6 +97,26 @@ def copy_blocks(k_pool, v_pool, pairs) -> None:
         v_pool[dst] = v_pool[src]
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs) -> None:
+    """Swapping (review of the vLLM paper, preemption paragraphs): whole blocks move
+    between two pools of the same block shape, the device pool and a host pool.  For
+    each (src, dst) pair block dst of the destination pools becomes block src of the
+    source pools, K and V.  Destinations must be distinct; sources and destinations
+    index different pools, so a destination may carry a source's number."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if ((pairs[:, 0] < 0) | (pairs[:, 0] >= src_k.shape[0])).any():
+        raise ValueError("source block out of range")
+    if ((pairs[:, 1] < 0) | (pairs[:, 1] >= dst_k.shape[0])).any():
+        raise ValueError("destination block out of range")
+    if len(set(pairs[:, 1].tolist())) != len(pairs):
+        raise ValueError("duplicate destination")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:]:
+        raise ValueError("pools of different block shapes")
+    for src, dst in pairs:
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 def apply_events(k_pool, v_pool, events, kv_input, in_dtype: str, kv_dtype: str,
                  k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Run the device work of an allocator script: copies and token writes, in order.
