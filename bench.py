@@ -280,6 +280,47 @@ def copy_calibration(n_bytes: int, reps: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n_bytes, "reps": reps}))
 
 
+def swap_sweep(total_bytes: int, reps: int, methods=("kernel", "dma")) -> None:
+    """Host-link rate of swapping (K+V bytes moved / time) against block size, for the
+    one-kernel copy and for one copy-engine transfer per block.  Device blocks are a
+    random permutation and host blocks consecutive, as the block manager hands them out."""
+    import torch
+
+    import paged_kv_cache_104_amd as pkv
+
+    rows = []
+    for D in (64, 128):
+        for B in (8, 16, 32):
+            per_block = 2 * 8 * B * D * 2                  # K + V, 8 KV heads, bf16
+            n = total_bytes // per_block
+            desc = pkv.cache_desc(n, 8, B, D, "bf16")
+            dk, dv = pkv.alloc_pools(desc, poison=False)
+            hk, hv = pkv.alloc_host_pools(desc, n)
+            perm = np.random.default_rng(B * D).permutation(n)
+            out = np.stack([perm, np.arange(n)], 1)
+            back = np.stack([np.arange(n), perm], 1)
+            for method in methods:
+                res = {}
+                for name, args, pairs in (("out", (dk, dv, hk, hv), out), ("in", (hk, hv, dk, dv), back)):
+                    pkv.swap_blocks(*args, pairs, desc, method)           # warm-up
+                    torch.cuda.synchronize()
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    ts = []
+                    for _ in range(reps):
+                        ev[0].record()
+                        pkv.swap_blocks(*args, pairs, desc, method)
+                        ev[1].record()
+                        torch.cuda.synchronize()
+                        ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+                    res[name] = round(n * per_block / float(np.median(ts)) / 1e9, 2)
+                rows.append({"head_dim": D, "block_size": B, "block_bytes": per_block // 2,
+                             "blocks": int(n), "method": method, "out_GBps": res["out"],
+                             "in_GBps": res["in"]})
+                log(f"swap D={D} B={B} {method}: out {res['out']} GB/s, in {res['in']} GB/s")
+            del dk, dv, hk, hv
+    print(json.dumps({"swap_sweep": rows, "bytes_per_direction": total_bytes, "reps": reps}))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +333,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--swap-sweep", type=int, default=0, metavar="BYTES",
+                    help="measure swapping rates moving BYTES of K+V each way, then exit")
+    ap.add_argument("--swap-methods", default="kernel,dma")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -300,6 +344,9 @@ def main() -> int:
         return 2
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 10)
+        return 0
+    if args.swap_sweep:
+        swap_sweep(args.swap_sweep, 5, tuple(args.swap_methods.split(",")))
         return 0
 
     import torch

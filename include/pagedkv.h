@@ -103,6 +103,37 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
                     int64_t num_pairs, const pkv_cache_desc* c, void* stream);
 
 /*
+ * swap_blocks -- move whole blocks (K and V) between two pools of the same block
+ * shape (c's heads, block size, head_dim and dtype): the device pool and a host
+ * pool, in either direction (review of the vLLM paper, the preemption
+ * paragraphs: swapping KV out to host memory and back).  For each pair (src,
+ * dst) block dst of dst_k / dst_v becomes block src of src_k / src_v.
+ *   src_*, dst_*     pools: device memory, or pinned host memory allocated with
+ *                    hipHostMalloc (torch's pin_memory), caller-owned, 16-byte
+ *                    aligned; src_num_blocks / dst_num_blocks are their sizes
+ *   src_dst_pairs    pkv_swap_blocks: device int64 [num_pairs][2]; ids out of
+ *                    range are skipped; destinations must be distinct (the
+ *                    caller's duty, as for pkv_copy_blocks).
+ *                    pkv_swap_blocks_dma: host int64 [num_pairs][2], checked on
+ *                    the host (PKV_E_INVAL before any copy).
+ * pkv_swap_blocks runs one kernel that copies every block with the GPU's own
+ * loads and stores across the host link.  pkv_swap_blocks_dma issues one
+ * copy-engine transfer per run of pairs that are consecutive on both sides (K
+ * and V apart) -- the per-block transfer whose cost for small blocks the page
+ * points out.  Both are asynchronous on `stream`.
+ */
+/* What kind of memory p points into, as the swap calls see it: 2 device memory,
+ * 1 pinned host memory mapped for the GPU at the same address, 0 anything else
+ * (pageable host memory, unknown pointers, NULL) -- which they refuse. */
+int32_t pkv_memory_kind(const void* p);
+int pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                    const int64_t* src_dst_pairs, int64_t num_pairs, int32_t src_num_blocks,
+                    int32_t dst_num_blocks, const pkv_cache_desc* c, void* stream);
+int pkv_swap_blocks_dma(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                        const int64_t* src_dst_pairs, int64_t num_pairs, int32_t src_num_blocks,
+                        int32_t dst_num_blocks, const pkv_cache_desc* c, void* stream);
+
+/*
  * Bytes of device workspace a decode call needs (0 only for an empty batch or
  * invalid sizes): a header, one record per (sequence, head) and the
  * (max, sum, output) rows of split contexts -- the matrix-core kernel's two
@@ -318,6 +349,48 @@ int pkv_bm_extend_tokens(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t
                          int64_t* slots, int64_t* cow_src, int64_t* cow_dst);
 int pkv_bm_cache_stats(pkv_bm* bm, int64_t* out);
 int32_t pkv_bm_evictable_list(pkv_bm* bm, int32_t* out, int32_t cap);
+
+/* ------------------------------------------------------------------ swapping
+ *
+ * Preemption by swapping (review of the vLLM paper, the preemption paragraphs):
+ * a set of sequences not needed for now moves its KV to a host pool, freeing
+ * device blocks, and moves back when there is room.  The host pool has the
+ * device pool's block shape (the caller allocates it in pinned host memory;
+ * pkv_swap_blocks moves the data).
+ *  - A set moves together; every block one of its sequences holds must be held
+ *    only by sequences of the set (forked samples move together), so a shared
+ *    block moves once and keeps its count.  Otherwise PKV_E_INVAL.
+ *  - Distinct blocks are taken in order of first appearance (sequences in the
+ *    order given, blocks in logical order).  The receiving pool's free list
+ *    (head) supplies new blocks; the giving pool's blocks return to the tail of
+ *    its free list in that order.  Device blocks leave without their
+ *    prefix-cache keys; blocks that come back carry none.
+ *  - The returned (src, dst) pairs -- device->host for swap-out, host->device
+ *    for swap-in -- must be copied before any later write reuses a block.
+ *  - A swapped-out sequence can only be swapped in or released (releasing
+ *    returns its host blocks); other calls on it give PKV_E_INVAL.
+ *  - All-or-nothing: PKV_E_NOMEM when the receiving pool lacks blocks.
+ *
+ * pkv_bm_set_host_pool -- (re)create a host pool of num_host_blocks blocks,
+ *   free list 0..n-1; PKV_E_INVAL while a sequence is swapped out.
+ * pkv_bm_swap_out / pkv_bm_swap_in -- pairs: caller array of cap int64 pairs;
+ *   *num_pairs receives the number of pairs (also when cap is too small, which
+ *   gives PKV_E_INVAL with nothing changed).
+ * pkv_bm_swap_stats -- out[0] free host blocks, out[1] host blocks, out[2]
+ *   swapped-out sequences.
+ * pkv_bm_host_refcount / pkv_bm_host_free_list -- host-side counts and free list.
+ * pkv_bm_seq_blocks -- a sequence's blocks (host blocks while swapped out);
+ *   returns the count (copies at most cap) or -1 for an unknown sequence.
+ */
+int pkv_bm_set_host_pool(pkv_bm* bm, int32_t num_host_blocks);
+int pkv_bm_swap_out(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t cap,
+                    int32_t* num_pairs);
+int pkv_bm_swap_in(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t cap,
+                   int32_t* num_pairs);
+int pkv_bm_swap_stats(pkv_bm* bm, int64_t* out);
+int32_t pkv_bm_host_refcount(pkv_bm* bm, int32_t block);
+int32_t pkv_bm_host_free_list(pkv_bm* bm, int32_t* out, int32_t cap);
+int pkv_bm_seq_blocks(pkv_bm* bm, int64_t seq, int32_t* out, int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,11 @@ _SIGNATURES = {
                                                _i32, _vp, _sz, _vp, _i32]),
     "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _vp, _sz, _vp, _vp]),
+    "pkv_swap_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                       ctypes.POINTER(CacheDesc), _vp]),
+    "pkv_swap_blocks_dma": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                           ctypes.POINTER(CacheDesc), _vp]),
+    "pkv_memory_kind": (_i32, [_vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
@@ -94,6 +99,13 @@ _SIGNATURES = {
     "pkv_bm_extend_tokens": (ctypes.c_int, [_vp, _i64, _pi32, _i64, _pi64, _pi64, _pi64]),
     "pkv_bm_cache_stats": (ctypes.c_int, [_vp, _pi64]),
     "pkv_bm_evictable_list": (_i32, [_vp, _pi32, _i32]),
+    "pkv_bm_set_host_pool": (ctypes.c_int, [_vp, _i32]),
+    "pkv_bm_swap_out": (ctypes.c_int, [_vp, _pi64, _i32, _pi64, _i32, _pi32]),
+    "pkv_bm_swap_in": (ctypes.c_int, [_vp, _pi64, _i32, _pi64, _i32, _pi32]),
+    "pkv_bm_swap_stats": (ctypes.c_int, [_vp, _pi64]),
+    "pkv_bm_host_refcount": (_i32, [_vp, _i32]),
+    "pkv_bm_host_free_list": (_i32, [_vp, _pi32, _i32]),
+    "pkv_bm_seq_blocks": (ctypes.c_int, [_vp, _i64, _pi32, _i32]),
 }
 
 
@@ -190,6 +202,60 @@ def alloc_pools(desc: CacheDesc, device="cuda", poison: bool = True):
 
 def _ptr(t) -> int:
     return int(t.data_ptr())
+
+
+def alloc_host_pools(desc: CacheDesc, num_host_blocks: int):
+    """Pinned host K and V pools of ``num_host_blocks`` blocks with the device pools' block
+    shape, for swapping (the GPU reads and writes them directly)."""
+    torch = _torch()
+    tdt = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}[desc.kv_dtype]
+    ks, vs = pool_shapes(desc)
+    k = torch.empty((num_host_blocks,) + ks[1:], dtype=tdt, pin_memory=True)
+    v = torch.empty((num_host_blocks,) + vs[1:], dtype=tdt, pin_memory=True)
+    return k, v
+
+
+def _check_swap_pool(t, shape, desc: CacheDesc, what: str) -> int:
+    if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{what} must be a contiguous device tensor or pinned host tensor")
+    if tuple(t.shape[1:]) != tuple(shape[1:]):
+        raise ValueError(f"{what} block shape {tuple(t.shape[1:])} != {tuple(shape[1:])}")
+    if dtype_code(t) != desc.kv_dtype:
+        raise ValueError(f"{what} dtype {t.dtype} does not match the descriptor")
+    return int(t.shape[0])
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, desc: CacheDesc, method: str = "kernel",
+                stream=None) -> None:
+    """Move whole blocks between the device pools and pinned host pools (either way): block
+    dst of ``dst_*`` becomes block src of ``src_*`` for each (src, dst) of ``pairs`` (host,
+    checked).  ``method`` 'kernel' copies with one GPU kernel, 'dma' with one copy-engine
+    transfer per run of consecutive blocks."""
+    torch = _torch()
+    ks, vs = pool_shapes(desc)
+    ns = _check_swap_pool(src_k, ks, desc, "src_k")
+    if _check_swap_pool(src_v, vs, desc, "src_v") != ns:
+        raise ValueError("src_k and src_v hold different numbers of blocks")
+    nd = _check_swap_pool(dst_k, ks, desc, "dst_k")
+    if _check_swap_pool(dst_v, vs, desc, "dst_v") != nd:
+        raise ValueError("dst_k and dst_v hold different numbers of blocks")
+    p = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+    if len(p) == 0:
+        return
+    if ((p[:, 0] < 0) | (p[:, 0] >= ns) | (p[:, 1] < 0) | (p[:, 1] >= nd)).any():
+        raise ValueError("block id out of range")
+    if len(np.unique(p[:, 1])) != len(p):
+        raise ValueError("duplicate destination")
+    args = (_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v))
+    if method == "kernel":
+        dev = torch.from_numpy(p).to("cuda")
+        _check(lib.pkv_swap_blocks(*args, _ptr(dev), len(p), ns, nd, ctypes.byref(desc),
+                                   _stream(stream)))
+    elif method == "dma":
+        _check(lib.pkv_swap_blocks_dma(*args, p.ctypes.data, len(p), ns, nd, ctypes.byref(desc),
+                                       _stream(stream)))
+    else:
+        raise ValueError(f"unknown method {method}")
 
 
 def _check_pool(t, shape, desc: CacheDesc, what: str) -> None:
@@ -466,6 +532,50 @@ class BlockManager:
         _check(lib.pkv_bm_cache_stats(self._h, _np_ptr(out, ctypes.c_int64)))
         return {"cached_blocks": int(out[0]), "evictable_blocks": int(out[1]),
                 "hit_tokens": int(out[2]), "query_tokens": int(out[3])}
+
+    # -- swapping ------------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        _check(lib.pkv_bm_set_host_pool(self._h, num_host_blocks))
+
+    def seq_blocks(self, seq: int) -> List[int]:
+        n = lib.pkv_bm_seq_blocks(self._h, seq, None, 0)
+        if n < 0:
+            raise PagedKVError(PKV_E_INVAL, f"unknown sequence {seq}")
+        out = np.empty(max(1, n), dtype=np.int32)
+        lib.pkv_bm_seq_blocks(self._h, seq, _np_ptr(out, ctypes.c_int32), n)
+        return out[:n].tolist()
+
+    def _swap(self, fn, seqs) -> np.ndarray:
+        s = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        cap = sum(max(0, lib.pkv_bm_seq_blocks(self._h, int(x), None, 0)) for x in s)
+        pairs = np.empty((max(1, cap), 2), dtype=np.int64)
+        n = ctypes.c_int32()
+        _check(fn(self._h, _np_ptr(s, ctypes.c_int64), len(s), _np_ptr(pairs, ctypes.c_int64),
+                  cap, ctypes.byref(n)))
+        return pairs[: n.value].copy()
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Move a set of sequences to the host pool; returns (device, host) pairs to copy."""
+        return self._swap(lib.pkv_bm_swap_out, seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Move swapped-out sequences back; returns (host, device) pairs to copy."""
+        return self._swap(lib.pkv_bm_swap_in, seqs)
+
+    def swap_stats(self) -> dict:
+        out = np.zeros(3, dtype=np.int64)
+        _check(lib.pkv_bm_swap_stats(self._h, _np_ptr(out, ctypes.c_int64)))
+        return {"host_free_blocks": int(out[0]), "host_blocks": int(out[1]),
+                "swapped_seqs": int(out[2])}
+
+    def host_refcount(self, block: int) -> int:
+        return int(lib.pkv_bm_host_refcount(self._h, block))
+
+    def host_free_list(self) -> List[int]:
+        n = lib.pkv_bm_host_free_list(self._h, None, 0)
+        out = np.empty(max(1, n), dtype=np.int32)
+        lib.pkv_bm_host_free_list(self._h, _np_ptr(out, ctypes.c_int32), n)
+        return out[:n].tolist()
 
     def evictable_list(self) -> List[int]:
         n = lib.pkv_bm_evictable_list(self._h, None, 0)

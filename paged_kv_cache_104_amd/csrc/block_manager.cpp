@@ -26,6 +26,16 @@
 // cached blocks join the evictable queue last block first; its uncached blocks
 // return to the free list as above.  A block that fills takes its key unless
 // another block already holds it.
+//
+// Swapping (review of the vLLM paper, the preemption paragraphs): a set of
+// sequences moves its KV to a host pool with the device pool's block shape and
+// back.  A shared block moves once and keeps its count; a set sharing a block
+// with a sequence outside it is refused.  Distinct blocks are taken in order
+// of first appearance (sequences as given, blocks in logical order), the
+// receiving side's free list supplies the new blocks, and the giving side's
+// blocks return to its free list in that order (device blocks without their
+// prefix-cache keys).  The caller copies the returned pairs before any later
+// write.  A swapped-out sequence can only be swapped in or released.
 #include <algorithm>
 #include <cstring>
 #include <deque>
@@ -51,8 +61,9 @@ struct Node {
 };
 
 struct Seq {
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;   // host blocks while swapped out
   int64_t len = 0;
+  bool swapped = false;
   bool tracked = false;          // admitted with its tokens (prefix caching)
   std::vector<int32_t> tokens;   // tracked sequences only
   std::vector<Node*> path;       // trie node of each full block (tracked only)
@@ -75,6 +86,11 @@ struct pkv_bm {
   std::vector<std::list<int32_t>::iterator> ev_pos;   // valid while ev_in[b]
   std::vector<char> ev_in;
   int64_t hit_tokens = 0, query_tokens = 0, cached_blocks = 0;
+
+  // swapping
+  std::deque<int32_t> host_free;
+  std::vector<int32_t> host_ref;
+  int64_t swapped_seqs = 0;
 
   ~pkv_bm() { drop_children(&root); }
 
@@ -271,7 +287,8 @@ int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int64_t num_tokens) {
 int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return fail(PKV_E_INVAL, "NULL manager");
   auto it = bm->seqs.find(parent);
-  if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown parent %lld", (long long)parent);
+  if (it == bm->seqs.end() || it->second.swapped)
+    return fail(PKV_E_INVAL, "unknown or swapped-out parent %lld", (long long)parent);
   if (bm->seqs.count(child)) return fail(PKV_E_INVAL, "child %lld exists", (long long)child);
   Seq s = it->second;
   for (int32_t b : s.blocks) bm->ref[b] += 1;
@@ -283,7 +300,8 @@ int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
 int pkv_bm_append(pkv_bm* bm, int64_t seq, int64_t* slot, int64_t* cow_src, int64_t* cow_dst) {
   if (!bm || !slot || !cow_src || !cow_dst) return fail(PKV_E_INVAL, "NULL argument");
   auto it = bm->seqs.find(seq);
-  if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
+  if (it == bm->seqs.end() || it->second.swapped)
+    return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seq);
   if (bm->needs_block(it->second) && bm->available() == 0)
     return fail(PKV_E_NOMEM, "append needs a block, none available");
   *slot = bm->append_one(it->second, cow_src, cow_dst);
@@ -298,7 +316,8 @@ int pkv_bm_append_batch(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* slo
   std::unordered_set<int64_t> uniq;
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seqs[i]);
+    if (it == bm->seqs.end() || it->second.swapped)
+      return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seqs[i]);
     if (!uniq.insert(seqs[i]).second)
       return fail(PKV_E_INVAL, "sequence %lld repeated in a batch", (long long)seqs[i]);
     ptr[i] = &it->second;
@@ -342,7 +361,8 @@ int pkv_bm_extend(pkv_bm* bm, int64_t seq, int64_t n, int64_t* slots, int64_t* c
   if (!bm || n < 0 || (n > 0 && !slots) || !cow_src || !cow_dst)
     return fail(PKV_E_INVAL, "bad extend arguments");
   auto it = bm->seqs.find(seq);
-  if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
+  if (it == bm->seqs.end() || it->second.swapped)
+    return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seq);
   Seq& s = it->second;
   const int64_t have = int64_t(s.blocks.size()) * bm->block_size - s.len;
   const int64_t rest = n > have ? n - have : 0;
@@ -367,6 +387,14 @@ int pkv_bm_free_seq(pkv_bm* bm, int64_t seq) {
   if (!bm) return fail(PKV_E_INVAL, "NULL manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
+  if (it->second.swapped) {                       // its blocks are host blocks
+    for (int32_t h : it->second.blocks)
+      if (--bm->host_ref[h] == 0) bm->host_free.push_back(h);
+    for (Node* n : it->second.path) bm->release(n);
+    bm->seqs.erase(it);
+    bm->swapped_seqs -= 1;
+    return PKV_OK;
+  }
   std::vector<int32_t> zero;
   for (int32_t b : it->second.blocks) {
     bm->ref[b] -= 1;
@@ -389,7 +417,8 @@ int pkv_bm_free_seq(pkv_bm* bm, int64_t seq) {
 int pkv_bm_slots(pkv_bm* bm, int64_t seq, int64_t start_pos, int64_t n, int64_t* out) {
   if (!bm || n < 0 || (n > 0 && !out)) return fail(PKV_E_INVAL, "bad slots arguments");
   auto it = bm->seqs.find(seq);
-  if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seq);
+  if (it == bm->seqs.end() || it->second.swapped)
+    return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seq);
   const Seq& s = it->second;
   if (start_pos < 0 || start_pos + n > s.len)
     return fail(PKV_E_INVAL, "positions [%lld, %lld) outside the %lld tokens of the sequence",
@@ -404,7 +433,8 @@ int pkv_bm_block_tables(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* tab
     return fail(PKV_E_INVAL, "bad block_tables arguments");
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
-    if (it == bm->seqs.end()) return fail(PKV_E_INVAL, "unknown sequence %lld", (long long)seqs[i]);
+    if (it == bm->seqs.end() || it->second.swapped)
+      return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seqs[i]);
     if (int64_t(it->second.blocks.size()) > max_blocks)
       return fail(PKV_E_INVAL, "sequence %lld holds %zu blocks > max_blocks %d",
                   (long long)seqs[i], it->second.blocks.size(), max_blocks);
@@ -427,6 +457,7 @@ int pkv_bm_stats(pkv_bm* bm, pkv_bm_stats_t* out) {
   out->used_blocks = bm->num_blocks - out->free_blocks;
   out->tokens = out->slots_allocated = out->logical_blocks = out->physical_blocks = 0;
   for (const auto& kv : bm->seqs) {
+    if (kv.second.swapped) continue;             // their tables hold host blocks
     out->tokens += kv.second.len;
     out->logical_blocks += int64_t(kv.second.blocks.size());
   }
@@ -546,6 +577,144 @@ int pkv_bm_cache_stats(pkv_bm* bm, int64_t* out) {
   out[2] = bm->hit_tokens;
   out[3] = bm->query_tokens;
   return PKV_OK;
+}
+
+// ------------------------------------------------------------------ swapping
+
+int pkv_bm_set_host_pool(pkv_bm* bm, int32_t num_host_blocks) {
+  if (!bm) return fail(PKV_E_INVAL, "NULL manager");
+  if (num_host_blocks < 0) return fail(PKV_E_INVAL, "negative host pool");
+  if (bm->swapped_seqs) return fail(PKV_E_INVAL, "sequences are swapped out");
+  bm->host_free.clear();
+  for (int32_t h = 0; h < num_host_blocks; ++h) bm->host_free.push_back(h);
+  bm->host_ref.assign(num_host_blocks, 0);
+  return PKV_OK;
+}
+
+namespace {
+
+// Distinct blocks of a set of sequences in order of first appearance, provided
+// every holder of each is in the set (counts[] = holders over all sequences).
+int distinct_blocks(pkv_bm* bm, const int64_t* seqs, int32_t n, bool swapped,
+                    const std::vector<int32_t>& counts, std::vector<Seq*>* ptr,
+                    std::vector<int32_t>* order) {
+  std::unordered_set<int64_t> uniq;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (!uniq.insert(seqs[i]).second)
+      return fail(PKV_E_INVAL, "sequence %lld repeated", (long long)seqs[i]);
+    if (it == bm->seqs.end() || it->second.swapped != swapped)
+      return fail(PKV_E_INVAL, "sequence %lld is unknown or %s", (long long)seqs[i],
+                  swapped ? "resident" : "swapped out");
+    ptr->push_back(&it->second);
+  }
+  std::unordered_map<int32_t, int32_t> seen;
+  for (Seq* s : *ptr)
+    for (int32_t b : s->blocks)
+      if (seen[b]++ == 0) order->push_back(b);
+  for (int32_t b : *order)
+    if (seen[b] != counts[b])
+      return fail(PKV_E_INVAL, "block %d is shared with a sequence outside the set", b);
+  return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_bm_swap_out(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t cap,
+                    int32_t* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && !seqs) || !num_pairs || cap < 0 || (cap > 0 && !pairs))
+    return fail(PKV_E_INVAL, "bad swap_out arguments");
+  std::vector<Seq*> ptr;
+  std::vector<int32_t> blocks;
+  int rc = distinct_blocks(bm, seqs, n, false, bm->ref, &ptr, &blocks);
+  if (rc) return rc;
+  *num_pairs = int32_t(blocks.size());
+  if (int64_t(blocks.size()) > cap) return fail(PKV_E_INVAL, "pairs buffer holds %d < %zu", cap, blocks.size());
+  if (blocks.size() > bm->host_free.size())
+    return fail(PKV_E_NOMEM, "swap_out needs %zu host blocks, %zu free", blocks.size(),
+                bm->host_free.size());
+  std::unordered_map<int32_t, int32_t> to;
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    const int32_t b = blocks[i], h = bm->host_free.front();
+    bm->host_free.pop_front();
+    bm->host_ref[h] = bm->ref[b];
+    to[b] = h;
+    pairs[2 * i] = b;
+    pairs[2 * i + 1] = h;
+  }
+  for (Seq* s : ptr) {
+    for (int32_t& b : s->blocks) b = to[b];
+    s->swapped = true;
+  }
+  bm->swapped_seqs += n;
+  for (int32_t b : blocks) {
+    bm->ref[b] = 0;
+    if (bm->caching && bm->node_of[b]) bm->uncache(b);
+    bm->free_list.push_back(b);
+  }
+  return PKV_OK;
+}
+
+int pkv_bm_swap_in(pkv_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t cap,
+                   int32_t* num_pairs) {
+  if (!bm || n < 0 || (n > 0 && !seqs) || !num_pairs || cap < 0 || (cap > 0 && !pairs))
+    return fail(PKV_E_INVAL, "bad swap_in arguments");
+  std::vector<Seq*> ptr;
+  std::vector<int32_t> hosts;
+  int rc = distinct_blocks(bm, seqs, n, true, bm->host_ref, &ptr, &hosts);
+  if (rc) return rc;
+  *num_pairs = int32_t(hosts.size());
+  if (int64_t(hosts.size()) > cap) return fail(PKV_E_INVAL, "pairs buffer holds %d < %zu", cap, hosts.size());
+  if (int64_t(hosts.size()) > bm->available())
+    return fail(PKV_E_NOMEM, "swap_in needs %zu blocks, %lld available", hosts.size(),
+                (long long)bm->available());
+  std::unordered_map<int32_t, int32_t> to;
+  for (size_t i = 0; i < hosts.size(); ++i) {
+    const int32_t h = hosts[i], d = bm->pop_free();
+    bm->ref[d] = bm->host_ref[h];
+    to[h] = d;
+    pairs[2 * i] = h;
+    pairs[2 * i + 1] = d;
+  }
+  for (Seq* s : ptr) {
+    for (int32_t& b : s->blocks) b = to[b];
+    s->swapped = false;
+  }
+  bm->swapped_seqs -= n;
+  for (int32_t h : hosts) {
+    bm->host_ref[h] = 0;
+    bm->host_free.push_back(h);
+  }
+  return PKV_OK;
+}
+
+int pkv_bm_swap_stats(pkv_bm* bm, int64_t* out) {
+  if (!bm || !out) return fail(PKV_E_INVAL, "NULL argument");
+  out[0] = int64_t(bm->host_free.size());
+  out[1] = int64_t(bm->host_ref.size());
+  out[2] = bm->swapped_seqs;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_host_refcount(pkv_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= int32_t(bm->host_ref.size())) return -1;
+  return bm->host_ref[block];
+}
+
+int32_t pkv_bm_host_free_list(pkv_bm* bm, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  const int32_t n = int32_t(bm->host_free.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) out[i] = bm->host_free[i];
+  return n;
+}
+
+int pkv_bm_seq_blocks(pkv_bm* bm, int64_t seq, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return -1;
+  const int32_t n = int32_t(it->second.blocks.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) out[i] = it->second.blocks[i];
+  return n;
 }
 
 int32_t pkv_bm_evictable_list(pkv_bm* bm, int32_t* out, int32_t cap) {

@@ -5,7 +5,12 @@
 // (key_pool[block_table[pos // B], pos % B] = key): slot = block * B + pos.
 // copy_blocks is the copy step of copy-on-write (ithome article 10417389,
 // section 4): the writer's new block receives the whole shared block.
+// swap_blocks moves whole blocks between the device pool and a host pool of
+// the same block shape (review of the vLLM paper, the preemption paragraphs:
+// swapping out to host memory and back).
 #include <hip/hip_runtime.h>
+
+#include <vector>
 
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -103,6 +108,23 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
 }
 
+// One workgroup per (pair, pool), 16-byte copies of a whole block from one pool
+// to another; either may be pinned host memory, which the GPU reads and writes
+// across the host link.  Many blocks in flight at once keep the link busy with
+// one launch, whatever the block size.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v, uint8_t* __restrict__ dst_k,
+    uint8_t* __restrict__ dst_v, const int64_t* __restrict__ pairs, int64_t block_bytes,
+    int64_t src_blocks, int64_t dst_blocks) {
+  const int64_t src = pairs[2 * int64_t(blockIdx.x)];
+  const int64_t dst = pairs[2 * int64_t(blockIdx.x) + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = reinterpret_cast<const uint4*>((blockIdx.y == 0 ? src_k : src_v) + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>((blockIdx.y == 0 ? dst_k : dst_v) + dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace pkv
@@ -177,5 +199,100 @@ extern "C" int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_ds
       c->num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_E_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int32_t pkv_memory_kind(const void* p) {
+  if (!p) return 0;
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (at.type == hipMemoryTypeDevice) return 2;
+  if (at.type == hipMemoryTypeHost && at.devicePointer == p) return 1;
+  return 0;
+}
+
+static int64_t block_bytes_of(const pkv_cache_desc* c) {
+  return int64_t(c->num_kv_heads) * c->block_size * c->head_dim * elem_bytes(c->kv_dtype);
+}
+
+static int check_swap(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                      int64_t num_pairs, int32_t src_num_blocks, int32_t dst_num_blocks,
+                      const pkv_cache_desc* c) {
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_pairs < 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+    return fail(PKV_E_INVAL, "negative size");
+  if (num_pairs > 0x7fffffff) return fail(PKV_E_INVAL, "too many pairs for one call");
+  if (num_pairs && (!src_k || !src_v || !dst_k || !dst_v)) return fail(PKV_E_INVAL, "NULL pool");
+  if (num_pairs && (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v)))
+    return fail(PKV_E_INVAL, "pools must be 16-byte aligned");
+  if (num_pairs) {
+    // every pool must be device memory or pinned host memory that the GPU sees at the
+    // same address: pageable host memory is refused here, never touched by a kernel
+    const void* pools[4] = {src_k, src_v, dst_k, dst_v};
+    for (const void* p : pools)
+      if (pkv_memory_kind(p) == 0)
+        return fail(PKV_E_INVAL, "pool %p is neither device nor mapped pinned host memory", p);
+  }
+  return PKV_OK;
+}
+
+extern "C" int pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                               const int64_t* src_dst_pairs, int64_t num_pairs,
+                               int32_t src_num_blocks, int32_t dst_num_blocks,
+                               const pkv_cache_desc* c, void* stream) {
+  clear_error();
+  int rc = check_swap(src_k, src_v, dst_k, dst_v, num_pairs, src_num_blocks, dst_num_blocks, c);
+  if (rc || num_pairs == 0) return rc;
+  if (!src_dst_pairs) return fail(PKV_E_INVAL, "NULL pairs");
+  const dim3 grid(static_cast<unsigned>(num_pairs), 2), block(256);
+  swap_blocks_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(src_k), static_cast<const uint8_t*>(src_v),
+      static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v), src_dst_pairs,
+      block_bytes_of(c), src_num_blocks, dst_num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "swap_blocks launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_swap_blocks_dma(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                                   const int64_t* src_dst_pairs, int64_t num_pairs,
+                                   int32_t src_num_blocks, int32_t dst_num_blocks,
+                                   const pkv_cache_desc* c, void* stream) {
+  clear_error();
+  int rc = check_swap(src_k, src_v, dst_k, dst_v, num_pairs, src_num_blocks, dst_num_blocks, c);
+  if (rc || num_pairs == 0) return rc;
+  if (!src_dst_pairs) return fail(PKV_E_INVAL, "NULL pairs");
+  // the pairs are on the host here: check them all before the first copy
+  std::vector<char> seen(size_t(dst_num_blocks), 0);
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    const int64_t sb = src_dst_pairs[2 * i], db = src_dst_pairs[2 * i + 1];
+    if (sb < 0 || sb >= src_num_blocks || db < 0 || db >= dst_num_blocks)
+      return fail(PKV_E_INVAL, "pair %lld (%lld, %lld) out of range", (long long)i, (long long)sb,
+                  (long long)db);
+    if (seen[size_t(db)]++) return fail(PKV_E_INVAL, "destination %lld repeated", (long long)db);
+  }
+  const int64_t bb = block_bytes_of(c);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one transfer per run of pairs that are consecutive on both sides
+  for (int64_t i = 0; i < num_pairs;) {
+    int64_t j = i + 1;
+    while (j < num_pairs && src_dst_pairs[2 * j] == src_dst_pairs[2 * i] + (j - i) &&
+           src_dst_pairs[2 * j + 1] == src_dst_pairs[2 * i + 1] + (j - i))
+      ++j;
+    const int64_t sb = src_dst_pairs[2 * i], db = src_dst_pairs[2 * i + 1], bytes = (j - i) * bb;
+    hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(dst_k) + db * bb,
+                                  static_cast<const uint8_t*>(src_k) + sb * bb, size_t(bytes),
+                                  hipMemcpyDefault, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(static_cast<uint8_t*>(dst_v) + db * bb,
+                         static_cast<const uint8_t*>(src_v) + sb * bb, size_t(bytes),
+                         hipMemcpyDefault, st);
+    if (e != hipSuccess) return fail(PKV_E_HIP, "swap copy: %s", hipGetErrorString(e));
+    i = j;
+  }
   return PKV_OK;
 }

@@ -19,8 +19,9 @@ from typing import Callable, Optional, Sequence
 
 import numpy as np
 
-from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_pools,
-               copy_blocks, decode_workspace_bytes, paged_attn_decode, reshape_and_cache)
+from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_host_pools,
+               alloc_pools, copy_blocks, decode_workspace_bytes, paged_attn_decode,
+               reshape_and_cache, swap_blocks)
 
 
 def to_device(x: np.ndarray, in_dtype: str, device):
@@ -54,6 +55,24 @@ class PagedKVCache:
     def copy(self, pairs) -> None:
         if len(pairs):
             copy_blocks(self.k_pool, self.v_pool, np.asarray(pairs, dtype=np.int64), self.desc)
+
+    # -- swapping ------------------------------------------------------------
+    def enable_swap(self, num_host_blocks: int) -> None:
+        """A pinned host pool of ``num_host_blocks`` blocks for swapped-out sequences."""
+        self.bm.set_host_pool(num_host_blocks)
+        self.host_k, self.host_v = alloc_host_pools(self.desc, num_host_blocks)
+
+    def swap_out(self, seqs, method: str = "kernel"):
+        """Move a set of sequences (with all their forks) to the host pool; their device
+        blocks are free for others once the copy, queued on the stream, has run."""
+        pairs = self.bm.swap_out(seqs)
+        swap_blocks(self.k_pool, self.v_pool, self.host_k, self.host_v, pairs, self.desc, method)
+        return pairs
+
+    def swap_in(self, seqs, method: str = "kernel"):
+        pairs = self.bm.swap_in(seqs)
+        swap_blocks(self.host_k, self.host_v, self.k_pool, self.v_pool, pairs, self.desc, method)
+        return pairs
 
     # -- allocator script ----------------------------------------------------
     def run_script(self, ops, kv_input: Callable[[int], tuple], in_dtype: str,
