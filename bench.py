@@ -2,10 +2,11 @@
 """Paged decode benchmark on one MI355X.
 
 One step is one pass of the whole hot path over the batch:
-  host   C++ block manager: append one token per sequence -> slots, copy pairs,
-         block tables (staged in pinned memory, one packed upload)
+  host   C++ block manager: append one token per sequence -> slots, copy pairs
   device copy_blocks (copy-on-write pairs, when there are any)
-         reshape_and_cache (the batch's new K/V into their slots)
+         append_tokens: the batch's new K/V into their slots, and the device-resident
+         block tables and lengths brought up to date (slots and positions travel in
+         the kernel arguments; the tables were uploaded once, before the steps)
          paged attention: decode kernel + merge of split contexts
 Inputs are resident in HBM before the timed region.  Contexts grow by one
 token per step, as in a real decode loop; the KV bytes of every step are
@@ -119,25 +120,10 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     bytes_per_token = wl.kv_bytes_per_token()
     dev = "cuda"
     stream = torch.cuda.current_stream()
-    # slots, lengths and tables of a step travel in one packed, double-buffered upload
-    def up(n):
-        return -(-n // 256) * 256
-    o_lens = up(8 * S)
-    o_tab = o_lens + up(4 * S)
-    nbytes = o_tab + up(4 * S * max_blocks)
-
-    def views(buf):
-        return (buf[:8 * S].view(torch.int64), buf[o_lens:o_lens + 4 * S].view(torch.int32),
-                buf[o_tab:o_tab + 4 * S * max_blocks].view(torch.int32).view(S, max_blocks))
-
-    # Host staging is double-buffered: the host fills one pinned buffer while the
-    # stream still copies from the other.  (A separate copy stream gains a few
-    # microseconds per step but stalls the host for milliseconds once, early on.)
-    pinned = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-    host_views = [views(b) for b in pinned]
-    packed_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    slots_d, lens_d, tables_d = views(packed_d)
-    uploaded = [torch.cuda.Event() for _ in range(2)]
+    # the batch's block tables and lengths stay on the device: uploaded once here, then each
+    # step's append writes the new tokens and updates them in the same launch
+    from paged_kv_cache_104_amd.engine import DecodeBatch
+    batch = DecodeBatch(cache, seqs, max_blocks)
     out = torch.empty_like(q)
     ws_bytes = pkv.decode_workspace_bytes(S, wl.num_q_heads, wl.head_dim, max_ctx, partition_size)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -145,7 +131,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     # steps after them also time the cache write and the merge.  Every event is
     # recorded once here so none is created inside the timed loop.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
-    for e in [x for row in ev for x in row] + uploaded:
+    for e in [x for row in ev for x in row]:
         e.record(stream)
     torch.cuda.synchronize()
     st = cache.bm.stats()
@@ -158,29 +144,18 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
 
     def step(i, all_events=False):
         nonlocal n_pairs
-        b = i % 2
-        uploaded[b].synchronize()                     # pinned buffer b is free again
         h0 = time.perf_counter()
-        slots, pairs = cache.bm.append_batch(seqs)
-        sh, lh, th = host_views[b]
-        np.copyto(sh.numpy(), slots)
-        _, lens = cache.bm.block_tables(seqs, max_blocks, out_tables=th.numpy(),
-                                        out_lens=lh.numpy())
-        kv_bytes[i] = float(lens.astype(np.int64).sum()) * bytes_per_token
-        packed_d.copy_(pinned[b], non_blocking=True)
-        uploaded[b].record(stream)
         e = ev[i]
         if all_events:
             e[0].record(stream)
-        if len(pairs):
-            n_pairs += len(pairs)
-            pkv.copy_blocks(cache.k_pool, cache.v_pool, pairs, desc)
-        pkv.reshape_and_cache(k_new, v_new, slots_d, cache.k_pool, cache.v_pool, desc)
+        _, pairs = batch.append(k_new, v_new)      # block manager, copies, write + tables
+        n_pairs += len(pairs)
+        kv_bytes[i] = float(batch.host_lens.sum()) * bytes_per_token
         e[1].record(stream)
-        pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, tables_d, lens_d, wl.scale, out,
-                                desc, max_ctx, partition_size, workspace, impl)
+        pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens, wl.scale,
+                                out, desc, max_ctx, partition_size, workspace, impl)
         e[2].record(stream)
-        pkv.paged_attn_merge(out, lens_d, wl.num_kv_heads, max_ctx, partition_size, workspace)
+        pkv.paged_attn_merge(out, batch.lens, wl.num_kv_heads, max_ctx, partition_size, workspace)
         if all_events:
             e[3].record(stream)
         host_s[i] = time.perf_counter() - h0
@@ -207,6 +182,10 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     t_attn_diag = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in diag]) * 1e-3
     kvb = kv_bytes[warmup:warmup + steps]
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    # the device tables the steps kept up to date equal the block manager's
+    t_host, l_host = cache.bm.block_tables(seqs, max_blocks)
+    assert np.array_equal(batch.tables.cpu().numpy(), t_host), "device block tables diverged"
+    assert np.array_equal(batch.lens.cpu().numpy(), l_host), "device context lengths diverged"
     # bytes of distinct blocks (a block shared by several sequences counted once), last step
     tables, lens = cache.bm.block_tables(seqs, max_blocks)
     fill = {}

@@ -103,6 +103,32 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
                     int64_t num_pairs, const pkv_cache_desc* c, void* stream);
 
 /*
+ * append_tokens -- the decode step's cache write for a batch whose block tables
+ * and context lengths stay on the device between steps.  Token i (batch row i)
+ * is written like pkv_reshape_and_cache writes it to slot host_slots[i], and
+ * the row's table entry and length are brought up to date:
+ *   block_tables[i][host_positions[i] / B] = host_slots[i] / B
+ *   context_lens[i] = host_positions[i] + 1
+ * which is everything an append changes in them (a new block when the last was
+ * full, or the copy that replaced a shared, partly filled last block -- the
+ * block manager's slot for position pos is table[pos / B] * B + pos % B).
+ *   k, v           device [num_tokens][Hkv][D] of in_dtype
+ *   host_slots     host int64 [num_tokens]: the block manager's slots; < 0 skips
+ *                  the token (its table row is left alone)
+ *   host_positions host int32 [num_tokens]: each token's position in its sequence
+ *   block_tables, context_lens  device int32 [rows][max_blocks_per_seq], [rows]
+ * The host arrays travel in the kernel arguments (256 tokens per launch), so
+ * nothing is uploaded.  PKV_E_INVAL, before any launch, for a slot outside the
+ * pool or a position that does not match its slot (pos % B != slot % B, or
+ * pos / B >= max_blocks_per_seq).
+ */
+int pkv_append_tokens(const void* k, const void* v, int32_t in_dtype,
+                      const int64_t* host_slots, const int32_t* host_positions,
+                      int32_t num_tokens, void* k_pool, void* v_pool, const pkv_cache_desc* c,
+                      int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* context_lens,
+                      void* stream);
+
+/*
  * swap_blocks -- move whole blocks (K and V) between two pools of the same block
  * shape (c's heads, block size, head_dim and dtype): the device pool and a host
  * pool, in either direction (review of the vLLM paper, the preemption

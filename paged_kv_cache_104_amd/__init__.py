@@ -76,6 +76,8 @@ _SIGNATURES = {
     "pkv_swap_blocks_dma": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                            ctypes.POINTER(CacheDesc), _vp]),
     "pkv_memory_kind": (_i32, [_vp]),
+    "pkv_append_tokens": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
+                                         ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
@@ -202,6 +204,29 @@ def alloc_pools(desc: CacheDesc, device="cuda", poison: bool = True):
 
 def _ptr(t) -> int:
     return int(t.data_ptr())
+
+
+def append_tokens(k, v, slots, positions, k_pool, v_pool, desc: CacheDesc, block_tables,
+                  context_lens, stream=None) -> None:
+    """Decode-step append: write token i's K, V ([T, H, D]) to host slot ``slots[i]`` and set
+    row i's device table entry for ``positions[i]`` and its context length."""
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    T = len(sl)
+    if len(pos) != T or tuple(k.shape) != (T, desc.num_kv_heads, desc.head_dim) or k.shape != v.shape:
+        raise ValueError(f"k/v must be [{T}, {desc.num_kv_heads}, {desc.head_dim}], one position per slot")
+    if not (block_tables.is_cuda and context_lens.is_cuda and block_tables.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("block_tables and context_lens must be contiguous device tensors")
+    if block_tables.shape[0] < T or context_lens.numel() < T:
+        raise ValueError("fewer table rows than tokens")
+    _check(lib.pkv_append_tokens(_ptr(k), _ptr(v), dtype_code(k), sl.ctypes.data, pos.ctypes.data,
+                                 T, _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+                                 _ptr(block_tables), int(block_tables.shape[1]),
+                                 _ptr(context_lens), _stream(stream)))
 
 
 def alloc_host_pools(desc: CacheDesc, num_host_blocks: int):

@@ -10,6 +10,7 @@
 // swapping out to host memory and back).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "device_common.h"
@@ -17,19 +18,16 @@
 
 namespace pkv {
 
-// One workgroup per token; each thread moves 8 consecutive dimensions of one
-// head: 16 B (bf16) or 32 B (f32) in, a contiguous row segment of the key
-// pool out, and 8 scattered elements of the dimension-major value block.
+// One token of k / v ([tokens][heads][D]) into slot `slot` of the pools, by one
+// workgroup: each thread moves 8 consecutive dimensions of one head -- 16 B
+// (bf16) or 32 B (f32) in, a contiguous row segment of the key pool out, and 8
+// scattered elements of the dimension-major value block.
 template <int KV, typename In>
-__global__ __launch_bounds__(128) void reshape_and_cache_kernel(
-    const In* __restrict__ k, const In* __restrict__ v, const int64_t* __restrict__ slots,
+__device__ __forceinline__ void write_token(
+    const In* __restrict__ k, const In* __restrict__ v, int64_t tok, int64_t slot,
     typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ v_pool,
-    int num_kv_heads, int head_dim, int block_size, int64_t num_slots, float k_scale,
-    float v_scale) {
+    int num_kv_heads, int head_dim, int block_size, float k_scale, float v_scale) {
   typedef typename KvTraits<KV>::T T;
-  const int64_t tok = blockIdx.x;
-  const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;             // skip (negative) / never write outside
   const int64_t blk = slot / block_size;
   const int pos = int(slot - blk * block_size);
   const int chunks = num_kv_heads * head_dim / 8;
@@ -90,6 +88,51 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) vd[i * block_size] = vf[i];
     }
+  }
+}
+
+template <int KV, typename In>
+__global__ __launch_bounds__(128) void reshape_and_cache_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const int64_t* __restrict__ slots,
+    typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ v_pool,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_slots, float k_scale,
+    float v_scale) {
+  const int64_t tok = blockIdx.x;
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;             // skip (negative) / never write outside
+  write_token<KV, In>(k, v, tok, slot, k_pool, v_pool, num_kv_heads, head_dim, block_size,
+                      k_scale, v_scale);
+}
+
+// The decode step's append for up to kAppendMax tokens, with the host's slots and
+// positions passed by value in the kernel arguments (no upload): token i of
+// the chunk is row `first + i` of the batch; besides its K / V it sets the
+// device block table entry that holds it and the row's context length, which
+// is all an append changes in them (a new block, or the copy that replaced a
+// shared last block).
+constexpr int kAppendMax = 256;
+struct AppendChunk {
+  int64_t slot[kAppendMax];
+  int32_t pos[kAppendMax];
+};
+
+template <int KV, typename In>
+__global__ __launch_bounds__(128) void append_tokens_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, AppendChunk chunk, int32_t first,
+    typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ v_pool,
+    int32_t* __restrict__ tables, int32_t max_blocks, int32_t* __restrict__ lens,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_slots, float k_scale,
+    float v_scale) {
+  const int i = blockIdx.x;
+  const int64_t slot = chunk.slot[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t row = int64_t(first) + i;
+  write_token<KV, In>(k, v, row, slot, k_pool, v_pool, num_kv_heads, head_dim, block_size,
+                      k_scale, v_scale);
+  if (threadIdx.x == 0) {
+    const int32_t pos = chunk.pos[i];
+    tables[row * max_blocks + pos / block_size] = int32_t(slot / block_size);
+    lens[row] = pos + 1;
   }
 }
 
@@ -177,6 +220,76 @@ extern "C" int pkv_reshape_and_cache(const void* k, const void* v, int32_t in_dt
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_E_HIP, "reshape_and_cache launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_append_tokens(const void* k, const void* v, int32_t in_dtype,
+                                 const int64_t* host_slots, const int32_t* host_positions,
+                                 int32_t num_tokens, void* k_pool, void* v_pool,
+                                 const pkv_cache_desc* c, int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, int32_t* context_lens,
+                                 void* stream) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_tokens < 0 || max_blocks_per_seq <= 0) return fail(PKV_E_INVAL, "bad sizes");
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !host_slots || !host_positions || !k_pool || !v_pool || !block_tables ||
+      !context_lens)
+    return fail(PKV_E_INVAL, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
+  const bool ok = (c->kv_dtype == PKV_F32 && in_dtype == PKV_F32) ||
+                  (c->kv_dtype == PKV_BF16 && in_dtype == PKV_BF16) ||
+                  (c->kv_dtype == PKV_FP8_E4M3 && (in_dtype == PKV_BF16 || in_dtype == PKV_F32));
+  if (!ok)
+    return fail(PKV_E_UNSUPPORTED, "%s input into a %s pool", dtype_name(in_dtype),
+                dtype_name(c->kv_dtype));
+  const int B = c->block_size;
+  const int64_t num_slots = int64_t(c->num_blocks) * B;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t sl = host_slots[i];
+    const int32_t pos = host_positions[i];
+    if (sl < 0) continue;
+    if (sl >= num_slots) return fail(PKV_E_INVAL, "slot %lld of token %d outside the pool", (long long)sl, i);
+    if (pos < 0 || pos / B >= max_blocks_per_seq || pos % B != sl % B)
+      return fail(PKV_E_INVAL, "position %d of token %d does not match slot %lld", pos, i,
+                  (long long)sl);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = c->num_kv_heads, D = c->head_dim;
+  for (int32_t first = 0; first < num_tokens; first += kAppendMax) {
+    const int32_t n = std::min<int32_t>(kAppendMax, num_tokens - first);
+    AppendChunk chunk;
+    for (int32_t i = 0; i < n; ++i) {
+      chunk.slot[i] = host_slots[first + i];
+      chunk.pos[i] = host_positions[first + i];
+    }
+    const dim3 grid(static_cast<unsigned>(n)), block(128);
+    if (c->kv_dtype == PKV_F32) {
+      append_tokens_kernel<KV_F32, float><<<grid, block, 0, st>>>(
+          static_cast<const float*>(k), static_cast<const float*>(v), chunk, first,
+          static_cast<float*>(k_pool), static_cast<float*>(v_pool), block_tables,
+          max_blocks_per_seq, context_lens, H, D, B, num_slots, 1.f, 1.f);
+    } else if (c->kv_dtype == PKV_BF16) {
+      append_tokens_kernel<KV_BF16, uint16_t><<<grid, block, 0, st>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk, first,
+          static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), block_tables,
+          max_blocks_per_seq, context_lens, H, D, B, num_slots, 1.f, 1.f);
+    } else if (in_dtype == PKV_BF16) {
+      append_tokens_kernel<KV_FP8, uint16_t><<<grid, block, 0, st>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk, first,
+          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), block_tables,
+          max_blocks_per_seq, context_lens, H, D, B, num_slots, c->k_scale, c->v_scale);
+    } else {
+      append_tokens_kernel<KV_FP8, float><<<grid, block, 0, st>>>(
+          static_cast<const float*>(k), static_cast<const float*>(v), chunk, first,
+          static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), block_tables,
+          max_blocks_per_seq, context_lens, H, D, B, num_slots, c->k_scale, c->v_scale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_E_HIP, "append_tokens launch: %s", hipGetErrorString(e));
+  }
   return PKV_OK;
 }
 

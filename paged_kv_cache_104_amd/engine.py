@@ -20,8 +20,8 @@ from typing import Callable, Optional, Sequence
 import numpy as np
 
 from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_host_pools,
-               alloc_pools, copy_blocks, decode_workspace_bytes, paged_attn_decode,
-               reshape_and_cache, swap_blocks)
+               alloc_pools, append_tokens, copy_blocks, decode_workspace_bytes,
+               paged_attn_decode, reshape_and_cache, swap_blocks)
 
 
 def to_device(x: np.ndarray, in_dtype: str, device):
@@ -168,3 +168,38 @@ class PagedKVCache:
         n = decode_workspace_bytes(num_seqs, num_q_heads, self.desc.head_dim, max_context_len,
                                    partition_size)
         return torch.empty(max(n, 16), dtype=torch.uint8, device=self.device) if n else None
+
+
+class DecodeBatch:
+    """A fixed batch of sequences whose block tables and context lengths live on the device.
+
+    They are uploaded once; each decode step's append then writes the new tokens and
+    brings the device tables up to date in the same launch (``append_tokens``), so a
+    step moves nothing from the host but the kernel arguments.
+    """
+
+    def __init__(self, cache: PagedKVCache, seqs: Sequence[int], max_blocks: int):
+        import torch
+
+        self.cache = cache
+        self.seqs = [int(s) for s in seqs]
+        self.max_blocks = max_blocks
+        t, lens = cache.bm.block_tables(self.seqs, max_blocks)
+        self.tables = torch.from_numpy(t).to(cache.device)
+        self.lens = torch.from_numpy(lens).to(cache.device)
+        self.host_lens = lens.astype(np.int64)
+
+    def append(self, k_new, v_new):
+        """One token per sequence: block manager, copy-on-write copies, write + table update.
+
+        Returns (slots, pairs) as host arrays."""
+        c = self.cache
+        slots, pairs = c.bm.append_batch(self.seqs)
+        c.copy(pairs)
+        append_tokens(k_new, v_new, slots, self.host_lens, c.k_pool, c.v_pool, c.desc,
+                      self.tables, self.lens)
+        self.host_lens += 1
+        return slots, pairs
+
+    def max_context_len(self) -> int:
+        return int(self.host_lens.max()) if len(self.host_lens) else 0
