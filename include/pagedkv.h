@@ -268,6 +268,83 @@ int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t n
                          int32_t max_context_len, int32_t partition_size, const void* workspace,
                          size_t workspace_bytes, void* out, void* stream);
 
+/* ------------------------------------------------------------------ query-aware block selection
+ *
+ * QUEST (tencent cloud article 2526001, section "QUEST: Query-Aware Sparsity
+ * for Efficient Long-Context LLM Inference"): each KV block carries the
+ * channel-wise minimum and maximum of its keys; for a query q the bound
+ * U = sum_d max(q_d * min_d, q_d * max_d) is never below q.k for any key k of
+ * the block, and only the blocks with the budget_blocks largest bounds are
+ * attended.  Readings where the page is silent:
+ *  - the minimum / maximum run over the block's valid slots (the last block
+ *    of a context may be partly filled);
+ *  - the budget is in blocks; a context of no more blocks is attended whole
+ *    (bit for bit as pkv_paged_attn_decode_ex with the same partition_size);
+ *  - with grouped-query attention a (sequence, KV head) makes one choice for
+ *    its query heads, ranking blocks by the largest bound over those heads;
+ *  - equal bounds rank the lower logical block first; the chosen blocks are
+ *    attended in logical order, the softmax running over their tokens only.
+ * The bounds are summed in fp32 (unscaled q and stored key values); blocks
+ * whose bounds differ by less than that rounding may rank either way.
+ *
+ * Metadata: device [num_blocks][num_kv_heads][2][head_dim] of the pool's
+ * kv_dtype, pkv_quest_meta_bytes(c) bytes; row 0 the minimum, row 1 the
+ * maximum (stored codes, exact: min / max of values of a type are values of
+ * it).  The caller keeps it current after writing keys: a block's entry
+ * covers its first `count` slots as of the last update.
+ */
+size_t pkv_quest_meta_bytes(const pkv_cache_desc* c);
+
+/* Recompute the metadata of blocks[i] over its first counts[i] slots, all heads.
+ * blocks, counts: device int32 [n].  Entries with a block outside the pool or a
+ * count outside [1, block_size] are skipped.  blocks must be distinct. */
+int pkv_quest_update_blocks(const void* k_pool, const pkv_cache_desc* c, void* meta,
+                            const int32_t* blocks, const int32_t* counts, int32_t n,
+                            void* stream);
+
+/* The decode step's update, from device-resident tables: for every row, the block
+ * holding its last token (context_lens - 1) over its first (context_lens - 1) % B + 1
+ * slots.  Rows that share that block must agree on its fill (they do whenever the
+ * shared block was copied on write before another row appended to it). */
+int pkv_quest_update_tails(const void* k_pool, const pkv_cache_desc* c, void* meta,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, void* stream);
+
+/* Workspace bytes of pkv_quest_decode (0 on invalid sizes; the message says why); it
+ * also serves pkv_quest_select.  Contexts may hold at most 16384 blocks. */
+size_t pkv_quest_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, int32_t partition_size,
+                                 int32_t budget_blocks);
+
+/*
+ * The selection alone.  For pair p = s * num_kv_heads + kvh:
+ *   sel_tables  device int32 [num_seqs * num_kv_heads][min(max_blocks_per_seq,
+ *               budget_blocks)]: the chosen blocks in logical order, each as
+ *               block * num_kv_heads + kvh (-1 for a table entry outside the pool)
+ *   sel_lens    device int32 [num_seqs * num_kv_heads]: tokens of the chosen blocks
+ * Other arguments as pkv_paged_attn_decode (max_context_len cuts contexts alike).
+ */
+int pkv_quest_select(const void* q, int32_t q_dtype, const void* meta, const pkv_cache_desc* c,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_context_len, int32_t budget_blocks, int32_t* sel_tables,
+                     int32_t* sel_lens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over the QUEST-chosen blocks: pkv_quest_select into the
+ * workspace, then the decode kernels of pkv_paged_attn_decode_ex (family and
+ * hints from `impl`) over one-head "sequences" (sequence, KV head), whose
+ * tables address the pools as [num_blocks * num_kv_heads] one-head blocks.
+ * Arguments as pkv_paged_attn_decode_ex plus `meta` and budget_blocks >= 1.
+ */
+int pkv_quest_decode(const void* q, int32_t q_dtype, const void* k_pool, const void* v_pool,
+                     const void* meta, const pkv_cache_desc* c, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_q_heads, float scale, void* out, int32_t max_context_len,
+                     int32_t partition_size, int32_t budget_blocks, void* workspace,
+                     size_t workspace_bytes, void* stream, int32_t impl);
+
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -78,6 +78,18 @@ _SIGNATURES = {
     "pkv_memory_kind": (_i32, [_vp]),
     "pkv_append_tokens": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
                                          ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp]),
+    "pkv_quest_meta_bytes": (_sz, [ctypes.POINTER(CacheDesc)]),
+    "pkv_quest_update_blocks": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), _vp, _vp, _vp,
+                                               _i32, _vp]),
+    "pkv_quest_update_tails": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), _vp, _vp, _i32,
+                                              _vp, _i32, _vp]),
+    "pkv_quest_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32, _i32,
+                                        _i32]),
+    "pkv_quest_select": (ctypes.c_int, [_vp, _i32, _vp, ctypes.POINTER(CacheDesc), _vp, _i32,
+                                        _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "pkv_quest_decode": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, ctypes.POINTER(CacheDesc),
+                                        _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32, _i32,
+                                        _i32, _vp, _sz, _vp, _i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
@@ -412,6 +424,156 @@ def paged_attn_merge(out, context_lens, num_kv_heads: int, max_context_len: int,
                                     int(num_kv_heads), D,
                                     int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
                                     _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- QUEST
+
+def quest_meta_shape(desc: CacheDesc) -> Tuple[int, ...]:
+    """[N, H, 2, D]: per block and KV head, the channel-wise minimum (row 0) and maximum
+    (row 1) of its valid keys, in the pool's element type."""
+    return (desc.num_blocks, desc.num_kv_heads, 2, desc.head_dim)
+
+
+def alloc_quest_meta(desc: CacheDesc, device="cuda"):
+    torch = _torch()
+    tdt = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}[desc.kv_dtype]
+    meta = torch.zeros(quest_meta_shape(desc), dtype=tdt, device=device)
+    assert meta.numel() * meta.element_size() == lib.pkv_quest_meta_bytes(ctypes.byref(desc))
+    return meta
+
+
+def _check_meta(meta, desc: CacheDesc) -> None:
+    _check_pool(meta, quest_meta_shape(desc), desc, "meta")
+
+
+def _dev_i32(x, device):
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.is_cuda:
+        if x.dtype != torch.int32 or not x.is_contiguous():
+            raise ValueError("device index arrays must be contiguous int32")
+        return x
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x), dtype=np.int32)).to(device)
+
+
+def quest_update_blocks(k_pool, meta, blocks, counts, desc: CacheDesc, stream=None) -> None:
+    """Recompute the metadata of ``blocks[i]`` over its first ``counts[i]`` slots (distinct
+    blocks; host arrays are uploaded)."""
+    ks, _ = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_meta(meta, desc)
+    b, c = _dev_i32(blocks, k_pool.device), _dev_i32(counts, k_pool.device)
+    if b.numel() != c.numel():
+        raise ValueError("one count per block")
+    if b.numel() == 0:
+        return
+    _check(lib.pkv_quest_update_blocks(_ptr(k_pool), ctypes.byref(desc), _ptr(meta), _ptr(b),
+                                       _ptr(c), int(b.numel()), _stream(stream)))
+
+
+def quest_blocks_of_slots(slots, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(distinct blocks, fill counts) touched by a write to ``slots`` (slots fill a block in
+    order, so the highest slot written gives its fill)."""
+    sl = np.asarray(slots, dtype=np.int64).ravel()
+    sl = sl[sl >= 0]
+    if len(sl) == 0:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    blk = sl // block_size
+    order = np.lexsort((sl, blk))
+    blk, sl = blk[order], sl[order]
+    last = np.r_[blk[1:] != blk[:-1], True]
+    return blk[last].astype(np.int32), (sl[last] % block_size + 1).astype(np.int32)
+
+
+def quest_update_tails(k_pool, meta, block_tables, context_lens, desc: CacheDesc,
+                       stream=None) -> None:
+    """After a decode-step append: recompute each row's last block from device tables."""
+    ks, _ = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_meta(meta, desc)
+    _check_tables(block_tables, context_lens)
+    _check(lib.pkv_quest_update_tails(_ptr(k_pool), ctypes.byref(desc), _ptr(meta),
+                                      _ptr(block_tables), int(block_tables.shape[1]),
+                                      _ptr(context_lens), int(context_lens.numel()),
+                                      _stream(stream)))
+
+
+def _check_tables(block_tables, context_lens) -> None:
+    torch = _torch()
+    if not (block_tables.is_cuda and context_lens.is_cuda and block_tables.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("block_tables and context_lens must be contiguous device tensors")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != context_lens.numel():
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+
+
+def quest_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_blocks: int,
+                          max_context_len: int, partition_size: int, budget_blocks: int) -> int:
+    n = int(lib.pkv_quest_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads, max_blocks,
+                                          max_context_len, partition_size, budget_blocks))
+    if n == 0:
+        raise PagedKVError(PKV_E_INVAL, (lib.pkv_last_error() or b"").decode())
+    return n
+
+
+def _quest_ws(workspace, desc, q, block_tables, max_context_len, partition_size, budget):
+    torch = _torch()
+    S, Hq, _ = q.shape
+    need = quest_workspace_bytes(desc, S, Hq, int(block_tables.shape[1]), max_context_len,
+                                 partition_size, budget)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return workspace, int(workspace.numel() * workspace.element_size())
+
+
+def quest_select(q, meta, desc: CacheDesc, block_tables, context_lens, max_context_len: int,
+                 budget_blocks: int, workspace=None, stream=None):
+    """(sel_tables [S*H, min(max_blocks, budget)], sel_lens [S*H]): per (sequence, KV head)
+    the chosen blocks in logical order as block * H + head, and their tokens."""
+    torch = _torch()
+    _check_meta(meta, desc)
+    _check_tables(block_tables, context_lens)
+    S, Hq, D = q.shape
+    if D != desc.head_dim or not q.is_contiguous() or block_tables.shape[0] != S:
+        raise ValueError("q must be a contiguous [S, Hq, D] with one table row per sequence")
+    H = desc.num_kv_heads
+    width = max(1, min(int(block_tables.shape[1]), int(budget_blocks)))
+    sel_t = torch.full((S * H, width), -1, dtype=torch.int32, device=q.device)
+    sel_l = torch.zeros(S * H, dtype=torch.int32, device=q.device)
+    ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, 0, budget_blocks)
+    _check(lib.pkv_quest_select(_ptr(q), dtype_code(q), _ptr(meta), ctypes.byref(desc),
+                                _ptr(block_tables), int(block_tables.shape[1]),
+                                _ptr(context_lens), S, Hq, int(max_context_len),
+                                int(budget_blocks), _ptr(sel_t), _ptr(sel_l), _ptr(ws), wsb,
+                                _stream(stream)))
+    return sel_t, sel_l
+
+
+def quest_decode(q, k_pool, v_pool, meta, desc: CacheDesc, block_tables, context_lens,
+                 scale: float, out, max_context_len: int, budget_blocks: int,
+                 partition_size: int = 0, workspace=None, impl: int = IMPL_AUTO, stream=None):
+    """Decode attention over the QUEST-chosen ``budget_blocks`` blocks of every
+    (sequence, KV head); arguments as paged_attn_decode plus the metadata and budget."""
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    _check_meta(meta, desc)
+    _check_tables(block_tables, context_lens)
+    S, Hq, D = q.shape
+    if D != desc.head_dim or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("q / out shapes or dtypes do not match")
+    if not (q.is_contiguous() and out.is_contiguous()) or block_tables.shape[0] != S:
+        raise ValueError("q and out must be contiguous, one table row per sequence")
+    ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, partition_size,
+                        budget_blocks)
+    _check(lib.pkv_quest_decode(_ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(meta),
+                                ctypes.byref(desc), _ptr(block_tables),
+                                int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+                                float(scale), _ptr(out), int(max_context_len),
+                                int(partition_size), int(budget_blocks), _ptr(ws), wsb,
+                                _stream(stream), int(impl)))
+    return out
 
 
 # ---------------------------------------------------------------------------- host side

@@ -1,0 +1,619 @@
+// Query-aware block selection for decode (QUEST; tencent cloud article
+// 2526001, section "QUEST: Query-Aware Sparsity for Efficient Long-Context LLM
+// Inference"): every KV block keeps the channel-wise minimum and maximum of its
+// keys; a query bounds its score with any key of a block by taking, channel by
+// channel, the larger of its products with that minimum and maximum, summed;
+// only the blocks with the K largest bounds are attended.
+//
+// Device design:
+//  * Metadata pool [N][H][2][D] in the pool's own element type (row 0 the
+//    minimum, row 1 the maximum of the block's valid keys).  The minimum or
+//    maximum of values of a type is a value of that type, so the metadata is
+//    exact; it is 2 rows per block of B rows, 2/B of the key pool.
+//    quest_update_*_kernel recompute it for written blocks.
+//  * quest_score_kernel: one bound per (sequence, KV head, block), the largest
+//    over the KV head's query heads (grouped-query attention), into a
+//    workspace row per (sequence, KV head).  Reads only metadata.
+//  * quest_select_kernel: one workgroup per (sequence, KV head); a 4-pass radix
+//    select of the K-th largest bound (keys held in registers, histograms in
+//    LDS), ties to the lower block index, then the chosen blocks compacted in
+//    logical order into a per-(sequence, KV head) block table.  Its entries
+//    are block * H + head: the (block, head) slab of the pools seen as
+//    [N * H] one-head blocks.  The decode kernels then run unchanged on
+//    S * H one-head "sequences" of g query heads each, whose q and out rows
+//    are exactly the rows of the original [S][Hq][D] layout.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kQuestChunk = 64;        // blocks per scoring workgroup
+constexpr int kScoreThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelPerThread = 16;      // keys held by one selecting thread
+constexpr int kQuestMaxBlocks = kSelThreads * kSelPerThread;
+constexpr int kQuestMaxGroup = 16;
+
+struct QuestArgs {
+  const void* q;
+  const void* meta;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* scores;          // [pairs][score_stride]
+  int32_t* sel_tables;    // [pairs][out_stride]
+  int32_t* sel_lens;      // [pairs]
+  int32_t max_blocks;     // row stride of tables
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_ctx;
+  int32_t budget;         // blocks kept per (sequence, KV head)
+  int32_t score_stride;   // blocks of the longest context
+  int32_t out_stride;     // min(max_blocks, budget)
+  int32_t chunks;         // scoring workgroups per pair
+};
+
+__device__ __forceinline__ int quest_ctx(const QuestArgs& a, int s) {
+  return max(0, min(a.lens[s], a.max_ctx));
+}
+
+// ------------------------------------------------------------------------ metadata
+
+// (min, max) per channel of rows [0, count) of one (block, head) key slab.
+template <int KV>
+__device__ __forceinline__ void slab_minmax(const typename KvTraits<KV>::T* __restrict__ slab,
+                                            typename KvTraits<KV>::T* __restrict__ meta,
+                                            int count, int D) {
+  typedef typename KvTraits<KV>::T T;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    T lo = slab[d], hi = lo;
+    float flo = kv_to_f32<KV>(lo), fhi = flo;
+    for (int r = 1; r < count; ++r) {
+      const T x = slab[int64_t(r) * D + d];
+      const float f = kv_to_f32<KV>(x);
+      if (f < flo) { flo = f; lo = x; }
+      if (f > fhi) { fhi = f; hi = x; }
+    }
+    meta[d] = lo;
+    meta[D + d] = hi;
+  }
+}
+
+// Entry i: block blocks[i] over its first counts[i] slots, for head blockIdx.y.
+template <int KV>
+__global__ __launch_bounds__(128) void quest_update_blocks_kernel(
+    const typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ meta,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ counts, int N, int H, int B,
+    int D) {
+  const int b = blocks[blockIdx.x], cnt = counts[blockIdx.x], h = blockIdx.y;
+  if (b < 0 || b >= N || cnt < 1 || cnt > B) return;
+  const int64_t slab = int64_t(b) * H + h;
+  slab_minmax<KV>(k_pool + slab * B * D, meta + slab * 2 * D, cnt, D);
+}
+
+// Row blockIdx.x: the block that holds its last token (context_lens - 1).
+template <int KV>
+__global__ __launch_bounds__(128) void quest_update_tails_kernel(
+    const typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ meta,
+    const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens, int N,
+    int H, int B, int D) {
+  const int len = lens[blockIdx.x], h = blockIdx.y;
+  if (len <= 0) return;
+  const int j = (len - 1) / B;
+  if (j >= max_blocks) return;
+  const int b = tables[int64_t(blockIdx.x) * max_blocks + j];
+  if (b < 0 || b >= N) return;
+  const int64_t slab = int64_t(b) * H + h;
+  slab_minmax<KV>(k_pool + slab * B * D, meta + slab * 2 * D, (len - 1) % B + 1, D);
+}
+
+// ------------------------------------------------------------------------ scores
+
+template <int KV>
+__device__ __forceinline__ void load8(const typename KvTraits<KV>::T* p, float (&f)[8]);
+template <>
+__device__ __forceinline__ void load8<KV_F32>(const float* p, float (&f)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<KV_BF16>(const uint16_t* p, float (&f)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<KV_FP8>(const uint8_t* p, float (&f)[8]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = e4m3_to_f32((u.x >> (8 * i)) & 0xffu);
+    f[4 + i] = e4m3_to_f32((u.y >> (8 * i)) & 0xffu);
+  }
+}
+
+template <typename QT>
+__device__ __forceinline__ void load_q8(const QT* p, float (&f)[8]);
+template <>
+__device__ __forceinline__ void load_q8<float>(const float* p, float (&f)[8]) {
+  load8<KV_F32>(p, f);
+}
+template <>
+__device__ __forceinline__ void load_q8<uint16_t>(const uint16_t* p, float (&f)[8]) {
+  load8<KV_BF16>(p, f);
+}
+
+// Workgroup (pair, chunk): bounds of blocks [chunk * 64, chunk * 64 + 64) of
+// the pair's context.  D / 8 lanes share a block, 8 channels each; each lane
+// keeps its channels of the group's g queries in registers.  The per-head
+// bound is summed lane-locally (8 channels) and then over the lanes by a
+// butterfly; the score is the largest over the g heads.  Pairs whose context
+// fits the budget are not scored (the selection keeps all their blocks).
+template <int KV, typename QT, int D>
+__global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(QuestArgs a) {
+  typedef typename KvTraits<KV>::T T;
+  constexpr int LPB = D / 8;
+  constexpr int BPP = kScoreThreads / LPB;
+  const int pair = blockIdx.x / a.chunks, chunk = blockIdx.x - pair * a.chunks;
+  const int H = a.num_kv_heads, s = pair / H, kvh = pair - s * H;
+  const int B = a.block_size;
+  const int ctx = quest_ctx(a, s);
+  const int nb = (ctx + B - 1) / B;
+  if (nb <= a.budget) return;
+  const int j0 = chunk * kQuestChunk;
+  if (j0 >= nb) return;
+  const int jend = min(nb, j0 + kQuestChunk);
+  const int sub = threadIdx.x % LPB, slot = threadIdx.x / LPB, d0 = sub * 8;
+  const int g = a.group;
+  float qv[kQuestMaxGroup][8];
+  const QT* qrow = static_cast<const QT*>(a.q) + (int64_t(s) * a.num_q_heads + kvh * g) * D + d0;
+#pragma unroll
+  for (int h = 0; h < kQuestMaxGroup; ++h)
+    if (h < g) load_q8<QT>(qrow + h * D, qv[h]);
+  const int32_t* trow = a.tables + int64_t(s) * a.max_blocks;
+  const T* meta = static_cast<const T*>(a.meta);
+  for (int j = j0 + slot; j < jend; j += BPP) {
+    const int pb = trow[j];
+    const bool valid = pb >= 0 && pb < a.num_blocks;
+    float mn[8], mx[8];
+    if (valid) {
+      const T* m = meta + (int64_t(pb) * H + kvh) * 2 * D + d0;
+      load8<KV>(m, mn);
+      load8<KV>(m + D, mx);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mn[i] = mx[i] = 0.f;
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < kQuestMaxGroup; ++h) {
+      if (h < g) {
+        float u = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u = fmaf(qv[h][i], qv[h][i] >= 0.f ? mx[i] : mn[i], u);
+#pragma unroll
+        for (int o = LPB / 2; o > 0; o >>= 1) u += __shfl_xor(u, o);
+        best = fmaxf(best, u);
+      }
+    }
+    if (sub == 0) a.scores[int64_t(pair) * a.score_stride + j] = valid ? best : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------------ selection
+
+// float -> uint32 with the same order (larger float, larger key).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int scan64_incl(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of v over the workgroup's threads in thread order.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int incl = scan64_incl(v, lane);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wv; ++w) off += wsum[w];
+  __syncthreads();
+  return off + incl - v;
+}
+
+// Histogram update from one key per lane (part: the lane takes part).  Scores
+// of one context often share their leading byte, so the lanes of the two most
+// common digits of the wave are added with one atomic each.
+__device__ __forceinline__ void hist_add(int* hist, bool part, int digit, int lane) {
+  uint64_t m = __ballot(part);
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    if (!m) break;
+    const int leader = __builtin_ctzll(m);
+    const int d0 = __shfl(digit, leader);
+    const uint64_t same = __ballot(part && digit == d0);
+    if (lane == leader) atomicAdd(&hist[d0], int(__popcll(same)));
+    if (digit == d0) part = false;
+    m &= ~same;
+  }
+  if (part) atomicAdd(&hist[digit], 1);
+}
+
+__global__ __launch_bounds__(kSelThreads) void quest_select_kernel(QuestArgs a) {
+  __shared__ int hist[256];
+  __shared__ int wsum[kSelThreads / 64];
+  __shared__ int sh_digit, sh_above;
+  const int pair = blockIdx.x;
+  const int H = a.num_kv_heads, s = pair / H, kvh = pair - s * H;
+  const int B = a.block_size;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ctx = quest_ctx(a, s);
+  const int nb = (ctx + B - 1) / B;
+  const int32_t* trow = a.tables + int64_t(s) * a.max_blocks;
+  int32_t* orow = a.sel_tables + int64_t(pair) * a.out_stride;
+  auto slab_id = [&](int pb) { return (pb >= 0 && pb < a.num_blocks) ? pb * H + kvh : -1; };
+  if (nb <= a.budget) {
+    for (int j = tid; j < nb; j += kSelThreads) orow[j] = slab_id(trow[j]);
+    if (tid == 0) a.sel_lens[pair] = ctx;
+    return;
+  }
+  const int nper = (nb + kSelThreads - 1) / kSelThreads;  // keys per thread (uniform)
+  const int first = tid * nper;
+  const float* srow = a.scores + int64_t(pair) * a.score_stride;
+  uint32_t key[kSelPerThread];
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {
+    key[i] = 0;
+    if (i < nper && first + i < nb) {
+      key[i] = order_key(srow[first + i]);
+      vmask |= 1u << i;
+    }
+  }
+  // K-th largest key: 8 bits per pass, most significant first
+  uint32_t prefix = 0, pmask = 0;
+  int k = a.budget;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i) {
+      if (i < nper) {
+        const bool part = ((vmask >> i) & 1u) && (key[i] & pmask) == prefix;
+        hist_add(hist, part, int((key[i] >> shift) & 0xffu), lane);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int h[4], tot = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        h[c] = hist[4 * tid + c];
+        tot += h[c];
+      }
+      int incl = tot;  // keys in this lane's bins and all higher ones
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_down(incl, o);
+        if (tid + o < 64) incl += t;
+      }
+      int above = incl - tot;
+#pragma unroll
+      for (int c = 3; c >= 0; --c) {
+        if (above < k && above + h[c] >= k) {
+          sh_digit = 4 * tid + c;
+          sh_above = above;
+        }
+        above += h[c];
+      }
+    }
+    __syncthreads();
+    prefix |= uint32_t(sh_digit) << shift;
+    pmask |= 0xffu << shift;
+    k -= sh_above;
+  }
+  const uint32_t kth = prefix;  // keys above it are kept, and the first k equal to it
+  int ceq = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i)
+    if (((vmask >> i) & 1u) && key[i] == kth) ++ceq;
+  int eq_rank = block_excl_scan(ceq, wsum);
+  uint32_t sel = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {
+    if (!((vmask >> i) & 1u)) continue;
+    if (key[i] > kth) {
+      sel |= 1u << i;
+    } else if (key[i] == kth) {
+      if (eq_rank < k) sel |= 1u << i;
+      ++eq_rank;
+    }
+  }
+  int pos = block_excl_scan(__popc(sel), wsum);
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i)
+    if (((sel >> i) & 1u) && pos < a.budget) orow[pos++] = slab_id(trow[first + i]);
+  // the thread holding the last block knows whether the partial block is kept
+  const int last = nb - 1;
+  if (last >= first && last < first + nper) {
+    const bool kept = (sel >> (last - first)) & 1u;
+    a.sel_lens[pair] = a.budget * B - (kept ? nb * B - ctx : 0);
+  }
+}
+
+// ------------------------------------------------------------------------ host side
+
+static size_t qalign(size_t n) { return (n + 255) & ~size_t(255); }
+static bool qaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct QuestLayout {
+  int64_t pairs, score_stride, out_stride, chunks;
+  int32_t max_ctx2;
+  size_t tables_off, lens_off, dec_off, dec_bytes, total;
+};
+
+static int quest_layout(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_blocks, int32_t max_ctx, int32_t partition_size,
+                        int32_t budget, QuestLayout* L) {
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks < 0 || max_ctx < 0 || partition_size < 0)
+    return fail(PKV_E_INVAL, "negative size");
+  if (num_q_heads % c->num_kv_heads)
+    return fail(PKV_E_INVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                c->num_kv_heads);
+  if (num_q_heads / c->num_kv_heads > kQuestMaxGroup)
+    return fail(PKV_E_UNSUPPORTED, "group size %d > %d", num_q_heads / c->num_kv_heads,
+                kQuestMaxGroup);
+  if (budget < 1) return fail(PKV_E_INVAL, "budget_blocks %d < 1", budget);
+  if (int64_t(max_blocks) * c->block_size < max_ctx)
+    return fail(PKV_E_INVAL, "max_blocks_per_seq %d cannot hold max_context_len %d", max_blocks,
+                max_ctx);
+  if (int64_t(c->num_blocks) * c->num_kv_heads >= (int64_t(1) << 31))
+    return fail(PKV_E_INVAL, "num_blocks * num_kv_heads does not fit 31 bits");
+  L->pairs = int64_t(num_seqs) * c->num_kv_heads;
+  L->score_stride = std::max<int64_t>(1, (int64_t(max_ctx) + c->block_size - 1) / c->block_size);
+  if (L->score_stride > kQuestMaxBlocks)
+    return fail(PKV_E_UNSUPPORTED, "contexts of more than %d blocks", kQuestMaxBlocks);
+  L->out_stride = std::max<int64_t>(1, std::min<int64_t>(max_blocks, budget));
+  L->chunks = (L->score_stride + kQuestChunk - 1) / kQuestChunk;
+  if (L->pairs * L->score_stride >= (int64_t(1) << 31) || L->pairs * L->chunks >= (int64_t(1) << 31))
+    return fail(PKV_E_INVAL, "batch too large for one call");
+  L->max_ctx2 = int32_t(std::min<int64_t>(max_ctx, L->out_stride * c->block_size));
+  const size_t scores = qalign(size_t(L->pairs) * L->score_stride * sizeof(float));
+  L->tables_off = scores;
+  L->lens_off = L->tables_off + qalign(size_t(L->pairs) * L->out_stride * sizeof(int32_t));
+  L->dec_off = L->lens_off + qalign(size_t(L->pairs) * sizeof(int32_t));
+  L->dec_bytes = pkv_decode_workspace_bytes(int32_t(std::max<int64_t>(1, L->pairs)),
+                                            num_q_heads / c->num_kv_heads, c->head_dim,
+                                            L->max_ctx2, partition_size);
+  L->total = L->dec_off + L->dec_bytes;
+  return PKV_OK;
+}
+
+template <typename K>
+static int qlaunch(K kernel, dim3 grid, dim3 block, hipStream_t s, const char* what,
+                   const QuestArgs& a) {
+  kernel<<<grid, block, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+template <int D>
+static int launch_score(const QuestArgs& a, int kv, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads * a.chunks));
+  const dim3 block(kScoreThreads);
+  if (kv == PKV_F32) return qlaunch(quest_score_kernel<KV_F32, float, D>, grid, block, s, "score", a);
+  if (kv == PKV_BF16)
+    return qlaunch(quest_score_kernel<KV_BF16, uint16_t, D>, grid, block, s, "score", a);
+  return qlaunch(quest_score_kernel<KV_FP8, uint16_t, D>, grid, block, s, "score", a);
+}
+
+// Validates, fills the arguments and launches scoring + selection.
+static int quest_select_impl(const void* q, int32_t q_dtype, const void* meta,
+                             const pkv_cache_desc* c, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_ctx, int32_t budget,
+                             int32_t* sel_tables, int32_t* sel_lens, void* workspace,
+                             size_t workspace_bytes, const QuestLayout& L, hipStream_t s) {
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
+    return fail(PKV_E_INVAL, "q_dtype must be f32 or bf16");
+  if ((c->kv_dtype == PKV_F32) != (q_dtype == PKV_F32))
+    return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(q_dtype),
+                dtype_name(c->kv_dtype));
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !meta || !block_tables || !context_lens || !sel_tables || !sel_lens || !workspace)
+    return fail(PKV_E_INVAL, "NULL pointer");
+  if (!qaligned16(q) || !qaligned16(meta) || !qaligned16(workspace))
+    return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
+  if (workspace_bytes < L.tables_off)
+    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", L.tables_off,
+                workspace_bytes);
+  QuestArgs a;
+  a.q = q;
+  a.meta = meta;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.scores = static_cast<float*>(workspace);
+  a.sel_tables = sel_tables;
+  a.sel_lens = sel_lens;
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.group = num_q_heads / c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.block_size = c->block_size;
+  a.max_ctx = max_ctx;
+  a.budget = budget;
+  a.score_stride = int32_t(L.score_stride);
+  a.out_stride = int32_t(L.out_stride);
+  a.chunks = int32_t(L.chunks);
+  int rc = c->head_dim == 64 ? launch_score<64>(a, c->kv_dtype, s)
+                             : launch_score<128>(a, c->kv_dtype, s);
+  if (rc) return rc;
+  return qlaunch(quest_select_kernel, dim3(static_cast<unsigned>(L.pairs)), dim3(kSelThreads), s,
+                 "select", a);
+}
+
+template <int KV>
+static int launch_update_blocks(const pkv_cache_desc* c, const void* k_pool, void* meta,
+                                const int32_t* blocks, const int32_t* counts, int32_t n,
+                                hipStream_t s) {
+  typedef typename KvTraits<KV>::T T;
+  quest_update_blocks_kernel<KV><<<dim3(n, c->num_kv_heads), dim3(128), 0, s>>>(
+      static_cast<const T*>(k_pool), static_cast<T*>(meta), blocks, counts, c->num_blocks,
+      c->num_kv_heads, c->block_size, c->head_dim);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "quest update launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+template <int KV>
+static int launch_update_tails(const pkv_cache_desc* c, const void* k_pool, void* meta,
+                               const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                               int32_t n, hipStream_t s) {
+  typedef typename KvTraits<KV>::T T;
+  quest_update_tails_kernel<KV><<<dim3(n, c->num_kv_heads), dim3(128), 0, s>>>(
+      static_cast<const T*>(k_pool), static_cast<T*>(meta), tables, max_blocks, lens,
+      c->num_blocks, c->num_kv_heads, c->block_size, c->head_dim);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "quest update launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t pkv_quest_meta_bytes(const pkv_cache_desc* c) {
+  if (!c || check_desc(c)) return 0;
+  return size_t(c->num_blocks) * c->num_kv_heads * 2 * c->head_dim * elem_bytes(c->kv_dtype);
+}
+
+extern "C" int pkv_quest_update_blocks(const void* k_pool, const pkv_cache_desc* c, void* meta,
+                                       const int32_t* blocks, const int32_t* counts, int32_t n,
+                                       void* stream) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (n < 0) return fail(PKV_E_INVAL, "negative count");
+  if (n == 0) return PKV_OK;
+  if (!k_pool || !meta || !blocks || !counts) return fail(PKV_E_INVAL, "NULL pointer");
+  if (!qaligned16(k_pool) || !qaligned16(meta))
+    return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->kv_dtype == PKV_F32) return launch_update_blocks<KV_F32>(c, k_pool, meta, blocks, counts, n, s);
+  if (c->kv_dtype == PKV_BF16) return launch_update_blocks<KV_BF16>(c, k_pool, meta, blocks, counts, n, s);
+  return launch_update_blocks<KV_FP8>(c, k_pool, meta, blocks, counts, n, s);
+}
+
+extern "C" int pkv_quest_update_tails(const void* k_pool, const pkv_cache_desc* c, void* meta,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      void* stream) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return fail(PKV_E_INVAL, "negative size");
+  if (num_seqs == 0 || max_blocks_per_seq == 0) return PKV_OK;
+  if (!k_pool || !meta || !block_tables || !context_lens) return fail(PKV_E_INVAL, "NULL pointer");
+  if (!qaligned16(k_pool) || !qaligned16(meta))
+    return fail(PKV_E_INVAL, "device pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->kv_dtype == PKV_F32)
+    return launch_update_tails<KV_F32>(c, k_pool, meta, block_tables, max_blocks_per_seq,
+                                       context_lens, num_seqs, s);
+  if (c->kv_dtype == PKV_BF16)
+    return launch_update_tails<KV_BF16>(c, k_pool, meta, block_tables, max_blocks_per_seq,
+                                        context_lens, num_seqs, s);
+  return launch_update_tails<KV_FP8>(c, k_pool, meta, block_tables, max_blocks_per_seq,
+                                     context_lens, num_seqs, s);
+}
+
+extern "C" size_t pkv_quest_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                            int32_t max_context_len, int32_t partition_size,
+                                            int32_t budget_blocks) {
+  QuestLayout L;
+  clear_error();
+  if (quest_layout(c, std::max(num_seqs, 1), num_q_heads, max_blocks_per_seq, max_context_len,
+                   partition_size, budget_blocks, &L))
+    return 0;
+  return L.total;
+}
+
+extern "C" int pkv_quest_select(const void* q, int32_t q_dtype, const void* meta,
+                                const pkv_cache_desc* c, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                int32_t budget_blocks, int32_t* sel_tables, int32_t* sel_lens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  QuestLayout L;
+  int rc = quest_layout(c, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len, 0,
+                        budget_blocks, &L);
+  if (rc) return rc;
+  return quest_select_impl(q, q_dtype, meta, c, block_tables, max_blocks_per_seq, context_lens,
+                           num_seqs, num_q_heads, max_context_len, budget_blocks, sel_tables,
+                           sel_lens, workspace, workspace_bytes, L,
+                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pkv_quest_decode(const void* q, int32_t q_dtype, const void* k_pool,
+                                const void* v_pool, const void* meta, const pkv_cache_desc* c,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, float scale, void* out,
+                                int32_t max_context_len, int32_t partition_size,
+                                int32_t budget_blocks, void* workspace, size_t workspace_bytes,
+                                void* stream, int32_t impl) {
+  clear_error();
+  QuestLayout L;
+  int rc = quest_layout(c, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
+                        partition_size, budget_blocks, &L);
+  if (rc) return rc;
+  if (num_seqs == 0) return PKV_OK;
+  if (!workspace || workspace_bytes < L.total)
+    return fail(PKV_E_INVAL, "workspace of %zu bytes needed (got %zu)", L.total, workspace_bytes);
+  if (!k_pool || !v_pool || !out) return fail(PKV_E_INVAL, "NULL pointer");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* sel_tables = reinterpret_cast<int32_t*>(ws + L.tables_off);
+  int32_t* sel_lens = reinterpret_cast<int32_t*>(ws + L.lens_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = quest_select_impl(q, q_dtype, meta, c, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, num_q_heads, max_context_len, budget_blocks, sel_tables,
+                         sel_lens, workspace, workspace_bytes, L, s);
+  if (rc) return rc;
+  // the pools as [N * H] one-head blocks; one "sequence" per (sequence, KV head)
+  pkv_cache_desc slabs = *c;
+  slabs.num_blocks = c->num_blocks * c->num_kv_heads;
+  slabs.num_kv_heads = 1;
+  return pkv_paged_attn_decode_ex(q, q_dtype, k_pool, v_pool, &slabs, sel_tables,
+                                  int32_t(L.out_stride), sel_lens, int32_t(L.pairs),
+                                  num_q_heads / c->num_kv_heads, scale, out, L.max_ctx2,
+                                  partition_size, ws + L.dec_off, L.dec_bytes, stream, impl);
+}

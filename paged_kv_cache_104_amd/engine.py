@@ -20,8 +20,9 @@ from typing import Callable, Optional, Sequence
 import numpy as np
 
 from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_host_pools,
-               alloc_pools, append_tokens, copy_blocks, decode_workspace_bytes,
-               paged_attn_decode, reshape_and_cache, swap_blocks)
+               alloc_pools, alloc_quest_meta, append_tokens, copy_blocks, decode_workspace_bytes,
+               paged_attn_decode, quest_blocks_of_slots, quest_decode, quest_update_blocks,
+               quest_update_tails, reshape_and_cache, swap_blocks)
 
 
 def to_device(x: np.ndarray, in_dtype: str, device):
@@ -44,6 +45,7 @@ class PagedKVCache:
         if prefix_caching:
             self.bm.set_prefix_caching(True)
         self.k_pool, self.v_pool = alloc_pools(desc, device, poison)
+        self.quest_meta = None
 
     # -- device work ------------------------------------------------------------
     def write(self, k, v, slots) -> None:
@@ -51,6 +53,9 @@ class PagedKVCache:
 
         slot_t = torch.as_tensor(np.ascontiguousarray(slots, dtype=np.int64)).to(self.device)
         reshape_and_cache(k, v, slot_t, self.k_pool, self.v_pool, self.desc)
+        if self.quest_meta is not None:
+            blocks, counts = quest_blocks_of_slots(slots, self.desc.block_size)
+            quest_update_blocks(self.k_pool, self.quest_meta, blocks, counts, self.desc)
 
     def copy(self, pairs) -> None:
         if len(pairs):
@@ -72,7 +77,38 @@ class PagedKVCache:
     def swap_in(self, seqs, method: str = "kernel"):
         pairs = self.bm.swap_in(seqs)
         swap_blocks(self.host_k, self.host_v, self.k_pool, self.v_pool, pairs, self.desc, method)
+        if self.quest_meta is not None and len(pairs):
+            self.quest_refresh(seqs)          # the set holds every sharer of its blocks
         return pairs
+
+    # -- query-aware block selection -----------------------------------------
+    def enable_quest(self, live_seqs: Sequence[int] = ()) -> None:
+        """Keep per-block key minimum / maximum metadata from now on (computed now for the
+        blocks of ``live_seqs``; later writes, appends and swap-ins keep it current)."""
+        self.quest_meta = alloc_quest_meta(self.desc, self.device)
+        self.quest_refresh(live_seqs)
+
+    def quest_refresh(self, seqs) -> None:
+        """Recompute the metadata of every block of ``seqs`` from the key pool."""
+        B = self.desc.block_size
+        fill = {}
+        for s in seqs:
+            n = self.bm.seq_len(int(s))
+            for j, b in enumerate(self.bm.seq_blocks(int(s))):
+                fill[b] = max(fill.get(b, 0), min(B, n - j * B))
+        if fill:
+            blocks = np.fromiter(fill.keys(), dtype=np.int32, count=len(fill))
+            counts = np.fromiter(fill.values(), dtype=np.int32, count=len(fill))
+            quest_update_blocks(self.k_pool, self.quest_meta, blocks, counts, self.desc)
+
+    def quest_decode(self, q, out, tables, lens, scale: float, max_context_len: int,
+                     budget_blocks: int, partition_size: int = 0, workspace=None,
+                     impl: int = IMPL_AUTO):
+        if self.quest_meta is None:
+            raise RuntimeError("enable_quest() first")
+        return quest_decode(q, self.k_pool, self.v_pool, self.quest_meta, self.desc, tables,
+                            lens, scale, out, max_context_len, budget_blocks, partition_size,
+                            workspace, impl)
 
     # -- allocator script ----------------------------------------------------
     def run_script(self, ops, kv_input: Callable[[int], tuple], in_dtype: str,
@@ -198,6 +234,8 @@ class DecodeBatch:
         c.copy(pairs)
         append_tokens(k_new, v_new, slots, self.host_lens, c.k_pool, c.v_pool, c.desc,
                       self.tables, self.lens)
+        if c.quest_meta is not None:
+            quest_update_tails(c.k_pool, c.quest_meta, self.tables, self.lens, c.desc)
         self.host_lens += 1
         return slots, pairs
 
