@@ -300,6 +300,80 @@ def swap_sweep(total_bytes: int, reps: int, methods=("kernel", "dma")) -> None:
     print(json.dumps({"swap_sweep": rows, "bytes_per_direction": total_bytes, "reps": reps}))
 
 
+def quest_bench(wl, budget: int, steps: int, warmup: int, partition_size: int, impl: int,
+                workers: int) -> None:
+    """QUEST decode against the dense decode on the same decode steps.
+
+    Each step appends one token per sequence (block manager, copies, the write and
+    the table update, then the metadata of every row's last block); the QUEST
+    decode (scoring, selection, decode kernel, merge) and the dense decode then run
+    on the same state, each between a pair of HIP events.  Bytes QUEST reads: the
+    metadata of every block of every context (2 rows of head_dim per block and KV
+    head) plus the K and V of the chosen tokens."""
+    import torch
+
+    import paged_kv_cache_104_amd as pkv
+    from paged_kv_cache_104_amd.engine import DecodeBatch
+
+    cache, desc, seqs, q, k_new, v_new = build_gpu_state(wl, workers)
+    S, B, H, D = len(seqs), wl.block_size, wl.num_kv_heads, wl.head_dim
+    total = warmup + steps
+    max_ctx = wl.max_context_len + total
+    max_blocks = -(-max_ctx // B)
+    batch = DecodeBatch(cache, seqs, max_blocks)
+    cache.enable_quest(seqs)
+    elt = {"bf16": 2, "fp8": 1, "f32": 4}[wl.kv_dtype]
+    qws = torch.empty(pkv.quest_workspace_bytes(desc, S, wl.num_q_heads, max_blocks, max_ctx,
+                                                partition_size, budget),
+                      dtype=torch.uint8, device="cuda")
+    dws = torch.empty(max(16, pkv.decode_workspace_bytes(S, wl.num_q_heads, D, max_ctx,
+                                                         partition_size)),
+                      dtype=torch.uint8, device="cuda")
+    out_q, out_d = torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    for e in [x for row in ev for x in row]:
+        e.record(stream)
+    torch.cuda.synchronize()
+    meta_bytes, kv_bytes = np.zeros(total), np.zeros(total)
+    for i in range(total):
+        batch.append(k_new, v_new)
+        lens = batch.host_lens
+        meta_bytes[i] = float((-(-lens // B)).sum()) * H * 2 * D * elt
+        kv_bytes[i] = float(lens.sum()) * wl.kv_bytes_per_token()
+        e = ev[i]
+        e[0].record(stream)
+        pkv.quest_decode(q, cache.k_pool, cache.v_pool, cache.quest_meta, desc, batch.tables,
+                         batch.lens, wl.scale, out_q, max_ctx, budget, partition_size, qws, impl)
+        e[1].record(stream)
+        pkv.paged_attn_decode(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens, wl.scale,
+                              out_d, desc, max_ctx, partition_size, dws, impl)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    # tokens actually chosen in the last step (the selection is deterministic)
+    _, sel_l = pkv.quest_select(q, cache.quest_meta, desc, batch.tables, batch.lens, max_ctx,
+                                budget)
+    chosen = float(sel_l.sum().item()) * 2 * D * elt
+    timed = range(warmup, total)
+    tq = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed]) * 1e-3
+    td = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed]) * 1e-3
+    assert torch.isfinite(out_q.float()).all(), "non-finite QUEST output"
+    last_bytes = meta_bytes[-1] + chosen
+    rate = last_bytes / float(tq[-5:].mean()) / 1e9
+    print(json.dumps({"quest": {
+        "workload": wl.name, "budget_blocks": budget, "budget_tokens": budget * B,
+        "steps": steps, "warmup": warmup, "partition_size": partition_size,
+        "quest_ms": round(float(tq.mean()) * 1e3, 4),
+        "dense_ms": round(float(td.mean()) * 1e3, 4),
+        "speedup_vs_dense": round(float(td.mean() / tq.mean()), 3),
+        "last_step": {"metadata_bytes": int(meta_bytes[-1]), "chosen_kv_bytes": int(chosen),
+                      "dense_kv_bytes": int(kv_bytes[-1]),
+                      "kept_fraction": round(chosen / kv_bytes[-1], 4)},
+        "achieved_GBps": round(rate, 1), "frac_of_hbm_peak": round(rate / HBM_PEAK_GBS, 4),
+        "dense_GBps": round(float(kv_bytes[-1]) / float(td[-5:].mean()) / 1e9, 1),
+    }}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +389,9 @@ def main() -> int:
     ap.add_argument("--swap-sweep", type=int, default=0, metavar="BYTES",
                     help="measure swapping rates moving BYTES of K+V each way, then exit")
     ap.add_argument("--swap-methods", default="kernel,dma")
+    ap.add_argument("--quest-budget", type=int, default=0, metavar="BLOCKS",
+                    help="time the QUEST decode with this budget against the dense decode "
+                         "on --config, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -334,6 +411,10 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = workloads.get(args.config)
+    if args.quest_budget:
+        ps = wl.partition_size if args.partition_size is None else args.partition_size
+        quest_bench(wl, args.quest_budget, args.steps, args.warmup, ps, args.impl, args.workers)
+        return 0
     wl.cache_sequences = True          # keep the drawn inputs for the oracle's sample
     ps = wl.partition_size if args.partition_size is None else args.partition_size
     r = run_gpu(wl, args.steps, args.warmup, ps, args.impl, args.workers)

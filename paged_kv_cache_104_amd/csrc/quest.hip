@@ -14,7 +14,8 @@
 //  * quest_score_kernel: one bound per (sequence, KV head, block), the largest
 //    over the KV head's query heads (grouped-query attention), into a
 //    workspace row per (sequence, KV head).  Reads only metadata.
-//  * quest_select_kernel: one workgroup per (sequence, KV head); a 4-pass radix
+//  * quest_select_kernel: one workgroup per (sequence, KV head) (256 threads up
+//    to 4096 blocks, 1024 up to 16384, 16 keys per thread); a 4-pass radix
 //    select of the K-th largest bound (keys held in registers, histograms in
 //    LDS), ties to the lower block index, then the chosen blocks compacted in
 //    logical order into a per-(sequence, KV head) block table.  Its entries
@@ -26,6 +27,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -34,7 +36,8 @@ namespace pkv {
 
 constexpr int kQuestChunk = 64;        // blocks per scoring workgroup
 constexpr int kScoreThreads = 256;
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreadsSmall = 256;  // selecting workgroup for contexts of <= 4096 blocks
+constexpr int kSelThreads = 1024;      // ... and up to 16384 blocks
 constexpr int kSelPerThread = 16;      // keys held by one selecting thread
 constexpr int kQuestMaxBlocks = kSelThreads * kSelPerThread;
 constexpr int kQuestMaxGroup = 16;
@@ -117,57 +120,67 @@ __global__ __launch_bounds__(128) void quest_update_tails_kernel(
 
 // ------------------------------------------------------------------------ scores
 
+// Eight consecutive stored values, kept packed until they are used.
 template <int KV>
-__device__ __forceinline__ void load8(const typename KvTraits<KV>::T* p, float (&f)[8]);
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<KV_F32>(const float* p, float (&f)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+struct Raw8<KV_F32> { float4 a, b; };
+template <>
+struct Raw8<KV_BF16> { uint4 a; };
+template <>
+struct Raw8<KV_FP8> { uint2 a; };
+
+template <int KV>
+__device__ __forceinline__ Raw8<KV> load_raw8(const typename KvTraits<KV>::T* p);
+template <>
+__device__ __forceinline__ Raw8<KV_F32> load_raw8<KV_F32>(const float* p) {
+  return Raw8<KV_F32>{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
 }
 template <>
-__device__ __forceinline__ void load8<KV_BF16>(const uint16_t* p, float (&f)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ Raw8<KV_BF16> load_raw8<KV_BF16>(const uint16_t* p) {
+  return Raw8<KV_BF16>{*reinterpret_cast<const uint4*>(p)};
+}
+template <>
+__device__ __forceinline__ Raw8<KV_FP8> load_raw8<KV_FP8>(const uint8_t* p) {
+  return Raw8<KV_FP8>{*reinterpret_cast<const uint2*>(p)};
+}
+
+__device__ __forceinline__ void unpack8(const Raw8<KV_F32>& r, float (&f)[8]) {
+  f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+  f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+}
+__device__ __forceinline__ void unpack8(const Raw8<KV_BF16>& r, float (&f)[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
     f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
 }
-template <>
-__device__ __forceinline__ void load8<KV_FP8>(const uint8_t* p, float (&f)[8]) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ void unpack8(const Raw8<KV_FP8>& r, float (&f)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[i] = e4m3_to_f32((u.x >> (8 * i)) & 0xffu);
-    f[4 + i] = e4m3_to_f32((u.y >> (8 * i)) & 0xffu);
+    f[i] = e4m3_to_f32((r.a.x >> (8 * i)) & 0xffu);
+    f[4 + i] = e4m3_to_f32((r.a.y >> (8 * i)) & 0xffu);
   }
 }
 
-template <typename QT>
-__device__ __forceinline__ void load_q8(const QT* p, float (&f)[8]);
-template <>
-__device__ __forceinline__ void load_q8<float>(const float* p, float (&f)[8]) {
-  load8<KV_F32>(p, f);
-}
-template <>
-__device__ __forceinline__ void load_q8<uint16_t>(const uint16_t* p, float (&f)[8]) {
-  load8<KV_BF16>(p, f);
-}
-
 // Workgroup (pair, chunk): bounds of blocks [chunk * 64, chunk * 64 + 64) of
-// the pair's context.  D / 8 lanes share a block, 8 channels each; each lane
-// keeps its channels of the group's g queries in registers.  The per-head
-// bound is summed lane-locally (8 channels) and then over the lanes by a
-// butterfly; the score is the largest over the g heads.  Pairs whose context
-// fits the budget are not scored (the selection keeps all their blocks).
+// the pair's context.  D / 8 lanes share a block, 8 channels each, so a
+// block's minimum and maximum rows are read with coalesced 16-byte loads.
+// Every table entry and then every metadata row of the chunk is requested
+// before any arithmetic, so the workgroup waits for memory twice in all.  The
+// group's queries sit in LDS as fp32.  Each lane sums its 8 channels per head,
+// a butterfly over the block's lanes completes the bound, and the score is the
+// largest bound over the group's heads.  Pairs whose context fits the budget
+// are not scored (the selection keeps all their blocks).
 template <int KV, typename QT, int D>
 __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(QuestArgs a) {
   typedef typename KvTraits<KV>::T T;
-  constexpr int LPB = D / 8;
-  constexpr int BPP = kScoreThreads / LPB;
+  constexpr int LPB = D / 8;                 // lanes per block
+  constexpr int BPP = kScoreThreads / LPB;   // blocks per pass
+  constexpr int PASSES = kQuestChunk / BPP;
+  __shared__ float q_s[kQuestMaxGroup][D];
   const int pair = blockIdx.x / a.chunks, chunk = blockIdx.x - pair * a.chunks;
   const int H = a.num_kv_heads, s = pair / H, kvh = pair - s * H;
   const int B = a.block_size;
@@ -177,40 +190,58 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(QuestArgs a)
   const int j0 = chunk * kQuestChunk;
   if (j0 >= nb) return;
   const int jend = min(nb, j0 + kQuestChunk);
-  const int sub = threadIdx.x % LPB, slot = threadIdx.x / LPB, d0 = sub * 8;
+  const int tid = threadIdx.x, sub = tid % LPB, slot = tid / LPB, d0 = sub * 8;
   const int g = a.group;
-  float qv[kQuestMaxGroup][8];
-  const QT* qrow = static_cast<const QT*>(a.q) + (int64_t(s) * a.num_q_heads + kvh * g) * D + d0;
-#pragma unroll
-  for (int h = 0; h < kQuestMaxGroup; ++h)
-    if (h < g) load_q8<QT>(qrow + h * D, qv[h]);
   const int32_t* trow = a.tables + int64_t(s) * a.max_blocks;
+  int pb[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int j = j0 + slot + p * BPP;
+    pb[p] = j < jend ? trow[j] : -1;
+  }
   const T* meta = static_cast<const T*>(a.meta);
-  for (int j = j0 + slot; j < jend; j += BPP) {
-    const int pb = trow[j];
-    const bool valid = pb >= 0 && pb < a.num_blocks;
+  // unconditional loads (an entry outside the pool reads block 0 and scores -inf),
+  // so no branch separates the requests
+  Raw8<KV> rmn[PASSES], rmx[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int b = (pb[p] >= 0 && pb[p] < a.num_blocks) ? pb[p] : 0;
+    const T* m = meta + (int64_t(b) * H + kvh) * 2 * D + d0;
+    rmn[p] = load_raw8<KV>(m);
+    rmx[p] = load_raw8<KV>(m + D);
+  }
+  // q after the metadata requests (its wait covers both), 8 values per thread
+  constexpr int QKV = std::is_same<QT, float>::value ? KV_F32 : KV_BF16;
+  const QT* qrow = static_cast<const QT*>(a.q) + (int64_t(s) * a.num_q_heads + kvh * g) * D;
+  for (int i = tid * 8; i < g * D; i += kScoreThreads * 8) {
+    float f[8];
+    unpack8(load_raw8<QKV>(qrow + i), f);
+    *reinterpret_cast<float4*>(&q_s[i / D][i % D]) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(&q_s[i / D][i % D + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int j = j0 + slot + p * BPP;
+    if (j0 + p * BPP >= jend) break;          // uniform: no block of this pass is in range
     float mn[8], mx[8];
-    if (valid) {
-      const T* m = meta + (int64_t(pb) * H + kvh) * 2 * D + d0;
-      load8<KV>(m, mn);
-      load8<KV>(m + D, mx);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mn[i] = mx[i] = 0.f;
-    }
+    unpack8(rmn[p], mn);
+    unpack8(rmx[p], mx);
     float best = -INFINITY;
+    for (int h = 0; h < g; ++h) {
+      const float4 qa = *reinterpret_cast<const float4*>(&q_s[h][d0]);
+      const float4 qb = *reinterpret_cast<const float4*>(&q_s[h][d0 + 4]);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      float u = 0.f;
 #pragma unroll
-    for (int h = 0; h < kQuestMaxGroup; ++h) {
-      if (h < g) {
-        float u = 0.f;
+      for (int i = 0; i < 8; ++i) u = fmaf(qv[i], qv[i] >= 0.f ? mx[i] : mn[i], u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u = fmaf(qv[h][i], qv[h][i] >= 0.f ? mx[i] : mn[i], u);
-#pragma unroll
-        for (int o = LPB / 2; o > 0; o >>= 1) u += __shfl_xor(u, o);
-        best = fmaxf(best, u);
-      }
+      for (int o = LPB / 2; o > 0; o >>= 1) u += __shfl_xor(u, o);
+      best = fmaxf(best, u);
     }
-    if (sub == 0) a.scores[int64_t(pair) * a.score_stride + j] = valid ? best : -INFINITY;
+    if (sub == 0 && j < jend)
+      a.scores[int64_t(pair) * a.score_stride + j] =
+          (pb[p] >= 0 && pb[p] < a.num_blocks) ? best : -INFINITY;
   }
 }
 
@@ -222,19 +253,47 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int scan64_incl(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round
+// trips): shifts by 1, 2, 4 and 8 lanes within each row of 16, then the last
+// lane of row 0 into row 1 and of row 2 into row 3, then lane 31 into rows 2
+// and 3.  Lanes a move does not reach add 0.
+__device__ __forceinline__ int scan64_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
+}
+
+// Minimum / maximum over the wave, in every lane: the scan's moves with min / max
+// (lanes a move does not reach take the identity), then lane 63's result.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  int t = int(v);
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x111, 0xf, 0xf, false))));
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x112, 0xf, 0xf, false))));
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x114, 0xf, 0xf, false))));
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x118, 0xf, 0xf, false))));
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x142, 0xa, 0xf, false))));
+  t = int(min(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(-1, t, 0x143, 0xc, 0xf, false))));
+  return uint32_t(__builtin_amdgcn_readlane(t, 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  int t = int(v);
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x111, 0xf, 0xf, false))));
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x112, 0xf, 0xf, false))));
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x114, 0xf, 0xf, false))));
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x118, 0xf, 0xf, false))));
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x142, 0xa, 0xf, false))));
+  t = int(max(uint32_t(t), uint32_t(__builtin_amdgcn_update_dpp(0, t, 0x143, 0xc, 0xf, false))));
+  return uint32_t(__builtin_amdgcn_readlane(t, 63));
 }
 
 // Exclusive prefix sum of v over the workgroup's threads in thread order.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int incl = scan64_incl(v, lane);
+  const int incl = scan64_incl(v);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
   int off = 0;
@@ -243,87 +302,102 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
   return off + incl - v;
 }
 
-// Histogram update from one key per lane (part: the lane takes part).  Scores
-// of one context often share their leading byte, so the lanes of the two most
-// common digits of the wave are added with one atomic each.
-__device__ __forceinline__ void hist_add(int* hist, bool part, int digit, int lane) {
-  uint64_t m = __ballot(part);
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    if (!m) break;
-    const int leader = __builtin_ctzll(m);
-    const int d0 = __shfl(digit, leader);
-    const uint64_t same = __ballot(part && digit == d0);
-    if (lane == leader) atomicAdd(&hist[d0], int(__popcll(same)));
-    if (digit == d0) part = false;
-    m &= ~same;
-  }
-  if (part) atomicAdd(&hist[digit], 1);
-}
-
-__global__ __launch_bounds__(kSelThreads) void quest_select_kernel(QuestArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void quest_select_kernel(QuestArgs a) {
+  static_assert(NT >= 256 && NT % 64 == 0, "one thread per histogram bin at least");
   __shared__ int hist[256];
-  __shared__ int wsum[kSelThreads / 64];
+  __shared__ int wsum[NT / 64];
   __shared__ int sh_digit, sh_above;
+  __shared__ uint32_t wlo[NT / 64], whi[NT / 64];
   const int pair = blockIdx.x;
   const int H = a.num_kv_heads, s = pair / H, kvh = pair - s * H;
   const int B = a.block_size;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int ctx = quest_ctx(a, s);
   const int nb = (ctx + B - 1) / B;
   const int32_t* trow = a.tables + int64_t(s) * a.max_blocks;
   int32_t* orow = a.sel_tables + int64_t(pair) * a.out_stride;
   auto slab_id = [&](int pb) { return (pb >= 0 && pb < a.num_blocks) ? pb * H + kvh : -1; };
   if (nb <= a.budget) {
-    for (int j = tid; j < nb; j += kSelThreads) orow[j] = slab_id(trow[j]);
+    for (int j = tid; j < nb; j += NT) orow[j] = slab_id(trow[j]);
     if (tid == 0) a.sel_lens[pair] = ctx;
     return;
   }
-  const int nper = (nb + kSelThreads - 1) / kSelThreads;  // keys per thread (uniform)
+  const int nper = (nb + NT - 1) / NT;  // keys per thread (uniform)
   const int first = tid * nper;
   const float* srow = a.scores + int64_t(pair) * a.score_stride;
+  // keys first + i for i < nper, with their table entries, all requested before
+  // any is used: every load is unconditional (indices past the thread's share or
+  // the context read the context's last block and are masked out)
   uint32_t key[kSelPerThread];
+  int32_t ent[kSelPerThread];
   uint32_t vmask = 0;
 #pragma unroll
   for (int i = 0; i < kSelPerThread; ++i) {
-    key[i] = 0;
-    if (i < nper && first + i < nb) {
-      key[i] = order_key(srow[first + i]);
-      vmask |= 1u << i;
-    }
+    const int j = min(first + min(i, nper - 1), nb - 1);
+    key[i] = order_key(srow[j]);
+    ent[i] = trow[j];
+    if (i < nper && first + i < nb) vmask |= 1u << i;
   }
-  // K-th largest key: 8 bits per pass, most significant first
-  uint32_t prefix = 0, pmask = 0;
+  // Bits above the highest one in which the smallest and largest key differ are
+  // common to every key (one context's bounds are usually of one magnitude):
+  // the radix passes start below them, so the first pass already spreads the
+  // keys over many bins.
+  uint32_t lo_k = 0xffffffffu, hi_k = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i)
+    if ((vmask >> i) & 1u) {
+      lo_k = min(lo_k, key[i]);
+      hi_k = max(hi_k, key[i]);
+    }
+  lo_k = wave_min_u32(lo_k);
+  hi_k = wave_max_u32(hi_k);
+  if ((tid & 63) == 63) {
+    wlo[tid >> 6] = lo_k;
+    whi[tid >> 6] = hi_k;
+  }
+  __syncthreads();
+  lo_k = wlo[0];
+  hi_k = whi[0];
+  for (int w = 1; w < NT / 64; ++w) {
+    lo_k = min(lo_k, wlo[w]);
+    hi_k = max(hi_k, whi[w]);
+  }
+  // K-th largest key: up to 8 bits per pass below the common bits, most significant first
+  int bits = lo_k == hi_k ? 0 : 32 - __clz(lo_k ^ hi_k);   // bits that still differ
+  uint32_t pmask = bits == 32 ? 0u : ~((1u << bits) - 1u);
+  uint32_t prefix = hi_k & pmask;
   int k = a.budget;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  while (bits > 0) {
+    const int shift = max(bits - 8, 0);
+    const uint32_t dmask = (1u << (bits - shift)) - 1u;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSelPerThread; ++i) {
       if (i < nper) {
-        const bool part = ((vmask >> i) & 1u) && (key[i] & pmask) == prefix;
-        hist_add(hist, part, int((key[i] >> shift) & 0xffu), lane);
+        // plain LDS atomics: lanes that hit one bin are serialised by the LDS, which
+        // costs less than combining them in the wave first
+        if (((vmask >> i) & 1u) && (key[i] & pmask) == prefix)
+          atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
       }
     }
     __syncthreads();
     if (tid < 64) {
+      // lane l holds bins 4 (63 - l) .. 4 (63 - l) + 3, so a prefix sum over the
+      // lanes counts the keys in this lane's bins and every higher bin
+      const int base = 4 * (63 - tid);
       int h[4], tot = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        h[c] = hist[4 * tid + c];
+        h[c] = hist[base + c];
         tot += h[c];
       }
-      int incl = tot;  // keys in this lane's bins and all higher ones
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_down(incl, o);
-        if (tid + o < 64) incl += t;
-      }
-      int above = incl - tot;
+      int above = scan64_incl(tot) - tot;  // keys in higher bins
 #pragma unroll
       for (int c = 3; c >= 0; --c) {
         if (above < k && above + h[c] >= k) {
-          sh_digit = 4 * tid + c;
+          sh_digit = base + c;
           sh_above = above;
         }
         above += h[c];
@@ -331,8 +405,9 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(QuestArgs a) 
     }
     __syncthreads();
     prefix |= uint32_t(sh_digit) << shift;
-    pmask |= 0xffu << shift;
+    pmask |= dmask << shift;
     k -= sh_above;
+    bits = shift;
   }
   const uint32_t kth = prefix;  // keys above it are kept, and the first k equal to it
   int ceq = 0;
@@ -354,7 +429,7 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(QuestArgs a) 
   int pos = block_excl_scan(__popc(sel), wsum);
 #pragma unroll
   for (int i = 0; i < kSelPerThread; ++i)
-    if (((sel >> i) & 1u) && pos < a.budget) orow[pos++] = slab_id(trow[first + i]);
+    if (((sel >> i) & 1u) && pos >= 0 && pos < a.budget) orow[pos++] = slab_id(ent[i]);
   // the thread holding the last block knows whether the partial block is kept
   const int last = nb - 1;
   if (last >= first && last < first + nper) {
@@ -475,8 +550,11 @@ static int quest_select_impl(const void* q, int32_t q_dtype, const void* meta,
   int rc = c->head_dim == 64 ? launch_score<64>(a, c->kv_dtype, s)
                              : launch_score<128>(a, c->kv_dtype, s);
   if (rc) return rc;
-  return qlaunch(quest_select_kernel, dim3(static_cast<unsigned>(L.pairs)), dim3(kSelThreads), s,
-                 "select", a);
+  const dim3 grid(static_cast<unsigned>(L.pairs));
+  if (L.score_stride <= kSelThreadsSmall * kSelPerThread)
+    return qlaunch(quest_select_kernel<kSelThreadsSmall>, grid, dim3(kSelThreadsSmall), s,
+                   "select", a);
+  return qlaunch(quest_select_kernel<kSelThreads>, grid, dim3(kSelThreads), s, "select", a);
 }
 
 template <int KV>
