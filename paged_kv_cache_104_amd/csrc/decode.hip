@@ -225,7 +225,6 @@ struct StepRegs {
   uint4 ka[NK];   // K rows, tile a (MFMA A operand of Q.K^T)
   uint4 kb[NK];   // K rows, tile b
   typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];  // V^T, 8 tokens x 1 dim
-  uint4 q[D / 32];  // Q^T of the step's head group (MFMA B operand of Q.K^T)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -312,7 +311,8 @@ __device__ __forceinline__ uint2 ld8(const void* p) {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int KV, int D>
-__device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, floatx4_t (&acc)[D / 16],
+__device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uint4 (&qv)[D / 32],
+                                             floatx4_t (&acc)[D / 16],
                                              floatx4_t& lsum, float& m, float sl2, int tt, int t1,
                                              int r) {
   // scores S^T[token][head] of the two 16-token tiles
@@ -330,8 +330,8 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, floatx4_t
       ka = as_bf16x8(R.ka[i]);
       kb = as_bf16x8(R.kb[i]);
     }
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(R.q[i]), sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, as_bf16x8(R.q[i]), sb, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(qv[i]), sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, as_bf16x8(qv[i]), sb, 0, 0, 0);
   }
   // lane (r, c): x[e] = raw score of head c for token 8r + e of the step
   float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
@@ -424,22 +424,30 @@ __device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* 
 // 16 bytes of the query through a buffer descriptor over the whole q tensor.
 // An offset at or past the descriptor's size reads zeros without touching
 // memory, which gives the padding columns of the head group a zero query
-// with the same instruction (no branch, so every step issues the same loads).
+// with the same instruction (no branch).
 __device__ __forceinline__ uint4 ld16_q(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
 }
 
-// Issue the loads of one step: K rows, V^T columns and the query of the pair.
-// Only lanes of real heads read the query (the group is padded to 16 MFMA
+// Q^T of one (sequence, KV head) pair's head group, the B operand of Q.K^T:
+// lane (r, c) holds the dimensions qk_dim0(i, r) .. +7 of query head c.  Only
+// lanes of real heads read the query (the group is padded to 16 MFMA
 // columns); the padding columns get a zero query, and their results are
 // computed and never written.
+template <int KV, int D>
+__device__ __forceinline__ void load_query(uint4 (&qv)[D / 32], __amdgpu_buffer_rsrc_t qrsrc,
+                                           uint32_t qoff, bool qlane, uint32_t qoob, int r) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+    qv[i] = ld16_q(qrsrc, qlane ? qoff + 2u * uint32_t(qk_dim0<KV>(i, r)) : qoob);
+}
+
+// Issue the loads of one step: K rows, then V^T columns.
 template <int KV, int D, int BS, bool NT>
 __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
                                            const typename KvTraits<KV>::T* vp,
                                            const int (&pbs)[32 / BS], int64_t blk_stride,
-                                           __amdgpu_buffer_rsrc_t qrsrc, uint32_t qoff,
-                                           bool qlane, uint32_t qoob,
-                                           const LaneMap<KV, D, BS>& L, int r) {
+                                           const LaneMap<KV, D, BS>& L) {
   const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
   const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
   const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
@@ -456,9 +464,6 @@ __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename Kv
     if constexpr (KV == KV_FP8) R.v[j] = ld8<NT>(col);
     else R.v[j] = ld16<NT>(col);
   }
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-    R.q[i] = ld16_q(qrsrc, qlane ? qoff + 2u * uint32_t(qk_dim0<KV>(i, r)) : qoob);
 }
 
 // A position in the step stream: pair (sequence s, KV head kvh), the pair's
@@ -592,6 +597,11 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
 // load cursor runs NS-1 steps ahead of the compute cursor; every iteration
 // issues exactly one step of loads (past the end of the range it repeats the
 // last step), so the count of loads in flight is the same on every path.
+// The query of a pair is loaded once: when the load cursor enters a pair, its
+// query goes into the `qn` registers, and the compute cursor takes them over
+// when it gets there.  Only when the load cursor enters two pairs while the
+// compute cursor is still short of the first (contexts of at most 32 (NS-2)
+// tokens) does the compute cursor load its pair's query itself.
 // Context lengths and block tables come in as separate restrict arguments:
 // the kernel's stores cannot alias them, so their uniform loads stay scalar
 // and never wait on the vector-load counter.
@@ -635,17 +645,30 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   StepRegs<KV, D> buf[NS];
+  // byte offset of a pair's query rows in q
+  auto q_off = [&](const Cursor& x) {
+    return uint32_t((x.s * a.num_q_heads + x.kvh * g + c) * D * 2);
+  };
+  uint4 qc[D / 32], qn[D / 32];     // queries of the compute cursor's pair and of the next
+  load_query<KV, D>(qc, qrsrc, q_off(cu), qlane, qbytes, r);
+  bool qn_ready = false;            // qn holds the query of the pair at stream step qn_P
+  int qn_P = -1;
 
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
   do {                                                                                         \
     issue_step<KV, D, BS, NT>(R, k_pool + int64_t(la.kvh) * head_stride,                       \
-                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride,      \
-                              qrsrc, uint32_t((la.s * a.num_q_heads + la.kvh * g + c) * D * 2), \
-                              qlane, qbytes, L, r);                                            \
+                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride, L);  \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
-      if (++la.x == la.n) next_pair(la, lens, hkv, max_ctx);                                   \
+      if (++la.x == la.n) {                                                                    \
+        next_pair(la, lens, hkv, max_ctx);                                                     \
+        if (!qn_ready) {                                                                       \
+          load_query<KV, D>(qn, qrsrc, q_off(la), qlane, qbytes, r);                          \
+          qn_ready = true;                                                                     \
+          qn_P = la.P;                                                                         \
+        }                                                                                      \
+      }                                                                                        \
       step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,       \
                       a.num_blocks);                                                           \
     }                                                                                          \
@@ -653,25 +676,39 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) PKV_ISSUE(buf[i]);
-  while (true) {
+  // Rounds of NS steps, the loop's only exit at the bottom of a round: an exit
+  // from inside the unrolled round would give the loop header a second
+  // incoming path on which the round's fresh loads are pending, and the
+  // compiler would then wait for them before reusing any of their registers.
+  // Steps of the last round past the range are skipped (their loads still
+  // issue, repeating the last step).
+  do {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       PKV_ISSUE(buf[(st + NS - 1) % NS]);
-      compute_step<KV, D>(buf[st], acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
-      --rem;
-      if (++cu.x == cu.n || rem == 0) {
-        write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
-        if (rem == 0) goto done;
-        next_pair(cu, lens, hkv, max_ctx);
+      if (rem > 0) {
+        compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
+        --rem;
+        if (++cu.x == cu.n || rem == 0) {
+          write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
+          if (rem > 0) {
+            next_pair(cu, lens, hkv, max_ctx);
+            if (qn_ready && qn_P == cu.P) {
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        m = -INFINITY;
+              for (int i = 0; i < D / 32; ++i) qc[i] = qn[i];
+              qn_ready = false;
+            } else {
+              load_query<KV, D>(qc, qrsrc, q_off(cu), qlane, qbytes, r);
+            }
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            m = -INFINITY;
+          }
+        }
       }
     }
-  }
-done:
-  return;
+  } while (rem > 0);
 #undef PKV_ISSUE
 }
 
