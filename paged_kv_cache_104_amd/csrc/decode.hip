@@ -716,74 +716,117 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 
 // out = sum_k w_k * o_k / sum_k w_k with w_k = l_k * 2^(m_k - max_k m_k): the
 // same rescaling the running softmax applies between tiles.  One workgroup per
-// (sequence, q head); its threads split the pieces into kMergeThreads / D
-// groups that accumulate independently.  The pieces are the vector kernel's
-// partitions or the MFMA kernel's segments, whichever wrote the workspace last
-// (its header says which).  Empty contexts get zeros here.
+// (sequence, KV head) pair merges the pieces of all the pair's query heads;
+// the pieces are the vector kernel's partitions or the MFMA kernel's segments,
+// whichever wrote the workspace last (its header says which).  Empty contexts
+// get zeros here.
+//
+// A thread owns 4 consecutive output elements (a float4 of one head's row) of
+// up to kMergeMaxChunks / kMergeThreads such chunks; when the pair has fewer
+// chunks than threads, the spare threads split the pieces into groups.  Each
+// thread runs the merge as one online pass over its pieces, loading a
+// piece's (max, sum) and its partial row together, so a workgroup waits for
+// memory twice: for the context length and piece record, then for the pieces.
+// The groups' partial results are combined through LDS.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
 template <typename QT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  constexpr int PG = kMergeThreads / D;       // piece groups
-  __shared__ float red[kMergeThreads];
-  __shared__ float part_o[PG][D];
-  __shared__ float part_l[PG];
-  const int row = blockIdx.x;                 // s * Hq + h
-  const int s = row / a.num_q_heads, h = row - s * a.num_q_heads;
-  const int g = a.group, kvh = h / g, hg = h - kvh * g;
-  const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
-  QT* out = static_cast<QT*>(a.out) + int64_t(row) * D;
+  __shared__ float4 part_o[kMergeThreads];
+  __shared__ float part_m[kMergeThreads], part_l[kMergeThreads];
+  const int pair = blockIdx.x;                       // s * Hkv + kvh
+  const int s = pair / a.num_kv_heads, kvh = pair - s * a.num_kv_heads;
+  const int g = a.group;
+  const int nchunks = g * D / 4;                     // float4 chunks of the pair's g rows
   const int tid = threadIdx.x;
+  const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
+  const int proto = a.hdr[0];
+  const int2 rec = a.recs[pair];
+  QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * D;
   if (ctx == 0) {
-    if (tid < D) store_out(out + tid, 0.f);
+    for (int e = tid; e < g * D; e += kMergeThreads) store_out(out + e, 0.f);
     return;
   }
-  // piece k is row first + k * stride (+ fix for k > 0)
+  // piece k of head hg is row first(hg) + k * stride (+ fix for k > 0)
   int count;
-  int64_t first, stride, fix = 0;
-  if (a.hdr[0] == kProtoSegments) {
+  int64_t first0, head_step, stride, fix = 0;
+  if (proto == kProtoSegments) {
     // segments of workers w0 .. w0+count-1: slot 1 of the first, slot 0 after
-    const int2 rec = a.recs[int64_t(s) * a.num_kv_heads + kvh];
     count = rec.y;
-    first = int64_t(2 * rec.x + 1) * g + hg;
+    first0 = int64_t(2 * rec.x + 1) * g;
+    head_step = 1;
     stride = 2 * int64_t(g);
     fix = -int64_t(g);
   } else {
     count = num_parts(ctx, a.part_tokens);
-    first = int64_t(row) * a.max_parts;
+    first0 = (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * a.max_parts;
+    head_step = a.max_parts;
     stride = 1;
   }
-  if (count <= 1) return;                     // written directly by the decode kernel
-  float mx = -INFINITY;
-  for (int k = tid; k < count; k += kMergeThreads)
-    mx = fmaxf(mx, a.ws_ml[(first + k * stride + (k ? fix : 0)) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const int d = tid % D, pg = tid / D;
-  float L = 0.f, o = 0.f;
+  if (count <= 1) return;                            // written directly by the decode kernel
+  const int groups = nchunks >= kMergeThreads ? 1 : kMergeThreads / nchunks;
+  const int pg = tid / min(nchunks, kMergeThreads);  // piece group of this thread
+  const int c0 = tid - pg * min(nchunks, kMergeThreads);
+  const float4* acc4 = reinterpret_cast<const float4*>(a.ws_acc);
+  for (int ch = c0; ch < nchunks && pg < groups; ch += kMergeThreads) {
+    const int hg = (4 * ch) / D, d4 = ch - hg * (D / 4);
+    const int64_t first = first0 + hg * head_step;
+    float M = -INFINITY, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-  for (int k = pg; k < count; k += PG) {
-    const int64_t pc = first + k * stride + (k ? fix : 0);
-    const float wk = a.ws_ml[pc * 2 + 1] * exp2f(a.ws_ml[pc * 2] - M);
-    L += wk;
-    o = fmaf(wk, a.ws_acc[pc * D + d], o);
-  }
-  part_o[pg][d] = o;
-  if (d == 0) part_l[pg] = L;
-  __syncthreads();
-  if (pg == 0) {
-    float ot = 0.f, lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < PG; ++k) {
-      ot += part_o[k][d];
-      lt += part_l[k];
+    for (int k = pg; k < count; k += groups) {
+      const int64_t pc = first + k * stride + (k ? fix : 0);
+      const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + pc * 2);
+      const float4 o = acc4[pc * (D / 4) + d4];
+      const float Mn = fmaxf(M, ml.x);
+      const float sc = exp2f(M - Mn);
+      const float wk = ml.y * exp2f(ml.x - Mn);
+      L = fmaf(L, sc, wk);
+      O.x = fmaf(O.x, sc, wk * o.x);
+      O.y = fmaf(O.y, sc, wk * o.y);
+      O.z = fmaf(O.z, sc, wk * o.z);
+      O.w = fmaf(O.w, sc, wk * o.w);
+      M = Mn;
     }
-    store_out(out + d, ot / lt);
+    if (groups > 1) {
+      part_o[tid] = O;
+      part_m[tid] = M;
+      part_l[tid] = L;
+    } else {
+      const float inv = 1.f / L;
+      QT* o = out + int64_t(hg) * D + 4 * d4;
+      store_out(o + 0, O.x * inv);
+      store_out(o + 1, O.y * inv);
+      store_out(o + 2, O.z * inv);
+      store_out(o + 3, O.w * inv);
+    }
+  }
+  if (groups == 1) return;
+  __syncthreads();
+  if (pg == 0 && c0 < nchunks) {
+    // combine the groups of chunk c0 (group k's partial sits at thread k * nchunks + c0)
+    float M = -INFINITY;
+    for (int k = 0; k < groups && k < count; ++k) M = fmaxf(M, part_m[k * nchunks + c0]);
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < groups && k < count; ++k) {
+      const int t = k * nchunks + c0;
+      const float sc = exp2f(part_m[t] - M);
+      const float4 o = part_o[t];
+      L = fmaf(part_l[t], sc, L);
+      O.x = fmaf(o.x, sc, O.x);
+      O.y = fmaf(o.y, sc, O.y);
+      O.z = fmaf(o.z, sc, O.z);
+      O.w = fmaf(o.w, sc, O.w);
+    }
+    const float inv = 1.f / L;
+    const int hg = (4 * c0) / D, d4 = c0 - hg * (D / 4);
+    QT* o = out + int64_t(hg) * D + 4 * d4;
+    store_out(o + 0, O.x * inv);
+    store_out(o + 1, O.y * inv);
+    store_out(o + 2, O.z * inv);
+    store_out(o + 3, O.w * inv);
   }
 }
 
@@ -1012,7 +1055,7 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
 }
 
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
-  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_q_heads));
+  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
   const dim3 block(kMergeThreads);
   if (head_dim == 64)
     return q_dtype == PKV_F32
