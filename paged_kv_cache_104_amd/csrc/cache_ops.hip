@@ -19,9 +19,16 @@
 namespace pkv {
 
 // One token of k / v ([tokens][heads][D]) into slot `slot` of the pools, by one
-// workgroup: each thread moves 8 consecutive dimensions of one head -- 16 B
-// (bf16) or 32 B (f32) in, a contiguous row segment of the key pool out, and 8
-// scattered elements of the dimension-major value block.
+// workgroup.  Keys: each thread moves 8 consecutive dimensions of one head, a
+// contiguous row segment of the key tile.  Values: the token is one column of
+// each dimension-major value tile, so each thread writes one element, with
+// consecutive threads on consecutive dimensions: the lanes that write into one
+// line do it in one instruction, which the memory pipeline merges into one
+// write.  The value elements go out as non-temporal (streaming) stores.  A
+// token's values touch every line of its tile with a few bytes each; written
+// through the caches, such partial lines slowed the next decode's reads of
+// those tiles (every context's last block is read right after its new token
+// is written) by up to 10% on a 40-head layer.
 template <int KV, typename In>
 __device__ __forceinline__ void write_token(
     const In* __restrict__ k, const In* __restrict__ v, int64_t tok, int64_t slot,
@@ -30,63 +37,60 @@ __device__ __forceinline__ void write_token(
   typedef typename KvTraits<KV>::T T;
   const int64_t blk = slot / block_size;
   const int pos = int(slot - blk * block_size);
-  const int chunks = num_kv_heads * head_dim / 8;
+  const int n = num_kv_heads * head_dim;
   const int64_t head_stride = int64_t(block_size) * head_dim;
-  for (int ch = threadIdx.x; ch < chunks; ch += blockDim.x) {
+  const int64_t tile0 = blk * num_kv_heads * head_stride;
+  // keys: 8 consecutive dimensions per thread, a contiguous row segment of the pool
+  for (int ch = threadIdx.x; ch < n / 8; ch += blockDim.x) {
     const int h = (ch * 8) / head_dim;
     const int d0 = ch * 8 - h * head_dim;
-    const In* ks = k + tok * num_kv_heads * head_dim + ch * 8;
-    const In* vs = v + tok * num_kv_heads * head_dim + ch * 8;
-    float kf[8], vf[8];
-    if constexpr (sizeof(In) == 2) {
-      const uint4 ku = *reinterpret_cast<const uint4*>(ks);
-      const uint4 vu = *reinterpret_cast<const uint4*>(vs);
-      const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w}, vw[4] = {vu.x, vu.y, vu.z, vu.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kf[2 * i] = bf16_to_f32(kw[i] & 0xffffu);
-        kf[2 * i + 1] = bf16_to_f32(kw[i] >> 16);
-        vf[2 * i] = bf16_to_f32(vw[i] & 0xffffu);
-        vf[2 * i + 1] = bf16_to_f32(vw[i] >> 16);
-      }
+    const In* ks = k + tok * n + ch * 8;
+    T* kd = k_pool + tile0 + h * head_stride + int64_t(pos) * head_dim + d0;
+    if constexpr (KV == KV_BF16) {
+      *reinterpret_cast<uint4*>(kd) = *reinterpret_cast<const uint4*>(ks);
     } else {
-      const float4 k0 = reinterpret_cast<const float4*>(ks)[0];
-      const float4 k1 = reinterpret_cast<const float4*>(ks)[1];
-      const float4 v0 = reinterpret_cast<const float4*>(vs)[0];
-      const float4 v1 = reinterpret_cast<const float4*>(vs)[1];
-      kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
-      kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
-      vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w;
-      vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+      float kf[8];
+      if constexpr (sizeof(In) == 2) {
+        const uint4 ku = *reinterpret_cast<const uint4*>(ks);
+        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kf[2 * i] = bf16_to_f32(kw[i] & 0xffffu);
+          kf[2 * i + 1] = bf16_to_f32(kw[i] >> 16);
+        }
+      } else {
+        const float4 k0 = reinterpret_cast<const float4*>(ks)[0];
+        const float4 k1 = reinterpret_cast<const float4*>(ks)[1];
+        kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
+        kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
+      }
+      if constexpr (KV == KV_FP8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo |= e4m3_encode(__fdiv_rn(kf[i], k_scale)) << (8 * i);
+          hi |= e4m3_encode(__fdiv_rn(kf[i + 4], k_scale)) << (8 * i);
+        }
+        *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
+      } else {
+        reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
+        reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
+      }
     }
-    T* kd = k_pool + (blk * num_kv_heads + h) * head_stride + int64_t(pos) * head_dim + d0;
-    T* vd = v_pool + (blk * num_kv_heads + h) * head_stride + int64_t(d0) * block_size + pos;
-    if constexpr (KV == KV_FP8) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_encode(__fdiv_rn(kf[i], k_scale)) << (8 * i);
-        hi |= e4m3_encode(__fdiv_rn(kf[i + 4], k_scale)) << (8 * i);
-      }
-      *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vd[i * block_size] = uint8_t(e4m3_encode(__fdiv_rn(vf[i], v_scale)));
-    } else if constexpr (KV == KV_BF16) {
-      // bf16 input into a bf16 pool: the bits are copied unchanged
-      const uint4 ku = *reinterpret_cast<const uint4*>(ks);
-      const uint4 vu = *reinterpret_cast<const uint4*>(vs);
-      *reinterpret_cast<uint4*>(kd) = ku;
-      const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vd[(2 * i) * block_size] = uint16_t(vw[i] & 0xffffu);
-        vd[(2 * i + 1) * block_size] = uint16_t(vw[i] >> 16);
-      }
+  }
+  // values: one element per thread, consecutive threads on consecutive dimensions, so
+  // the lanes that write one line of the dimension-major tile do it in one instruction
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int h = e / head_dim, d = e - h * head_dim;
+    T* vd = v_pool + tile0 + h * head_stride + int64_t(d) * block_size + pos;
+    const In x = v[tok * n + e];
+    if constexpr (KV == KV_BF16) {
+      __builtin_nontemporal_store(x, vd);
     } else {
-      reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
-      reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vd[i * block_size] = vf[i];
+      float f;
+      if constexpr (sizeof(In) == 2) f = bf16_to_f32(x); else f = x;
+      if constexpr (KV == KV_FP8) __builtin_nontemporal_store(uint8_t(e4m3_encode(__fdiv_rn(f, v_scale))), vd);
+      else __builtin_nontemporal_store(f, vd);
     }
   }
 }

@@ -225,6 +225,7 @@ struct StepRegs {
   uint4 ka[NK];   // K rows, tile a (MFMA A operand of Q.K^T)
   uint4 kb[NK];   // K rows, tile b
   typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];  // V^T, 8 tokens x 1 dim
+  uint4 q[D / 32];  // Q^T of the pair's head group, loaded with a pair's first step only
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -407,16 +408,18 @@ struct MfmaTuning {
 };
 
 // Physical blocks of the step at tokens tt .. tt+31 of a context of t1 tokens
-// whose table row is `table`; blocks past the context (masked tokens) and ids
+// whose table row is `table`.  The part of the step past the context (masked
+// tokens) reads the context's last block again: the same lines the step
+// already reads.  (Reading one fixed block there instead made every worker's
+// last step of every context hit the same few DRAM pages at once.)  Ids
 // outside the pool read block 0.
 template <int BS>
 __device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* __restrict__ table,
                                             int tt, int t1, int num_blocks) {
-  const int nlb = (t1 + BS - 1) / BS;
+  const int last = (t1 + BS - 1) / BS - 1;
 #pragma unroll
   for (int b = 0; b < 32 / BS; ++b) {
-    const int lb = tt / BS + b;
-    const int pb = lb < nlb ? table[lb] : 0;
+    const int pb = table[min(tt / BS + b, last)];
     pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
   }
 }
@@ -442,12 +445,16 @@ __device__ __forceinline__ void load_query(uint4 (&qv)[D / 32], __amdgpu_buffer_
     qv[i] = ld16_q(qrsrc, qlane ? qoff + 2u * uint32_t(qk_dim0<KV>(i, r)) : qoob);
 }
 
-// Issue the loads of one step: K rows, then V^T columns.
+// Issue the loads of one step: the pair's query when the step is the first the
+// worker computes of that pair, then K rows, then V^T columns.
 template <int KV, int D, int BS, bool NT>
 __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
                                            const typename KvTraits<KV>::T* vp,
                                            const int (&pbs)[32 / BS], int64_t blk_stride,
-                                           const LaneMap<KV, D, BS>& L) {
+                                           const LaneMap<KV, D, BS>& L, bool with_q,
+                                           __amdgpu_buffer_rsrc_t qrsrc, uint32_t qoff,
+                                           bool qlane, uint32_t qoob, int r) {
+  if (with_q) load_query<KV, D>(R.q, qrsrc, qoff, qlane, qoob, r);
   const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
   const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
   const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
@@ -597,11 +604,13 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
 // load cursor runs NS-1 steps ahead of the compute cursor; every iteration
 // issues exactly one step of loads (past the end of the range it repeats the
 // last step), so the count of loads in flight is the same on every path.
-// The query of a pair is loaded once: when the load cursor enters a pair, its
-// query goes into the `qn` registers, and the compute cursor takes them over
-// when it gets there.  Only when the load cursor enters two pairs while the
-// compute cursor is still short of the first (contexts of at most 32 (NS-2)
-// tokens) does the compute cursor load its pair's query itself.
+// The query of a pair is loaded once, with the first step of the pair that the
+// worker computes, into that step's ring slot (ahead of its K and V, so the
+// wait for the step's data covers it); the compute cursor copies it from the
+// slot when it reaches that step and keeps it for the pair's other steps.
+// Loading it into registers of its own instead would leave the compiler
+// unable to tell, at the copy, that the load is older than the step's data,
+// and it would drain the whole load pipeline at every change of pair.
 // Context lengths and block tables come in as separate restrict arguments:
 // the kernel's stores cannot alias them, so their uniform loads stay scalar
 // and never wait on the vector-load counter.
@@ -645,30 +654,21 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   StepRegs<KV, D> buf[NS];
-  // byte offset of a pair's query rows in q
-  auto q_off = [&](const Cursor& x) {
-    return uint32_t((x.s * a.num_q_heads + x.kvh * g + c) * D * 2);
-  };
-  uint4 qc[D / 32], qn[D / 32];     // queries of the compute cursor's pair and of the next
-  load_query<KV, D>(qc, qrsrc, q_off(cu), qlane, qbytes, r);
-  bool qn_ready = false;            // qn holds the query of the pair at stream step qn_P
-  int qn_P = -1;
+  uint4 qc[D / 32];                 // query of the compute cursor's pair
+  bool la_first = true, cu_first = true;   // the next step is the worker's first
 
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
   do {                                                                                         \
     issue_step<KV, D, BS, NT>(R, k_pool + int64_t(la.kvh) * head_stride,                       \
-                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride, L);  \
+                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride, L,   \
+                              la_first || la.x == 0, qrsrc,                                    \
+                              uint32_t((la.s * a.num_q_heads + la.kvh * g + c) * D * 2), qlane, \
+                              qbytes, r);                                                      \
+    la_first = false;                                                                          \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
-      if (++la.x == la.n) {                                                                    \
-        next_pair(la, lens, hkv, max_ctx);                                                     \
-        if (!qn_ready) {                                                                       \
-          load_query<KV, D>(qn, qrsrc, q_off(la), qlane, qbytes, r);                          \
-          qn_ready = true;                                                                     \
-          qn_P = la.P;                                                                         \
-        }                                                                                      \
-      }                                                                                        \
+      if (++la.x == la.n) next_pair(la, lens, hkv, max_ctx);                                   \
       step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,       \
                       a.num_blocks);                                                           \
     }                                                                                          \
@@ -687,19 +687,17 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
     for (int st = 0; st < NS; ++st) {
       PKV_ISSUE(buf[(st + NS - 1) % NS]);
       if (rem > 0) {
+        if (cu_first || cu.x == 0) {
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i) qc[i] = buf[st].q[i];
+          cu_first = false;
+        }
         compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
         --rem;
         if (++cu.x == cu.n || rem == 0) {
           write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
           if (rem > 0) {
             next_pair(cu, lens, hkv, max_ctx);
-            if (qn_ready && qn_P == cu.P) {
-#pragma unroll
-              for (int i = 0; i < D / 32; ++i) qc[i] = qn[i];
-              qn_ready = false;
-            } else {
-              load_query<KV, D>(qc, qrsrc, q_off(cu), qlane, qbytes, r);
-            }
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
