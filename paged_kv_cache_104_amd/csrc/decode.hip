@@ -276,12 +276,25 @@ struct LaneMap {
   }
 };
 
+// Block `which` of the step's 32 / BS blocks (uniform values, a lane-dependent
+// choice).  Each block id goes through readfirstlane (free: it is uniform)
+// before the selects, so the compiler cannot fold the choice into an indexed
+// load, which would put the array in scratch memory.
 template <int BS>
 __device__ __forceinline__ int pick_block(const int (&pbs)[32 / BS], int which) {
-  int pb = pbs[0];
+  int v[32 / BS];
 #pragma unroll
-  for (int b = 1; b < 32 / BS; ++b) pb = which == b ? pbs[b] : pb;
-  return pb;
+  for (int b = 0; b < 32 / BS; ++b) v[b] = __builtin_amdgcn_readfirstlane(pbs[b]);
+  if constexpr (32 / BS == 1) {
+    return v[0];
+  } else if constexpr (32 / BS == 2) {
+    return (which & 1) ? v[1] : v[0];
+  } else {
+    static_assert(32 / BS == 4, "block sizes 8, 16, 32");
+    const int lo = (which & 1) ? v[1] : v[0];
+    const int hi = (which & 1) ? v[3] : v[2];
+    return (which & 2) ? hi : lo;
+  }
 }
 
 // A KV block that no other sequence shares is read once per decode: streaming
@@ -558,36 +571,105 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int32_t* _
   return false;
 }
 
+// A worker's outputs, staged in LDS while its loop runs and written to memory
+// after it: a store in the loop waits for room behind the loads that keep the
+// memory pipeline full, which cost about 3 us at every change of pair.  The
+// staged items are the outputs of pairs that lie inside the worker's range
+// (bf16 rows), the piece records of the pairs it starts, and the partial
+// segment of the pair that began before its range.  A full buffer is written
+// out where it fills.
+template <int D>
+struct OutStage {
+  static constexpr int kOutBytes = 8192;
+  static constexpr int kMaxOut = kOutBytes / (D * 2);   // entries of a one-head group
+  static constexpr int kMaxRecs = 64;
+  uint2 out[kOutBytes / 8];
+  int out_row[kMaxOut];            // first q row (s * Hq + kvh * g) of each entry
+  int rec_pair[kMaxRecs];
+  int2 rec[kMaxRecs];
+  float seg[kMaxGroup * D];        // normalised rows of the slot-0 segment
+  float seg_ml[kMaxGroup * 2];
+};
+
+template <int D>
+__device__ __forceinline__ void flush_outputs(const DecodeArgs& a, OutStage<D>& st, int& n_out,
+                                              int lane) {
+  if (n_out == 0) return;
+  __syncthreads();
+  const int cpe = a.group * D / 4;               // 8-byte chunks of one entry
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int i = lane; i < n_out * cpe; i += 64) {
+    const int e = i / cpe, k = i - e * cpe;
+    *reinterpret_cast<uint2*>(out + int64_t(st.out_row[e]) * D + 4 * k) = st.out[e * cpe + k];
+  }
+  __syncthreads();
+  n_out = 0;
+}
+
+template <int D>
+__device__ __forceinline__ void flush_recs(const DecodeArgs& a, OutStage<D>& st, int& n_rec,
+                                           int lane) {
+  if (n_rec == 0) return;
+  __syncthreads();
+  for (int i = lane; i < n_rec; i += 64) a.recs[st.rec_pair[i]] = st.rec[i];
+  __syncthreads();
+  n_rec = 0;
+}
+
 // End of a worker's share of a pair.  A pair that lies inside the worker's
-// range [lo, lo + q) writes its output; otherwise the share is a partial
-// segment, stored in the worker's slot 0 (the pair began before the range)
-// or slot 1 (it goes on past the range).  The worker that holds a pair's
-// first step also records {first worker, workers} of the pair for the merge.
+// range [lo, lo + q) has its output staged; otherwise the share is a partial
+// segment, for the worker's slot 0 (the pair began before the range, staged)
+// or slot 1 (it goes on past the range: the end of the range, stored now).
+// The worker that holds a pair's first step also records {first worker,
+// workers} of the pair for the merge.
 template <int D>
 __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
                                               const floatx4_t (&acc)[D / 16],
-                                              const floatx4_t& lsum, float m, int r, int c) {
+                                              const floatx4_t& lsum, float m, int r, int c,
+                                              int lane, OutStage<D>& st, int& n_out, int& n_rec,
+                                              bool& seg0) {
   const int g = a.group;
   const int lo = w * q;
   const bool head = cu.P >= lo;                  // the pair starts in this range
   const bool whole = head && cu.P + cu.n <= lo + q;
-  const int64_t pair = int64_t(cu.s) * a.num_kv_heads + cu.kvh;
-  if (head && r == 0 && c == 0) a.recs[pair] = make_int2(w, (cu.P + cu.n - 1) / q - w + 1);
-  if (c >= g) return;
+  if (head) {
+    if (n_rec == OutStage<D>::kMaxRecs) flush_recs<D>(a, st, n_rec, lane);
+    if (lane == 0) {
+      st.rec_pair[n_rec] = cu.s * a.num_kv_heads + cu.kvh;
+      st.rec[n_rec] = make_int2(w, (cu.P + cu.n - 1) / q - w + 1);
+    }
+    ++n_rec;
+  }
   const float l = lsum[0];
   const float inv = a.v_scale / l;
   if (whole) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) +
-                    (int64_t(cu.s) * a.num_q_heads + cu.kvh * g + c) * D;
+    if ((n_out + 1) * g > OutStage<D>::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
+    if (lane == 0) st.out_row[n_out] = cu.s * a.num_q_heads + cu.kvh * g;
+    if (c < g) {
+      uint2* o = st.out + (n_out * g + c) * (D / 4);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      uint2 v;
-      v.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
-      v.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
-      *reinterpret_cast<uint2*>(out + 16 * j + 4 * r) = v;
+      for (int j = 0; j < D / 16; ++j) {
+        uint2 v;
+        v.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+        v.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
+        o[4 * j + r] = v;
+      }
     }
-  } else {
-    const int64_t row = int64_t(2 * w + (head ? 1 : 0)) * g + c;
+    ++n_out;
+  } else if (!head) {
+    if (c < g) {
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j)
+        *reinterpret_cast<float4*>(st.seg + c * D + 16 * j + 4 * r) =
+            make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+      if (r == 0) {
+        st.seg_ml[2 * c] = m;
+        st.seg_ml[2 * c + 1] = l;
+      }
+    }
+    seg0 = true;
+  } else if (c < g) {
+    const int64_t row = int64_t(2 * w + 1) * g + c;
     float* wacc = a.ws_acc + row * D;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
@@ -597,6 +679,23 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
       a.ws_ml[row * 2] = m;
       a.ws_ml[row * 2 + 1] = l;
     }
+  }
+}
+
+// The staged outputs, records and slot-0 segment, after the loop.
+template <int D>
+__device__ __forceinline__ void flush_stage(const DecodeArgs& a, OutStage<D>& st, int w, int n_out,
+                                            int n_rec, bool seg0, int lane) {
+  flush_outputs<D>(a, st, n_out, lane);
+  flush_recs<D>(a, st, n_rec, lane);
+  if (seg0) {
+    __syncthreads();
+    const int g = a.group;
+    float4* wacc = reinterpret_cast<float4*>(a.ws_acc + int64_t(2 * w) * g * D);
+    const float4* src = reinterpret_cast<const float4*>(st.seg);
+    for (int i = lane; i < g * D / 4; i += 64) wacc[i] = src[i];
+    float* wml = a.ws_ml + int64_t(2 * w) * g * 2;
+    for (int i = lane; i < 2 * g; i += 64) wml[i] = st.seg_ml[i];
   }
 }
 
@@ -655,6 +754,9 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   float m = -INFINITY;
   StepRegs<KV, D> buf[NS];
   uint4 qc[D / 32];                 // query of the compute cursor's pair
+  __shared__ OutStage<D> stage;
+  int n_out = 0, n_rec = 0;         // staged outputs and records
+  bool seg0 = false;                // the slot-0 segment is staged
   bool la_first = true, cu_first = true;   // the next step is the worker's first
 
   // issue the load cursor's step into R, then move the cursor on
@@ -695,7 +797,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
         compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
         --rem;
         if (++cu.x == cu.n || rem == 0) {
-          write_segment<D>(a, cu, w, q, acc, lsum, m, r, c);
+          write_segment<D>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec, seg0);
           if (rem > 0) {
             next_pair(cu, lens, hkv, max_ctx);
 #pragma unroll
@@ -707,6 +809,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
       }
     }
   } while (rem > 0);
+  flush_stage<D>(a, stage, w, n_out, n_rec, seg0, lane);
 #undef PKV_ISSUE
 }
 
