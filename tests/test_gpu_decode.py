@@ -275,3 +275,28 @@ def test_workspace_contents_never_matter():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), outs[0].view(torch.int16))
     assert np.abs(out_host(out_h) - ref[:half]).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=320, Hq=2, Hkv=2, D=128, kv_dtype="bf16"),
+    dict(seed=321, Hq=8, Hkv=2, D=128, kv_dtype="bf16"),
+    dict(seed=322, Hq=16, Hkv=1, D=128, kv_dtype="bf16"),
+    dict(seed=323, Hq=8, Hkv=2, D=64, kv_dtype="bf16"),
+    dict(seed=324, Hq=8, Hkv=2, D=128, kv_dtype="fp8"),
+], ids=lambda c: f"{c['kv_dtype']}-D{c['D']}-g{c['Hq'] // c['Hkv']}")
+def test_many_pairs_per_worker(case):
+    """Hundreds of short contexts with a partition size that hands them all to one or two
+    matrix-core workers: each worker ends far more pairs than its LDS stage holds (64 piece
+    records, 8 KB of output rows), so the stage is written out inside the loop many times."""
+    wl = workloads.random_small(case["seed"], S=150, Hq=case["Hq"], Hkv=case["Hkv"],
+                                D=case["D"], B=16, max_ctx=40, kv_dtype=case["kv_dtype"],
+                                in_dtype="bf16")
+    print(f"many pairs {case}", flush=True)
+    st = oracle_run(wl)
+    ref = oracle_decode(st)
+    g = GpuState(wl)
+    tol = TOL[wl.kv_dtype]
+    for ps in (8192, 1024, 0):
+        out = out_host(g.decode(ps, IMPLS["mfma"]))
+        err = np.abs(out - ref).max()
+        assert err <= tol, (ps, err)
