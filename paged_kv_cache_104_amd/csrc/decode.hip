@@ -829,11 +829,14 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 // piece's (max, sum) and its partial row together, so a workgroup waits for
 // memory twice: for the context length and piece record, then for the pieces.
 // The groups' partial results are combined through LDS.
+// 256 threads, or 512 for batches of few pairs (long contexts, many pieces each).
 constexpr int kMergeThreads = 256;
+constexpr int kMergeFewPairs = 512;
 constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
-template <typename QT, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+template <typename QT, int D, int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
+  constexpr int kMergeThreads = NT;
   __shared__ float4 part_o[kMergeThreads];
   __shared__ float part_m[kMergeThreads], part_l[kMergeThreads];
   const int pair = blockIdx.x;                       // s * Hkv + kvh
@@ -1155,15 +1158,24 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
              : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, s);
 }
 
-static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
+template <int NT>
+static int launch_merge_nt(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
   const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
-  const dim3 block(kMergeThreads);
+  const dim3 block(NT);
   if (head_dim == 64)
     return q_dtype == PKV_F32
-               ? launch(merge_kernel<float, 64>, mgrid, block, s, a, "merge")
-               : launch(merge_kernel<uint16_t, 64>, mgrid, block, s, a, "merge");
-  return q_dtype == PKV_F32 ? launch(merge_kernel<float, 128>, mgrid, block, s, a, "merge")
-                            : launch(merge_kernel<uint16_t, 128>, mgrid, block, s, a, "merge");
+               ? launch(merge_kernel<float, 64, NT>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 64, NT>, mgrid, block, s, a, "merge");
+  return q_dtype == PKV_F32 ? launch(merge_kernel<float, 128, NT>, mgrid, block, s, a, "merge")
+                            : launch(merge_kernel<uint16_t, 128, NT>, mgrid, block, s, a, "merge");
+}
+
+// A batch of few (sequence, KV head) pairs has long contexts in many pieces each:
+// wider workgroups split those pieces into more groups.
+static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
+  return int64_t(a.num_seqs) * a.num_kv_heads < 256
+             ? launch_merge_nt<kMergeFewPairs>(a, head_dim, q_dtype, s)
+             : launch_merge_nt<kMergeThreads>(a, head_dim, q_dtype, s);
 }
 
 extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const void* k_pool,
