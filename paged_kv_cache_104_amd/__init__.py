@@ -71,6 +71,11 @@ _SIGNATURES = {
                                                _i32, _vp, _sz, _vp, _i32]),
     "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _vp, _sz, _vp, _vp]),
+    "pkv_prefix_rows": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pkv_rows_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32]),
+    "pkv_paged_attn_decode_rows": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
+                                                  _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
+                                                  _i32, _vp, _i32, _vp, _vp, _sz, _vp, _i32]),
     "pkv_swap_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
                                        ctypes.POINTER(CacheDesc), _vp]),
     "pkv_swap_blocks_dma": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
@@ -424,6 +429,55 @@ def paged_attn_merge(out, context_lens, num_kv_heads: int, max_context_len: int,
                                     int(num_kv_heads), D,
                                     int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
                                     _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- shared-prefix decode
+
+def prefix_rows(tables: np.ndarray, lens: np.ndarray, block_size: int, group: int,
+                min_shared_blocks: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows of the shared-prefix decode for a batch (host): ``(rows [R, 4], seq_rows [S, 4])``
+    int32, built by the library from the batch's block tables and context lengths."""
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    S = int(t.shape[0])
+    rows = np.zeros((max(1, 2 * S), 4), dtype=np.int32)
+    seq_rows = np.zeros((max(1, S), 4), dtype=np.int32)
+    n = int(lib.pkv_prefix_rows(t.ctypes.data_as(_pi32), ln.ctypes.data_as(_pi32), S,
+                                int(t.shape[1]) if t.ndim == 2 else 0, int(block_size),
+                                int(group), int(min_shared_blocks),
+                                rows.ctypes.data_as(_pi32), seq_rows.ctypes.data_as(_pi32)))
+    _check(min(n, 0))
+    return rows[:n].copy(), seq_rows[:S].copy()
+
+
+def rows_workspace_bytes(desc: CacheDesc, num_rows: int) -> int:
+    return int(lib.pkv_rows_workspace_bytes(ctypes.byref(desc), int(num_rows)))
+
+
+def paged_attn_decode_rows(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                           desc: CacheDesc, max_context_len: int, partition_size: int,
+                           rows, seq_rows, workspace=None, phases: int = 3, stream=None):
+    """Shared-prefix decode (see include/pagedkv.h): ``rows`` / ``seq_rows`` are device int32
+    tensors [R, 4] / [S, 4] (``prefix_rows`` builds them on the host)."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    if rows.dtype != torch.int32 or seq_rows.dtype != torch.int32:
+        raise ValueError("rows and seq_rows must be int32")
+    if rows.dim() != 2 or rows.shape[1] != 4 or tuple(seq_rows.shape) != (S, 4):
+        raise ValueError("rows must be [R, 4] and seq_rows [S, 4]")
+    if not (rows.is_contiguous() and seq_rows.is_contiguous()):
+        raise ValueError("rows and seq_rows must be contiguous")
+    R = int(rows.shape[0])
+    if workspace is None:
+        workspace = torch.empty(rows_workspace_bytes(desc, R), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = int(workspace.numel() * workspace.element_size())
+    _check(lib.pkv_paged_attn_decode_rows(
+        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+        float(scale), _ptr(out), int(max_context_len), int(partition_size), _ptr(rows), R,
+        _ptr(seq_rows), _ptr(workspace), ws_bytes, _stream(stream), int(phases)))
+    return out
 
 
 # ---------------------------------------------------------------------------- QUEST

@@ -20,7 +20,8 @@ LIB = os.environ.get("PKV_LIB_OUT", os.path.join(HERE, "libpagedkv.so"))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["errors.cpp", "block_manager.cpp", "cache_ops.hip", "decode.hip", "quest.hip"]
+SOURCES = ["errors.cpp", "block_manager.cpp", "prefix_rows.cpp", "cache_ops.hip", "decode.hip",
+           "quest.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-result"]

@@ -65,6 +65,11 @@ struct DecodeArgs {
   int32_t workers;      // MFMA kernel: persistent workers launched
   float qk_scale_log2;  // scale * log2(e) * k_scale
   float v_scale;
+  // shared-prefix (row) decode only
+  const int4* rows;     // [num_rows] {table row, first token, end token (< 0: context length), members}
+  const int4* seq_rows; // [num_seqs] {own row, prefix row (< 0: none), member index, 0}
+  int32_t num_rows;
+  int32_t whole_base;   // first workspace row of the pieces of pairs inside one worker's range
 };
 
 // Partitions of a context of ctx tokens for the vector kernel: max(1, ctx / P),
@@ -486,18 +491,56 @@ __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename Kv
   }
 }
 
-// A position in the step stream: pair (sequence s, KV head kvh), the pair's
-// first step P in the stream, its steps n and context length ctx, and the
-// step x within the pair.  The stream orders pairs by sequence, then KV head.
+// A position in the step stream: pair (row s, KV head kvh), the pair's first
+// step P in the stream, its steps n, the row's tokens ctx, and the step x
+// within the pair.  The stream orders pairs by row, then KV head.  A row is a
+// sequence (plain decode: seq = s, tokens from tb = 0, one member) or, in the
+// shared-prefix decode, a span [tb, tb + ctx) of sequence seq's context whose
+// query columns come from M consecutive sequences seq .. seq + M - 1.
 struct Cursor {
   int s, kvh, x, P, n, ctx;
+  int seq, tb, M;
 };
 
 __device__ __forceinline__ int clamp_ctx(int len, int max_ctx) { return max(0, min(len, max_ctx)); }
 __device__ __forceinline__ int ctx_steps(int ctx) { return (ctx + 31) >> 5; }
 
+// Tokens of row r: sequence, first token and count (clamped to the context
+// and to max_ctx; an out-of-range sequence has none), and the members.
+// The span of row descriptor d given its sequence's context length len.
+__device__ __forceinline__ void row_span_of(const DecodeArgs& a, int4 d, int len, int& seq,
+                                            int& tb, int& ctx, int& M) {
+  seq = d.x;
+  M = max(1, min(d.w, kMaxGroup / a.group));
+  if (seq < 0 || seq >= a.num_seqs) {
+    seq = 0;
+    tb = 0;
+    ctx = 0;
+    return;
+  }
+  M = min(M, a.num_seqs - seq);
+  len = clamp_ctx(len, a.max_ctx);
+  const int te = d.z < 0 ? len : min(d.z, len);
+  tb = max(0, d.y);
+  ctx = max(0, te - tb);
+}
+
+__device__ __forceinline__ int row_seq(const DecodeArgs& a, int4 d) {
+  return (d.x >= 0 && d.x < a.num_seqs) ? d.x : 0;
+}
+
+__device__ __forceinline__ void row_span(const DecodeArgs& a, const int4* __restrict__ rows,
+                                         const int32_t* __restrict__ lens, int r, int& seq,
+                                         int& tb, int& ctx, int& M) {
+  const int4 d = rows[r];
+  row_span_of(a, d, lens[row_seq(a, d)], seq, tb, ctx, M);
+}
+
 // Move to the next pair that has steps; the caller knows there is one.
-__device__ __forceinline__ void next_pair(Cursor& cu, const int32_t* __restrict__ lens, int hkv,
+template <bool ROWS>
+__device__ __forceinline__ void next_pair(Cursor& cu, const DecodeArgs& a,
+                                          const int4* __restrict__ rows,
+                                          const int32_t* __restrict__ lens, int hkv,
                                           int max_ctx) {
   cu.P += cu.n;
   cu.x = 0;
@@ -505,7 +548,12 @@ __device__ __forceinline__ void next_pair(Cursor& cu, const int32_t* __restrict_
   cu.kvh = 0;
   do {
     ++cu.s;
-    cu.ctx = clamp_ctx(lens[cu.s], max_ctx);
+    if constexpr (ROWS) {
+      row_span(a, rows, lens, cu.s, cu.seq, cu.tb, cu.ctx, cu.M);
+    } else {
+      cu.seq = cu.s;
+      cu.ctx = clamp_ctx(lens[cu.s], max_ctx);
+    }
   } while (cu.ctx == 0);
   cu.n = ctx_steps(cu.ctx);
 }
@@ -525,33 +573,63 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
+// Steps of row (or sequence) i, for the scan in find_start.
+template <bool ROWS>
+__device__ __forceinline__ int unit_steps(const DecodeArgs& a, const int4* __restrict__ rows,
+                                          const int32_t* __restrict__ lens, int i) {
+  if constexpr (ROWS) {
+    int seq, tb, ctx, M;
+    row_span(a, rows, lens, i, seq, tb, ctx, M);
+    return ctx_steps(ctx);
+  } else {
+    return ctx_steps(clamp_ctx(lens[i], a.max_ctx));
+  }
+}
+
 // Every worker derives the split itself from the context lengths (the wave's
 // results are made uniform so the cursor lives in scalar registers): the
 // stream's length `total`, the steps per worker `q` (equal for all, at least
 // part_tokens / 32) and the cursor at its own first step w * q.  False when
 // worker w has no steps.
-__device__ __forceinline__ bool find_start(const DecodeArgs& a, const int32_t* __restrict__ lens,
-                                           int w, int lane, int& total, int& q, Cursor& cu) {
-  const int S = a.num_seqs, hkv = a.num_kv_heads;
+template <bool ROWS>
+__device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __restrict__ rows,
+                                           const int32_t* __restrict__ lens, int w, int lane,
+                                           int& total, int& q, Cursor& cu) {
+  const int S = ROWS ? a.num_rows : a.num_seqs, hkv = a.num_kv_heads;
   int sum = 0;
   for (int s0 = 0; s0 < S; s0 += 256) {
+    // every load of the chunk is requested before any is used
     int v[4];
+    if constexpr (ROWS) {
+      int4 d[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + 64 * u + lane;
-      v[u] = s < S ? lens[s] : 0;
+      for (int u = 0; u < 4; ++u) d[u] = rows[min(s0 + 64 * u + lane, S - 1)];  // unconditional
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = lens[row_seq(a, d[u])];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int seq, tb, ctx, M;
+        row_span_of(a, d[u], v[u], seq, tb, ctx, M);
+        v[u] = s0 + 64 * u + lane < S ? ctx_steps(ctx) : 0;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + 64 * u + lane;
+        v[u] = s < S ? ctx_steps(clamp_ctx(lens[s], a.max_ctx)) : 0;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sum += ctx_steps(clamp_ctx(v[u], a.max_ctx));
+    for (int u = 0; u < 4; ++u) sum += v[u];
   }
   total = __builtin_amdgcn_readfirstlane(wave_sum(sum)) * hkv;
   q = max(max(1, a.part_tokens >> 5), (total + a.workers - 1) / a.workers);
   if (int64_t(w) * q >= total) return false;
   const int target = w * q;
-  int base = 0;  // steps of one KV head of the sequences before the chunk
+  int base = 0;  // steps of one KV head of the rows before the chunk
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int s = s0 + lane;
-    const int n = s < S ? ctx_steps(clamp_ctx(lens[s], a.max_ctx)) : 0;
+    const int n = s < S ? unit_steps<ROWS>(a, rows, lens, s) : 0;
     const int incl = wave_inclusive_scan(n, lane);
     const uint64_t hit = __ballot(hkv * (base + incl) > target);
     if (hit) {
@@ -563,7 +641,14 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int32_t* _
       cu.x = target - first - cu.kvh * ns;
       cu.n = ns;
       cu.P = first + cu.kvh * ns;
-      cu.ctx = clamp_ctx(lens[cu.s], a.max_ctx);
+      if constexpr (ROWS) {
+        row_span(a, rows, lens, cu.s, cu.seq, cu.tb, cu.ctx, cu.M);
+      } else {
+        cu.seq = cu.s;
+        cu.tb = 0;
+        cu.M = 1;
+        cu.ctx = clamp_ctx(lens[cu.s], a.max_ctx);
+      }
       return true;
     }
     base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
@@ -616,22 +701,58 @@ __device__ __forceinline__ void flush_recs(const DecodeArgs& a, OutStage<D>& st,
   n_rec = 0;
 }
 
+// Columns of a pair with a query behind them, and the workspace rows per
+// partial-segment slot: the head group (plain decode), or up to 16 columns of
+// M member sequences (shared-prefix decode, whose slots are 16 rows apart).
+template <bool ROWS>
+__device__ __forceinline__ int pair_cols(const DecodeArgs& a, const Cursor& cu) {
+  return ROWS ? cu.M * a.group : a.group;
+}
+template <bool ROWS>
+__device__ __forceinline__ int slot_rows(const DecodeArgs& a) {
+  return ROWS ? kMaxGroup : a.group;
+}
+
+// Normalised output rows of the pair's columns, or its partial segment, at
+// workspace row `row0` (column c at row0 + c).
+template <int D>
+__device__ __forceinline__ void store_piece(const DecodeArgs& a, int64_t row0, int ncols,
+                                            const floatx4_t (&acc)[D / 16], float m, float l,
+                                            float inv, int r, int c) {
+  if (c >= ncols) return;
+  const int64_t row = row0 + c;
+  float* wacc = a.ws_acc + row * D;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+    *reinterpret_cast<float4*>(wacc + 16 * j + 4 * r) =
+        make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+  if (r == 0) {
+    a.ws_ml[row * 2] = m;
+    a.ws_ml[row * 2 + 1] = l;
+  }
+}
+
 // End of a worker's share of a pair.  A pair that lies inside the worker's
 // range [lo, lo + q) has its output staged; otherwise the share is a partial
 // segment, for the worker's slot 0 (the pair began before the range, staged)
 // or slot 1 (it goes on past the range: the end of the range, stored now).
-// The worker that holds a pair's first step also records {first worker,
-// workers} of the pair for the merge.
-template <int D>
+// In the shared-prefix decode, pairs of a shared prefix and of the spans after
+// it are pieces of their sequences' contexts: one that lies inside the range
+// goes to the pair's own workspace rows instead of the output.  The worker
+// that holds a pair's first step also records {first worker, workers} of the
+// pair for the merge.
+template <int D, bool ROWS>
 __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
                                               const floatx4_t (&acc)[D / 16],
                                               const floatx4_t& lsum, float m, int r, int c,
                                               int lane, OutStage<D>& st, int& n_out, int& n_rec,
-                                              bool& seg0) {
+                                              int& seg0_cols) {
   const int g = a.group;
+  const int ncols = pair_cols<ROWS>(a, cu), srows = slot_rows<ROWS>(a);
   const int lo = w * q;
   const bool head = cu.P >= lo;                  // the pair starts in this range
   const bool whole = head && cu.P + cu.n <= lo + q;
+  const bool direct = !ROWS || (cu.tb == 0 && cu.M == 1);
   if (head) {
     if (n_rec == OutStage<D>::kMaxRecs) flush_recs<D>(a, st, n_rec, lane);
     if (lane == 0) {
@@ -642,9 +763,9 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
   }
   const float l = lsum[0];
   const float inv = a.v_scale / l;
-  if (whole) {
+  if (whole && direct) {
     if ((n_out + 1) * g > OutStage<D>::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
-    if (lane == 0) st.out_row[n_out] = cu.s * a.num_q_heads + cu.kvh * g;
+    if (lane == 0) st.out_row[n_out] = cu.seq * a.num_q_heads + cu.kvh * g;
     if (c < g) {
       uint2* o = st.out + (n_out * g + c) * (D / 4);
 #pragma unroll
@@ -656,8 +777,11 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
       }
     }
     ++n_out;
+  } else if (whole) {
+    store_piece<D>(a, a.whole_base + (int64_t(cu.s) * a.num_kv_heads + cu.kvh) * kMaxGroup,
+                   ncols, acc, m, l, inv, r, c);
   } else if (!head) {
-    if (c < g) {
+    if (c < ncols) {
 #pragma unroll
       for (int j = 0; j < D / 16; ++j)
         *reinterpret_cast<float4*>(st.seg + c * D + 16 * j + 4 * r) =
@@ -667,35 +791,26 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
         st.seg_ml[2 * c + 1] = l;
       }
     }
-    seg0 = true;
-  } else if (c < g) {
-    const int64_t row = int64_t(2 * w + 1) * g + c;
-    float* wacc = a.ws_acc + row * D;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-      *reinterpret_cast<float4*>(wacc + 16 * j + 4 * r) =
-          make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-    if (r == 0) {
-      a.ws_ml[row * 2] = m;
-      a.ws_ml[row * 2 + 1] = l;
-    }
+    seg0_cols = ncols;
+  } else {
+    store_piece<D>(a, int64_t(2 * w + 1) * srows, ncols, acc, m, l, inv, r, c);
   }
 }
 
 // The staged outputs, records and slot-0 segment, after the loop.
-template <int D>
+template <int D, bool ROWS>
 __device__ __forceinline__ void flush_stage(const DecodeArgs& a, OutStage<D>& st, int w, int n_out,
-                                            int n_rec, bool seg0, int lane) {
+                                            int n_rec, int seg0_cols, int lane) {
   flush_outputs<D>(a, st, n_out, lane);
   flush_recs<D>(a, st, n_rec, lane);
-  if (seg0) {
+  if (seg0_cols > 0) {
     __syncthreads();
-    const int g = a.group;
-    float4* wacc = reinterpret_cast<float4*>(a.ws_acc + int64_t(2 * w) * g * D);
+    const int64_t row0 = int64_t(2 * w) * slot_rows<ROWS>(a);
+    float4* wacc = reinterpret_cast<float4*>(a.ws_acc + row0 * D);
     const float4* src = reinterpret_cast<const float4*>(st.seg);
-    for (int i = lane; i < g * D / 4; i += 64) wacc[i] = src[i];
-    float* wml = a.ws_ml + int64_t(2 * w) * g * 2;
-    for (int i = lane; i < 2 * g; i += 64) wml[i] = st.seg_ml[i];
+    for (int i = lane; i < seg0_cols * D / 4; i += 64) wacc[i] = src[i];
+    float* wml = a.ws_ml + row0 * 2;
+    for (int i = lane; i < 2 * seg0_cols; i += 64) wml[i] = st.seg_ml[i];
   }
 }
 
@@ -713,9 +828,10 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, OutStage<D>& st
 // Context lengths and block tables come in as separate restrict arguments:
 // the kernel's stores cannot alias them, so their uniform loads stay scalar
 // and never wait on the vector-load counter.
-template <int KV, int D, int BS, bool NT>
+template <int KV, int D, int BS, bool NT, bool ROWS>
 __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
-    DecodeArgs a, const int32_t* __restrict__ lens, const int32_t* __restrict__ tables) {
+    DecodeArgs a, const int32_t* __restrict__ lens, const int32_t* __restrict__ tables,
+    const int4* __restrict__ rows) {
   typedef typename KvTraits<KV>::T T;
   constexpr int NS = MfmaTuning<KV>::stages;
   constexpr int NB = 32 / BS;
@@ -725,7 +841,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   if (w == 0 && lane == 0) a.hdr[0] = kProtoSegments;
   int total, q;
   Cursor cu;                                       // compute cursor
-  if (!find_start(a, lens, w, lane, total, q, cu)) return;
+  if (!find_start<ROWS>(a, rows, lens, w, lane, total, q, cu)) return;
   int rem = min(total - w * q, q);                 // steps left to compute
   const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
   const int64_t head_stride = int64_t(BS) * D;
@@ -735,7 +851,6 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   const LaneMap<KV, D, BS> L(r, c);
   const float sl2 = a.qk_scale_log2;
   const int g = a.group, hkv = a.num_kv_heads, max_ctx = a.max_ctx;
-  const bool qlane = c < g;
   // q is [num_seqs][num_q_heads][D] bf16; its size fits 31 bits (checked on the host)
   const uint32_t qbytes = uint32_t(a.num_seqs) * uint32_t(a.num_q_heads) * uint32_t(D) * 2u;
   const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -744,8 +859,8 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   Cursor la = cu;                                  // load cursor
   int la_left = rem;                               // steps the load cursor still has to load
   int la_pbs[NB];
-  step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,
-                  a.num_blocks);
+  step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks, la.tb + 32 * la.x,
+                  la.tb + la.ctx, a.num_blocks);
 
   floatx4_t acc[D / 16];
 #pragma unroll
@@ -756,23 +871,25 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   uint4 qc[D / 32];                 // query of the compute cursor's pair
   __shared__ OutStage<D> stage;
   int n_out = 0, n_rec = 0;         // staged outputs and records
-  bool seg0 = false;                // the slot-0 segment is staged
+  int seg0_cols = 0;                // columns of the staged slot-0 segment (0: none)
   bool la_first = true, cu_first = true;   // the next step is the worker's first
 
+  // query column c of the load cursor's pair: head c % g of member c / g
+  const int cm = c / g, ch = c - cm * g;
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
   do {                                                                                         \
-    issue_step<KV, D, BS, NT>(R, k_pool + int64_t(la.kvh) * head_stride,                       \
-                              v_pool + int64_t(la.kvh) * head_stride, la_pbs, blk_stride, L,   \
-                              la_first || la.x == 0, qrsrc,                                    \
-                              uint32_t((la.s * a.num_q_heads + la.kvh * g + c) * D * 2), qlane, \
-                              qbytes, r);                                                      \
+    issue_step<KV, D, BS, NT>(                                                                 \
+        R, k_pool + int64_t(la.kvh) * head_stride, v_pool + int64_t(la.kvh) * head_stride,     \
+        la_pbs, blk_stride, L, la_first || la.x == 0, qrsrc,                                   \
+        uint32_t(((la.seq + cm) * a.num_q_heads + la.kvh * g + ch) * D * 2),                   \
+        c < pair_cols<ROWS>(a, la), qbytes, r);                                                \
     la_first = false;                                                                          \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
-      if (++la.x == la.n) next_pair(la, lens, hkv, max_ctx);                                   \
-      step_blocks<BS>(la_pbs, tables + int64_t(la.s) * a.max_blocks, 32 * la.x, la.ctx,       \
-                      a.num_blocks);                                                           \
+      if (++la.x == la.n) next_pair<ROWS>(la, a, rows, lens, hkv, max_ctx);                    \
+      step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks, la.tb + 32 * la.x,      \
+                      la.tb + la.ctx, a.num_blocks);                                           \
     }                                                                                          \
   } while (0)
 
@@ -797,9 +914,10 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
         compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
         --rem;
         if (++cu.x == cu.n || rem == 0) {
-          write_segment<D>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec, seg0);
+          write_segment<D, ROWS>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec,
+                                 seg0_cols);
           if (rem > 0) {
-            next_pair(cu, lens, hkv, max_ctx);
+            next_pair<ROWS>(cu, a, rows, lens, hkv, max_ctx);
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -809,7 +927,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
       }
     }
   } while (rem > 0);
-  flush_stage<D>(a, stage, w, n_out, n_rec, seg0, lane);
+  flush_stage<D, ROWS>(a, stage, w, n_out, n_rec, seg0_cols, lane);
 #undef PKV_ISSUE
 }
 
@@ -834,7 +952,38 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeFewPairs = 512;
 constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
-template <typename QT, int D, int NT>
+// The pieces of one (row, KV head) pair in the shared-prefix decode: a pair
+// inside one worker's range has its own workspace rows; a split pair's pieces
+// are the slots of workers u0 .. u0 + count - 1 (slot 1 of the first, slot 0
+// after), 16 rows a slot.  Column col of piece k is workspace row at(k).
+struct PieceRange {
+  int64_t whole;
+  int u0, count, col;
+  bool direct;       // a plain row (first token 0, one member): written directly when whole
+  __device__ int64_t at(int k) const {
+    if (count == 1) return whole + col;
+    return (k == 0 ? int64_t(2 * u0 + 1) : int64_t(2 * (u0 + k))) * kMaxGroup + col;
+  }
+};
+
+// Row r of the shared-prefix decode as a piece range of KV head kvh at column
+// col; no pieces when the row has no tokens.
+__device__ __forceinline__ PieceRange row_pieces(const DecodeArgs& a, int r, int kvh, int col) {
+  PieceRange p{0, 0, 0, col, false};
+  if (r < 0 || r >= a.num_rows) return p;
+  int seq, tb, ctx, M;
+  row_span(a, a.rows, a.context_lens, r, seq, tb, ctx, M);
+  p.direct = tb == 0 && M == 1;
+  if (ctx == 0) return p;
+  const int64_t pr = int64_t(r) * a.num_kv_heads + kvh;
+  const int2 rec = a.recs[pr];
+  p.whole = a.whole_base + pr * kMaxGroup;
+  p.u0 = rec.x;
+  p.count = rec.y;
+  return p;
+}
+
+template <typename QT, int D, int NT, bool ROWS>
 __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   constexpr int kMergeThreads = NT;
   __shared__ float4 part_o[kMergeThreads];
@@ -845,30 +994,44 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   const int nchunks = g * D / 4;                     // float4 chunks of the pair's g rows
   const int tid = threadIdx.x;
   const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
-  const int proto = a.hdr[0];
-  const int2 rec = a.recs[pair];
   QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * D;
   if (ctx == 0) {
     for (int e = tid; e < g * D; e += kMergeThreads) store_out(out + e, 0.f);
     return;
   }
   // piece k of head hg is row first(hg) + k * stride (+ fix for k > 0)
-  int count;
-  int64_t first0, head_step, stride, fix = 0;
-  if (proto == kProtoSegments) {
-    // segments of workers w0 .. w0+count-1: slot 1 of the first, slot 0 after
-    count = rec.y;
-    first0 = int64_t(2 * rec.x + 1) * g;
-    head_step = 1;
-    stride = 2 * int64_t(g);
-    fix = -int64_t(g);
+  int count = 0;
+  int64_t first0 = 0, head_step = 0, stride = 0, fix = 0;
+  // shared-prefix decode: the sequence's own row, then the members' prefix row
+  PieceRange own{0, 0, 0, 0, false}, pre{0, 0, 0, 0, false};
+  if constexpr (ROWS) {
+    const int4 sr = a.seq_rows[s];
+    own = row_pieces(a, sr.x, kvh, 0);
+    // a member index past the 16 columns is cut (it has no prefix piece)
+    pre = sr.y >= 0 && sr.z >= 0 && (sr.z + 1) * g <= kMaxGroup
+              ? row_pieces(a, sr.y, kvh, sr.z * g)
+              : PieceRange{0, 0, 0, 0, false};
+    // a plain row inside one worker's range was written directly by the decode kernel
+    if (pre.count == 0 && own.direct && own.count <= 1) return;
+    count = own.count + pre.count;
   } else {
-    count = num_parts(ctx, a.part_tokens);
-    first0 = (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * a.max_parts;
-    head_step = a.max_parts;
-    stride = 1;
+    const int proto = a.hdr[0];
+    const int2 rec = a.recs[pair];
+    if (proto == kProtoSegments) {
+      // segments of workers w0 .. w0+count-1: slot 1 of the first, slot 0 after
+      count = rec.y;
+      first0 = int64_t(2 * rec.x + 1) * g;
+      head_step = 1;
+      stride = 2 * int64_t(g);
+      fix = -int64_t(g);
+    } else {
+      count = num_parts(ctx, a.part_tokens);
+      first0 = (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * a.max_parts;
+      head_step = a.max_parts;
+      stride = 1;
+    }
+    if (count <= 1) return;                          // written directly by the decode kernel
   }
-  if (count <= 1) return;                            // written directly by the decode kernel
   const int groups = nchunks >= kMergeThreads ? 1 : kMergeThreads / nchunks;
   const int pg = tid / min(nchunks, kMergeThreads);  // piece group of this thread
   const int c0 = tid - pg * min(nchunks, kMergeThreads);
@@ -880,7 +1043,12 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
     for (int k = pg; k < count; k += groups) {
-      const int64_t pc = first + k * stride + (k ? fix : 0);
+      int64_t pc;
+      if constexpr (ROWS) {
+        pc = k < own.count ? own.at(k) + hg : pre.at(k - own.count) + hg;
+      } else {
+        pc = first + k * stride + (k ? fix : 0);
+      }
       const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + pc * 2);
       const float4 o = acc4[pc * (D / 4) + d4];
       const float Mn = fmaxf(M, ml.x);
@@ -970,6 +1138,21 @@ static WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
   return w;
 }
 
+// Shared-prefix decode workspace: header | records of the (row, KV head) pairs |
+// partial rows: the workers' slots (16 rows each) and then 16 rows per pair for
+// pairs that lie inside one worker's range.
+static WsLayout ws_layout_rows(int32_t num_rows, int32_t num_kv_heads, int32_t head_dim) {
+  WsLayout w;
+  w.parts = 1;
+  w.pairs = int64_t(num_rows) * num_kv_heads;
+  w.recs_off = 256;
+  w.ml_off = w.recs_off + align256(size_t(w.pairs) * sizeof(int2));
+  w.rows = 2 * int64_t(kMaxWorkers) * kMaxGroup + w.pairs * kMaxGroup;
+  w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
+  w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
+  return w;
+}
+
 template <typename K, typename... Extra>
 static int launch(K kernel, dim3 grid, dim3 block, hipStream_t s, const DecodeArgs& a,
                   const char* what, Extra... extra) {
@@ -1017,36 +1200,42 @@ static int dispatch_vector(const DecodeArgs& a, int kv, int qd, hipStream_t s) {
   return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(qd), dtype_name(kv));
 }
 
-template <int KV, int D, int BS, bool NT>
+template <int KV, int D, int BS, bool NT, bool ROWS>
 static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
-  auto kernel = decode_mfma_kernel<KV, D, BS, NT>;
+  auto kernel = decode_mfma_kernel<KV, D, BS, NT, ROWS>;
   DecodeArgs a = a0;
   a.workers = int32_t(std::min<int64_t>(kMaxWorkers, resident_workers(kernel)));
   return launch(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a, "decode",
-                a.context_lens, a.block_tables);
+                a.context_lens, a.block_tables, a.rows);
 }
 
+// The shared-prefix decode reads each shared block once, so it always streams.
 template <int D, int BS>
-static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, hipStream_t s) {
+static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, bool rows, hipStream_t s) {
   if (kv == PKV_BF16)
-    return shared ? launch_mfma<KV_BF16, D, BS, false>(a, s)
-                  : launch_mfma<KV_BF16, D, BS, true>(a, s);
+    return rows     ? launch_mfma<KV_BF16, D, BS, true, true>(a, s)
+           : shared ? launch_mfma<KV_BF16, D, BS, false, false>(a, s)
+                    : launch_mfma<KV_BF16, D, BS, true, false>(a, s);
   if (kv == PKV_FP8_E4M3)
-    return shared ? launch_mfma<KV_FP8, D, BS, false>(a, s)
-                  : launch_mfma<KV_FP8, D, BS, true>(a, s);
+    return rows     ? launch_mfma<KV_FP8, D, BS, true, true>(a, s)
+           : shared ? launch_mfma<KV_FP8, D, BS, false, false>(a, s)
+                    : launch_mfma<KV_FP8, D, BS, true, false>(a, s);
   return fail(PKV_E_UNSUPPORTED, "the MFMA kernel needs a bf16 or fp8 pool");
 }
 
 template <int D>
 static int dispatch_bs(const DecodeArgs& a, int bs, int kv, int qd, bool mfma, bool shared,
-                       hipStream_t s) {
+                       bool rows, hipStream_t s) {
   switch (bs) {
     case 8:
-      return mfma ? dispatch_mfma<D, 8>(a, kv, shared, s) : dispatch_vector<D, 8>(a, kv, qd, s);
+      return mfma ? dispatch_mfma<D, 8>(a, kv, shared, rows, s)
+                  : dispatch_vector<D, 8>(a, kv, qd, s);
     case 16:
-      return mfma ? dispatch_mfma<D, 16>(a, kv, shared, s) : dispatch_vector<D, 16>(a, kv, qd, s);
+      return mfma ? dispatch_mfma<D, 16>(a, kv, shared, rows, s)
+                  : dispatch_vector<D, 16>(a, kv, qd, s);
     case 32:
-      return mfma ? dispatch_mfma<D, 32>(a, kv, shared, s) : dispatch_vector<D, 32>(a, kv, qd, s);
+      return mfma ? dispatch_mfma<D, 32>(a, kv, shared, rows, s)
+                  : dispatch_vector<D, 32>(a, kv, qd, s);
   }
   return fail(PKV_E_UNSUPPORTED, "block_size %d", bs);
 }
@@ -1070,7 +1259,7 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                    int32_t num_q_heads, float scale, void* out, int32_t max_context_len,
                    int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   DecodeArgs* a, WsLayout* lay) {
+                   DecodeArgs* a, WsLayout* lay, int32_t num_rows = -1) {
   int rc = check_desc(c);
   if (rc) return rc;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -1087,7 +1276,8 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   if (int64_t(max_blocks_per_seq) * c->block_size < max_context_len)
     return fail(PKV_E_INVAL, "max_blocks_per_seq %d cannot hold max_context_len %d",
                 max_blocks_per_seq, max_context_len);
-  if (int64_t(num_seqs) * c->num_kv_heads * ((int64_t(max_context_len) + 31) / 32) >= (1 << 30) ||
+  if (int64_t(std::max(num_seqs, num_rows)) * c->num_kv_heads *
+              ((int64_t(max_context_len) + 31) / 32) >= (1 << 30) ||
       int64_t(num_seqs) * num_q_heads * c->head_dim * 4 >= (int64_t(1) << 31))
     return fail(PKV_E_INVAL, "batch too large for one call");
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
@@ -1095,8 +1285,9 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   if ((c->kv_dtype == PKV_F32) != (q_dtype == PKV_F32))
     return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(q_dtype),
                 dtype_name(c->kv_dtype));
-  *lay = ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim, max_context_len,
-                   partition_size);
+  *lay = num_rows >= 0 ? ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim)
+                       : ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim,
+                                   max_context_len, partition_size);
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return fail(PKV_E_INVAL, "NULL pointer");
@@ -1130,6 +1321,10 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   a->workers = 0;
   a->qk_scale_log2 = scale * kLog2e * (c->kv_dtype == PKV_FP8_E4M3 ? c->k_scale : 1.f);
   a->v_scale = c->kv_dtype == PKV_FP8_E4M3 ? c->v_scale : 1.f;
+  a->rows = nullptr;
+  a->seq_rows = nullptr;
+  a->num_rows = 0;
+  a->whole_base = int32_t(2 * int64_t(kMaxWorkers) * kMaxGroup);
   return PKV_OK;
 }
 
@@ -1154,28 +1349,37 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
   if (!mfma && lay.parts <= 1) a.part_tokens = 0;   // the vector kernel does not split
   *merge = mfma || lay.parts > 1;
   return c->head_dim == 64
-             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, s)
-             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, s);
+             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, false, s)
+             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, false, s);
 }
 
-template <int NT>
+template <int NT, bool ROWS>
 static int launch_merge_nt(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
   const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
   const dim3 block(NT);
+  if (ROWS)  // bf16 q / out only (the matrix-core kernel)
+    return head_dim == 64
+               ? launch(merge_kernel<uint16_t, 64, NT, true>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 128, NT, true>, mgrid, block, s, a, "merge");
   if (head_dim == 64)
     return q_dtype == PKV_F32
-               ? launch(merge_kernel<float, 64, NT>, mgrid, block, s, a, "merge")
-               : launch(merge_kernel<uint16_t, 64, NT>, mgrid, block, s, a, "merge");
-  return q_dtype == PKV_F32 ? launch(merge_kernel<float, 128, NT>, mgrid, block, s, a, "merge")
-                            : launch(merge_kernel<uint16_t, 128, NT>, mgrid, block, s, a, "merge");
+               ? launch(merge_kernel<float, 64, NT, false>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 64, NT, false>, mgrid, block, s, a, "merge");
+  return q_dtype == PKV_F32
+             ? launch(merge_kernel<float, 128, NT, false>, mgrid, block, s, a, "merge")
+             : launch(merge_kernel<uint16_t, 128, NT, false>, mgrid, block, s, a, "merge");
 }
 
 // A batch of few (sequence, KV head) pairs has long contexts in many pieces each:
 // wider workgroups split those pieces into more groups.
-static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
-  return int64_t(a.num_seqs) * a.num_kv_heads < 256
-             ? launch_merge_nt<kMergeFewPairs>(a, head_dim, q_dtype, s)
-             : launch_merge_nt<kMergeThreads>(a, head_dim, q_dtype, s);
+static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s,
+                        bool rows = false) {
+  const bool few = int64_t(a.num_seqs) * a.num_kv_heads < 256;
+  if (rows)
+    return few ? launch_merge_nt<kMergeFewPairs, true>(a, head_dim, q_dtype, s)
+               : launch_merge_nt<kMergeThreads, true>(a, head_dim, q_dtype, s);
+  return few ? launch_merge_nt<kMergeFewPairs, false>(a, head_dim, q_dtype, s)
+             : launch_merge_nt<kMergeThreads, false>(a, head_dim, q_dtype, s);
 }
 
 extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const void* k_pool,
@@ -1272,4 +1476,46 @@ extern "C" int pkv_paged_attn_decode(const void* q, int32_t q_dtype, const void*
                                   context_lens, num_seqs, num_q_heads, scale, out, max_context_len,
                                   partition_size, workspace, workspace_bytes, stream,
                                   PKV_IMPL_AUTO);
+}
+
+extern "C" size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows) {
+  if (check_desc(c) || num_rows < 0) return 0;
+  return ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim).total;
+}
+
+extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const void* k_pool,
+                                          const void* v_pool, const pkv_cache_desc* c,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, float scale, void* out,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          const int32_t* rows, int32_t num_rows,
+                                          const int32_t* seq_rows, void* workspace,
+                                          size_t workspace_bytes, void* stream, int32_t phases) {
+  clear_error();
+  if (num_rows < 0) return fail(PKV_E_INVAL, "negative num_rows");
+  if (phases < 1 || phases > 3) return fail(PKV_E_INVAL, "phases must be 1, 2 or 3");
+  DecodeArgs a;
+  WsLayout lay;
+  int rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
+                   num_seqs, num_q_heads, scale, out, max_context_len, partition_size, workspace,
+                   workspace_bytes, &a, &lay, num_rows);
+  if (rc || num_seqs == 0) return rc;
+  if (c->kv_dtype == PKV_F32)
+    return fail(PKV_E_UNSUPPORTED, "the shared-prefix decode needs a bf16 or fp8 pool");
+  if (!rows || !seq_rows || num_rows == 0) return fail(PKV_E_INVAL, "no rows");
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(seq_rows)) & 15u)
+    return fail(PKV_E_INVAL, "rows and seq_rows must be 16-byte aligned");
+  a.rows = reinterpret_cast<const int4*>(rows);
+  a.seq_rows = reinterpret_cast<const int4*>(seq_rows);
+  a.num_rows = num_rows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (phases & 1) {
+    rc = c->head_dim == 64
+             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, true, false, true, s)
+             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, true, false, true, s);
+    if (rc) return rc;
+  }
+  if (phases & 2) return launch_merge(a, c->head_dim, q_dtype, s, true);
+  return PKV_OK;
 }

@@ -1,0 +1,86 @@
+// Rows of the shared-prefix decode: which sequences of a batch attend a run of
+// shared leading blocks together.  Sequences forked from one prompt share the
+// prompt's full blocks through their block tables (ithome article 10417389,
+// section 4, "Physical block sharing"; glossary "PagedAttention", "Sharing
+// blocks between sequences"): their keys and values are the same bytes, so
+// the decode reads them once for all the sharers' queries.
+//
+// A group is a run of consecutive batch sequences (at most 16 / group size of
+// them, the matrix-core kernel's query columns) whose tables start with the
+// same nb >= min_shared_blocks block ids; nb is also kept below every
+// member's last block, so each member has tokens after the shared part.  A
+// group becomes one prefix row (tokens [0, nb * B) of the first member's
+// table, queries of all members) and one row per member for the rest of its
+// context; any other sequence is one row for its whole context.
+#include <algorithm>
+#include <cstdint>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, int32_t num_seqs,
+                                   int32_t max_blocks, int32_t block_size, int32_t group,
+                                   int32_t min_shared_blocks, int32_t* rows, int32_t* seq_rows) {
+  clear_error();
+  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0 || group < 1 || group > 16)
+    return fail(PKV_E_INVAL, "bad sizes (num_seqs %d, max_blocks %d, block_size %d, group %d)",
+                num_seqs, max_blocks, block_size, group);
+  if (num_seqs > 0 && (!tables || !lens || !rows || !seq_rows))
+    return fail(PKV_E_INVAL, "NULL pointer");
+  const int max_members = 16 / group;
+  const int min_nb = std::max(1, min_shared_blocks);
+  // full blocks of sequence i before its last token: the most it can share
+  auto shareable = [&](int i) {
+    const int64_t n = lens[i] > 0 ? (int64_t(lens[i]) - 1) / block_size : 0;
+    return int(std::min<int64_t>(n, max_blocks));
+  };
+  auto common = [&](int i, int j, int limit) {
+    const int32_t* a = tables + int64_t(i) * max_blocks;
+    const int32_t* b = tables + int64_t(j) * max_blocks;
+    int k = 0;
+    while (k < limit && a[k] == b[k] && a[k] >= 0) ++k;
+    return k;
+  };
+  int nr = 0;
+  auto put_row = [&](int seq, int tb, int te, int m) {
+    int32_t* r = rows + int64_t(nr) * 4;
+    r[0] = seq;
+    r[1] = tb;
+    r[2] = te;
+    r[3] = m;
+    return nr++;
+  };
+  for (int i = 0; i < num_seqs;) {
+    int nb = shareable(i);
+    int n = 1;
+    while (n < max_members && i + n < num_seqs) {
+      const int c = common(i, i + n, std::min(nb, shareable(i + n)));
+      if (c < min_nb) break;
+      nb = c;
+      ++n;
+    }
+    if (n >= 2 && nb >= min_nb) {
+      const int pre = put_row(i, 0, nb * block_size, n);
+      for (int m = 0; m < n; ++m) {
+        const int own = put_row(i + m, nb * block_size, -1, 1);
+        int32_t* sr = seq_rows + int64_t(i + m) * 4;
+        sr[0] = own;
+        sr[1] = pre;
+        sr[2] = m;
+        sr[3] = 0;
+      }
+      i += n;
+    } else {
+      const int own = put_row(i, 0, -1, 1);
+      int32_t* sr = seq_rows + int64_t(i) * 4;
+      sr[0] = own;
+      sr[1] = -1;
+      sr[2] = 0;
+      sr[3] = 0;
+      ++i;
+    }
+  }
+  return nr;
+}

@@ -21,8 +21,8 @@ import numpy as np
 
 from . import (IMPL_AUTO, IMPL_SHARED_BLOCKS, BlockManager, CacheDesc, alloc_host_pools,
                alloc_pools, alloc_quest_meta, append_tokens, copy_blocks, decode_workspace_bytes,
-               paged_attn_decode, quest_blocks_of_slots, quest_decode, quest_update_blocks,
-               quest_update_tails, reshape_and_cache, swap_blocks)
+               paged_attn_decode, prefix_rows, quest_blocks_of_slots, quest_decode,
+               quest_update_blocks, quest_update_tails, reshape_and_cache, swap_blocks)
 
 
 def to_device(x: np.ndarray, in_dtype: str, device):
@@ -241,3 +241,16 @@ class DecodeBatch:
 
     def max_context_len(self) -> int:
         return int(self.host_lens.max()) if len(self.host_lens) else 0
+
+    def shared_prefix_rows(self, group: int, min_shared_blocks: int = 1):
+        """Rows of the shared-prefix decode for the batch as it stands, uploaded:
+        ``(rows, seq_rows)`` device int32.  Sequences that share leading blocks must be
+        consecutive in the batch.  The rows stay valid while no shared block is replaced
+        (appends only grow the contexts after the shared part)."""
+        import torch
+
+        t, lens = self.cache.bm.block_tables(self.seqs, self.max_blocks)
+        rows, seq_rows = prefix_rows(t, lens, self.cache.desc.block_size, group,
+                                     min_shared_blocks)
+        dev = self.cache.device
+        return (torch.from_numpy(rows).to(dev), torch.from_numpy(seq_rows).to(dev))

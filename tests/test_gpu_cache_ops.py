@@ -47,14 +47,15 @@ def test_tiny_config_pools_bitexact():
     assert np.array_equal(g.lens.cpu().numpy(), st.ctx)
 
 
-def _shared_prefix_small(seed, prompts=3, n=4, prefix=40, B=16, Hkv=2, D=64):
+def _shared_prefix_small(seed, prompts=3, n=4, prefix=40, B=16, Hkv=2, D=64, g=2, max_tail=40,
+                         kv_dtype="bf16"):
     """A reduced copy of the shared-prefix workload: forks, one copy-on-write batch, tails."""
     import dataclasses
     import math
 
     base = workloads.shared_prefix_bf16()
     rng = np.random.default_rng(seed)
-    tails = rng.integers(0, 40, size=prompts * n)
+    tails = rng.integers(0, max_tail, size=prompts * n)
     ids = np.arange(prompts * n, dtype=np.int64)
     ctx = prefix + 1 + tails + 1
     need = sum(prefix // B + sum(-(-(int(ctx[p * n + k]) - (prefix // B) * B) // B)
@@ -74,8 +75,8 @@ def _shared_prefix_small(seed, prompts=3, n=4, prefix=40, B=16, Hkv=2, D=64):
         return [((i // n) * n, 0, prefix), (10_000 + i, 0, int(ctx[i]) - prefix)]
 
     return dataclasses.replace(
-        base, name="shared-prefix-small", seed=seed, num_q_heads=2 * Hkv, num_kv_heads=Hkv,
-        head_dim=D, block_size=B, num_blocks=N, scale=1 / math.sqrt(D),
+        base, name="shared-prefix-small", seed=seed, num_q_heads=g * Hkv, num_kv_heads=Hkv,
+        head_dim=D, block_size=B, num_blocks=N, scale=1 / math.sqrt(D), kv_dtype=kv_dtype,
         free_order=rng.permutation(N).astype(np.int32), setup_ops=ops, decode_seqs=ids,
         ctx_lens=ctx, _segments=seg, _cache={})
 

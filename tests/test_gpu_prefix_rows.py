@@ -1,0 +1,132 @@
+"""GPU parity of the shared-prefix decode (rows): forked samples attend their shared
+prompt blocks once for all members' queries, then their own tokens; the result must
+match the fp64 oracle within the dtype tolerance and the plain decode of the same
+state, and with no shared run it must be the plain decode bit for bit."""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, GpuState, out_host, torch_mod
+from oracle_pipeline import decode as oracle_decode
+from oracle_pipeline import run as oracle_run
+from test_gpu_cache_ops import _shared_prefix_small
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows_decode(g, rows, seq_rows, ps, phases=3):
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = g.wl
+    out = torch.empty_like(g.q)
+    pkv.paged_attn_decode_rows(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens, wl.scale,
+                               out, g.desc, wl.max_context_len, ps, rows, seq_rows)
+    torch.cuda.synchronize()
+    return out
+
+
+def _rows(g, group, min_blocks=1):
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    t = g.tables.cpu().numpy()
+    ln = g.lens.cpu().numpy()
+    rows, seq_rows = pkv.prefix_rows(t, ln, g.wl.block_size, group, min_blocks)
+    return rows, seq_rows, torch.from_numpy(rows).cuda(), torch.from_numpy(seq_rows).cuda()
+
+
+CASES = [
+    dict(seed=401, prompts=3, n=4, prefix=40, D=64, Hkv=2, g=2),
+    dict(seed=402, prompts=3, n=4, prefix=200, D=128, Hkv=2, g=4),
+    dict(seed=403, prompts=2, n=4, prefix=520, D=128, Hkv=4, g=4, max_tail=300),
+    dict(seed=404, prompts=2, n=3, prefix=97, D=128, Hkv=1, g=5),
+    dict(seed=405, prompts=3, n=4, prefix=200, D=128, Hkv=2, g=4, kv_dtype="fp8"),
+    dict(seed=406, prompts=2, n=4, prefix=130, D=64, Hkv=2, g=4, B=8),
+    dict(seed=407, prompts=2, n=4, prefix=300, D=128, Hkv=2, g=2, B=32),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c['seed']}")
+def test_rows_match_oracle_and_plain_decode(case):
+    wl = _shared_prefix_small(**case)
+    print(f"rows case {case}", flush=True)
+    g = GpuState(wl)
+    st = oracle_run(wl)
+    ref = oracle_decode(st)
+    group = wl.num_q_heads // wl.num_kv_heads
+    rows, seq_rows, rows_d, sr_d = _rows(g, group)
+    # every prompt's samples form one group sharing the prompt's full blocks (the half-full
+    # last prompt block was copied on the first divergent write)
+    n, B = case["n"], wl.block_size
+    prefix_rows = rows[rows[:, 3] > 1]
+    assert len(prefix_rows) == case["prompts"], rows
+    nb = case["prefix"] // B
+    assert (prefix_rows[:, 2] == nb * B).all(), rows
+    assert (prefix_rows[:, 3] == min(n, 16 // group)).all()
+    tol = TOL[wl.kv_dtype]
+    plain = out_host(g.decode(0, 2))
+    for ps in (0, 32, 256):
+        out = out_host(_rows_decode(g, rows_d, sr_d, ps))
+        err = np.abs(out - ref).max()
+        assert err <= tol, (ps, err)
+        assert np.abs(out - plain).max() <= tol
+
+
+def test_no_shared_run_is_the_plain_decode_bit_for_bit():
+    torch = torch_mod()
+    wl = _shared_prefix_small(410, prompts=2, n=4, prefix=100, D=128, Hkv=2, g=4)
+    g = GpuState(wl)
+    group = wl.num_q_heads // wl.num_kv_heads
+    # a minimum longer than the prompt: every row is a plain sequence
+    rows, seq_rows, rows_d, sr_d = _rows(g, group, min_blocks=100)
+    assert len(rows) == len(g.seqs) and (rows[:, 1] == 0).all() and (seq_rows[:, 1] == -1).all()
+    for ps in (0, 64):
+        a = _rows_decode(g, rows_d, sr_d, ps)
+        b = g.decode(ps, 2)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_interleaved_families_are_not_grouped():
+    """Samples of different prompts alternating in the batch share nothing with their
+    neighbours: no group is formed and the result is still right."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = _shared_prefix_small(411, prompts=2, n=2, prefix=64, D=64, Hkv=2, g=2)
+    g = GpuState(wl)
+    order = [0, 2, 1, 3]                       # prompt 0, prompt 1, prompt 0, prompt 1
+    t = g.tables.cpu().numpy()[order]
+    ln = g.lens.cpu().numpy()[order]
+    rows, seq_rows = pkv.prefix_rows(t, ln, wl.block_size, 2, 1)
+    assert (rows[:, 3] == 1).all()
+    st = oracle_run(wl)
+    ref = oracle_decode(st)[order]
+    q = g.q[order].contiguous()
+    out = torch.empty_like(q)
+    pkv.paged_attn_decode_rows(q, g.cache.k_pool, g.cache.v_pool,
+                               g.tables[order].contiguous(), g.lens[order].contiguous(),
+                               wl.scale, out, g.desc, wl.max_context_len, 0,
+                               torch.from_numpy(rows).cuda(), torch.from_numpy(seq_rows).cuda())
+    torch.cuda.synchronize()
+    assert np.abs(out_host(out) - ref).max() <= TOL["bf16"]
+
+
+def test_split_phases_equal_the_single_call():
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = _shared_prefix_small(412, prompts=3, n=4, prefix=200, D=128, Hkv=2, g=4)
+    g = GpuState(wl)
+    rows, seq_rows, rows_d, sr_d = _rows(g, 4)
+    ws = torch.empty(pkv.rows_workspace_bytes(g.desc, len(rows)), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for phases in ((3,), (1, 2)):
+        out = torch.empty_like(g.q)
+        for ph in phases:
+            pkv.paged_attn_decode_rows(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens,
+                                       wl.scale, out, g.desc, wl.max_context_len, 0, rows_d,
+                                       sr_d, workspace=ws, phases=ph)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
