@@ -140,7 +140,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     torch.cuda.synchronize()
     st = cache.bm.stats()
     shared = st["logical_blocks"] > st["physical_blocks"]
-    # forked samples share blocks: read them once for all sharers (shared-prefix rows), or
+    # forked samples share blocks: read them once for all sharers (shared-prefix units), or
     # per sequence with the shared blocks kept cached
     use_rows = shared and rows_mode != "off"
     if use_rows:
@@ -148,8 +148,8 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         n_rows = int(rows_d.shape[0])
         ws_bytes = pkv.rows_workspace_bytes(desc, n_rows)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        log(f"shared-prefix rows: {n_rows} rows for {S} sequences, "
-            f"{int((rows_d[:, 3] > 1).sum())} shared prefixes")
+        log(f"shared-prefix units: {n_rows} units for {S} sequences, "
+            f"{int((rows_d[:, 2] > 1).sum())} with shared blocks")
     elif shared:
         impl |= pkv.IMPL_SHARED_BLOCKS
     kv_bytes = np.zeros(total)
@@ -418,7 +418,7 @@ def main() -> int:
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 vector, 2 mfma")
     ap.add_argument("--workers", type=int, default=16)
     ap.add_argument("--rows", choices=("auto", "off"), default="auto",
-                    help="shared-prefix rows decode for batches whose sequences share blocks "
+                    help="shared-prefix (unit) decode for batches whose sequences share blocks "
                          "(auto), or the per-sequence decode (off)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -479,7 +479,7 @@ def main() -> int:
             "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
             "mean_context": round(mean_ctx, 1), "partition_size": ps,
-            "kv_loads": ("shared-prefix rows" if r["rows"] else
+            "kv_loads": ("shared-prefix units" if r["rows"] else
                          "cached (shared blocks)" if r["shared"] else "streaming"),
             "prefix_cache": r["cache_stats"],
             "description": wl.description,

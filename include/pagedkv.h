@@ -278,44 +278,46 @@ int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t n
  * matrix-core kernel has 16 query columns, of which a head group uses
  * num_q_heads / num_kv_heads.  The result is the same attention as
  * pkv_paged_attn_decode gives (softmax over each sequence's whole context),
- * up to rounding: each context is cut into the shared part and the rest,
- * and the pieces are merged as split contexts are.
+ * up to rounding: a member's running softmax goes on from the shared tokens
+ * to its own, and a unit split between workers is merged as a split context
+ * is.
  *
- * Rows: the decode runs over rows instead of sequences.  Row r is int32
- * [4] {seq, first_token, end_token, members}: tokens [first_token, end_token)
- * of sequence seq's context (end_token < 0: up to its context length;
- * first_token a multiple of block_size), scored with the queries of the
- * `members` consecutive sequences seq .. seq + members - 1 (at most
- * 16 / group; members > 1 requires that all of them hold the same block ids
- * over those tokens).  seq_rows[s] = {own row, prefix row or -1, member
- * index within the prefix row, 0}: sequence s's context is its own row plus,
- * when it has one, its column of the prefix row.  A row with first_token 0
- * and one member is a plain sequence.
+ * Units: the decode runs over units instead of sequences.  Unit u is int32
+ * [4] {seq0, shared_tokens, members, 0}: the `members` consecutive sequences
+ * seq0 .. seq0 + members - 1 (at most 16 / group) hold the same block ids
+ * over their first shared_tokens tokens (a multiple of block_size, at most
+ * every member's context length).  The kernel reads those tokens once,
+ * through seq0's table, scoring every member's queries, then each member's
+ * remaining tokens through its own table.  seq_rows[s] = {unit, member index
+ * within the unit, 0, 0}.  A unit {s, 0, 1, 0} is a plain sequence.
  */
 
-/* Build the rows for a batch on the host: runs of consecutive sequences (at
+/* Build the units for a batch on the host: runs of consecutive sequences (at
  * most 16 / group) whose tables start with the same >= min_shared_blocks
  * block ids share those blocks, kept below each member's last block.
  *   tables   host int32 [num_seqs][max_blocks] (the batch's block tables)
  *   lens     host int32 [num_seqs] context lengths
- *   rows     host int32 [2 * num_seqs][4] out; seq_rows host int32 [num_seqs][4] out
- * Returns the number of rows (>= num_seqs) or a negative pkv_status. */
+ *   rows     host int32 [num_seqs][4] out (units); seq_rows host int32 [num_seqs][4] out
+ * Returns the number of units (1 .. num_seqs; 0 for an empty batch) or a
+ * negative pkv_status. */
 int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, int32_t num_seqs,
                         int32_t max_blocks, int32_t block_size, int32_t group,
                         int32_t min_shared_blocks, int32_t* rows, int32_t* seq_rows);
 
-/* Workspace bytes of pkv_paged_attn_decode_rows for num_rows rows (0 on invalid
- * arguments): a header, one record per (row, KV head), the persistent workers'
- * partial-segment slots and 16 partial rows per (row, KV head). */
+/* Workspace bytes of pkv_paged_attn_decode_rows for num_rows units (0 on
+ * invalid arguments): a header, one record per (unit, KV head) and the
+ * persistent workers' partial-segment slots (two of 16 rows each). */
 size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows);
 
-/* Decode attention over rows (see above); arguments as pkv_paged_attn_decode,
+/* Decode attention over units (see above); arguments as pkv_paged_attn_decode,
  * plus rows / seq_rows (device int32 [num_rows][4] / [num_seqs][4], 16-byte
  * aligned, e.g. uploaded from pkv_prefix_rows) and phases: 1 the decode
  * kernel, 2 the merge, 3 both (1 then 2 on the same workspace and stream).
- * bf16 or fp8 pools only (PKV_E_UNSUPPORTED for f32).  Row fields are trusted
- * only as far as memory safety: out-of-range sequences or members are cut, and
- * token ranges are clamped to the context. */
+ * bf16 or fp8 pools only (PKV_E_UNSUPPORTED for f32).  Unit fields are
+ * trusted only as far as memory safety: out-of-range sequences and members
+ * are cut, shared tokens are cut to whole blocks of seq0's context, and a
+ * sequence whose seq_rows entry is out of range gets no output.  Outputs of
+ * sequences whose units break the rules above are undefined. */
 int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype,
                                const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -435,12 +435,13 @@ def paged_attn_merge(out, context_lens, num_kv_heads: int, max_context_len: int,
 
 def prefix_rows(tables: np.ndarray, lens: np.ndarray, block_size: int, group: int,
                 min_shared_blocks: int = 1) -> Tuple[np.ndarray, np.ndarray]:
-    """Rows of the shared-prefix decode for a batch (host): ``(rows [R, 4], seq_rows [S, 4])``
-    int32, built by the library from the batch's block tables and context lengths."""
+    """Units of the shared-prefix decode for a batch (host): ``(rows [U, 4], seq_rows [S, 4])``
+    int32, built by the library from the batch's block tables and context lengths; a unit
+    is {first sequence, shared tokens, members, 0}, seq_rows[s] = {unit, member, 0, 0}."""
     t = np.ascontiguousarray(tables, dtype=np.int32)
     ln = np.ascontiguousarray(lens, dtype=np.int32)
     S = int(t.shape[0])
-    rows = np.zeros((max(1, 2 * S), 4), dtype=np.int32)
+    rows = np.zeros((max(1, S), 4), dtype=np.int32)
     seq_rows = np.zeros((max(1, S), 4), dtype=np.int32)
     n = int(lib.pkv_prefix_rows(t.ctypes.data_as(_pi32), ln.ctypes.data_as(_pi32), S,
                                 int(t.shape[1]) if t.ndim == 2 else 0, int(block_size),

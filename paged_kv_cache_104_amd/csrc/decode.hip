@@ -65,11 +65,11 @@ struct DecodeArgs {
   int32_t workers;      // MFMA kernel: persistent workers launched
   float qk_scale_log2;  // scale * log2(e) * k_scale
   float v_scale;
-  // shared-prefix (row) decode only
-  const int4* rows;     // [num_rows] {table row, first token, end token (< 0: context length), members}
-  const int4* seq_rows; // [num_seqs] {own row, prefix row (< 0: none), member index, 0}
+  // shared-prefix decode only
+  const int4* rows;     // [num_rows] units {first sequence, shared tokens, members, 0}
+  const int4* seq_rows; // [num_seqs] {unit, member index, 0, 0}
   int32_t num_rows;
-  int32_t whole_base;   // first workspace row of the pieces of pairs inside one worker's range
+  int32_t block_size;
 };
 
 // Partitions of a context of ctx tokens for the vector kernel: max(1, ctx / P),
@@ -333,7 +333,7 @@ template <int KV, int D>
 __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uint4 (&qv)[D / 32],
                                              floatx4_t (&acc)[D / 16],
                                              floatx4_t& lsum, float& m, float sl2, int tt, int t1,
-                                             int r) {
+                                             int r, bool active) {
   // scores S^T[token][head] of the two 16-token tiles
   floatx4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -359,6 +359,11 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (tt + 8 * r + e >= t1) x[e] = -INFINITY;
+  }
+  // a query column that does not attend these tokens (shared-prefix decode)
+  if (!active) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
   }
   float lmax = x[0];
 #pragma unroll
@@ -491,49 +496,144 @@ __device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename Kv
   }
 }
 
-// A position in the step stream: pair (row s, KV head kvh), the pair's first
-// step P in the stream, its steps n, the row's tokens ctx, and the step x
-// within the pair.  The stream orders pairs by row, then KV head.  A row is a
-// sequence (plain decode: seq = s, tokens from tb = 0, one member) or, in the
-// shared-prefix decode, a span [tb, tb + ctx) of sequence seq's context whose
-// query columns come from M consecutive sequences seq .. seq + M - 1.
+// A position in the step stream: pair (unit s, KV head kvh), step x of the
+// pair's n steps, P the pair's first step in the stream.  The stream orders
+// pairs by unit, then KV head.  In the plain decode a unit is one sequence.
+// In the shared-prefix decode a unit is a family of M consecutive sequences
+// seq0 .. seq0 + M - 1 whose first T tokens sit in the same blocks: its steps
+// are the shared span [0, T), read through seq0's table with every member's
+// query columns active, then each member's own span [T, its context), read
+// through its own table with only its columns active.  The current span
+// (sub = -1 shared, else the member): table row seq, first token tb, tokens
+// ctx, pair steps [x0, xe).
 struct Cursor {
-  int s, kvh, x, P, n, ctx;
-  int seq, tb, M;
+  int s, kvh, x, P, n;
+  int seq, tb, ctx, x0, xe;
+  int seq0, M, T, sub;
 };
 
 __device__ __forceinline__ int clamp_ctx(int len, int max_ctx) { return max(0, min(len, max_ctx)); }
 __device__ __forceinline__ int ctx_steps(int ctx) { return (ctx + 31) >> 5; }
 
-// Tokens of row r: sequence, first token and count (clamped to the context
-// and to max_ctx; an out-of-range sequence has none), and the members.
-// The span of row descriptor d given its sequence's context length len.
-__device__ __forceinline__ void row_span_of(const DecodeArgs& a, int4 d, int len, int& seq,
-                                            int& tb, int& ctx, int& M) {
-  seq = d.x;
-  M = max(1, min(d.w, kMaxGroup / a.group));
-  if (seq < 0 || seq >= a.num_seqs) {
-    seq = 0;
-    tb = 0;
-    ctx = 0;
-    return;
-  }
-  M = min(M, a.num_seqs - seq);
-  len = clamp_ctx(len, a.max_ctx);
-  const int te = d.z < 0 ? len : min(d.z, len);
-  tb = max(0, d.y);
-  ctx = max(0, te - tb);
-}
-
+// Sequence whose context length a unit descriptor needs first (a valid index).
 __device__ __forceinline__ int row_seq(const DecodeArgs& a, int4 d) {
   return (d.x >= 0 && d.x < a.num_seqs) ? d.x : 0;
 }
 
-__device__ __forceinline__ void row_span(const DecodeArgs& a, const int4* __restrict__ rows,
-                                         const int32_t* __restrict__ lens, int r, int& seq,
-                                         int& tb, int& ctx, int& M) {
-  const int4 d = rows[r];
-  row_span_of(a, d, lens[row_seq(a, d)], seq, tb, ctx, M);
+// Unit of descriptor d {first sequence, shared tokens, members, 0} given the
+// first sequence's context length len0: members cut to the 16 query columns
+// and to the batch, shared tokens to whole blocks of the first member's
+// context.  An out-of-range first sequence gives a unit without members.
+__device__ __forceinline__ void unit_of(const DecodeArgs& a, int4 d, int len0, int& seq0, int& M,
+                                        int& T) {
+  if (d.x < 0 || d.x >= a.num_seqs) {
+    seq0 = 0;
+    M = 0;
+    T = 0;
+    return;
+  }
+  seq0 = d.x;
+  M = max(1, min(min(d.z, kMaxGroup / a.group), a.num_seqs - d.x));
+  T = min(max(0, d.y), clamp_ctx(len0, a.max_ctx)) & ~(a.block_size - 1);
+}
+
+// Unit d's fields and the steps of one of its KV heads: the shared span, then
+// every member's own.  The members' lengths are all requested before any is
+// used (a loop over M would wait for each load in turn).
+__device__ __forceinline__ int unit_load(const DecodeArgs& a, int4 d,
+                                         const int32_t* __restrict__ lens, int& seq0, int& M,
+                                         int& T) {
+  const int first = row_seq(a, d);
+  int len[kMaxGroup];
+#pragma unroll
+  for (int m = 0; m < kMaxGroup; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
+  unit_of(a, d, len[0], seq0, M, T);
+  int n = ctx_steps(T);
+#pragma unroll
+  for (int m = 0; m < kMaxGroup; ++m)
+    n += m < M ? ctx_steps(max(0, clamp_ctx(len[m], a.max_ctx) - T)) : 0;
+  return n;
+}
+
+// Enter span cu.sub of the unit, whose first step is pair step cu.x0.
+__device__ __forceinline__ void enter_span(Cursor& cu, const DecodeArgs& a,
+                                           const int32_t* __restrict__ lens) {
+  if (cu.sub < 0) {
+    cu.seq = cu.seq0;
+    cu.tb = 0;
+    cu.ctx = cu.T;
+  } else {
+    cu.seq = cu.seq0 + cu.sub;
+    cu.tb = cu.T;
+    cu.ctx = max(0, clamp_ctx(lens[cu.seq], a.max_ctx) - cu.T);
+  }
+  cu.xe = cu.x0 + ctx_steps(cu.ctx);
+}
+
+// Move on to the span that holds pair step cu.x (the pair has that step):
+// from the first span, or from the one after the current.
+__device__ __forceinline__ void seek_span(Cursor& cu, const DecodeArgs& a,
+                                          const int32_t* __restrict__ lens) {
+  cu.sub = -1;
+  cu.x0 = 0;
+  enter_span(cu, a, lens);
+  while (cu.x >= cu.xe) {
+    cu.x0 = cu.xe;
+    ++cu.sub;
+    enter_span(cu, a, lens);
+  }
+}
+__device__ __forceinline__ void next_span(Cursor& cu, const DecodeArgs& a,
+                                          const int32_t* __restrict__ lens) {
+  do {
+    cu.x0 = cu.xe;
+    ++cu.sub;
+    enter_span(cu, a, lens);
+  } while (cu.x >= cu.xe);
+}
+
+// The cursor at step x of the pair of unit s, KV head kvh (fields s, kvh, x,
+// P, n already set).
+template <bool ROWS>
+__device__ __forceinline__ void enter_unit(Cursor& cu, const DecodeArgs& a,
+                                           const int4* __restrict__ rows,
+                                           const int32_t* __restrict__ lens) {
+  if constexpr (ROWS) {
+    // the members' lengths requested together, then the spans walked in registers
+    // (a walk span by span would wait for one length after another)
+    const int4 d = rows[cu.s];
+    const int first = row_seq(a, d);
+    int len[kMaxGroup];
+#pragma unroll
+    for (int m = 0; m < kMaxGroup; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
+    unit_of(a, d, len[0], cu.seq0, cu.M, cu.T);
+    cu.sub = -1;
+    cu.seq = cu.seq0;
+    cu.tb = 0;
+    cu.ctx = cu.T;
+    cu.x0 = 0;
+    cu.xe = ctx_steps(cu.T);
+#pragma unroll
+    for (int m = 0; m < kMaxGroup; ++m) {
+      if (m < cu.M && cu.x >= cu.xe) {
+        cu.sub = m;
+        cu.seq = cu.seq0 + m;
+        cu.tb = cu.T;
+        cu.ctx = max(0, clamp_ctx(len[m], a.max_ctx) - cu.T);
+        cu.x0 = cu.xe;
+        cu.xe += ctx_steps(cu.ctx);
+      }
+    }
+  } else {
+    cu.seq0 = cu.seq = cu.s;
+    cu.M = 1;
+    cu.T = 0;
+    cu.sub = 0;
+    cu.tb = 0;
+    cu.x0 = 0;
+    cu.ctx = clamp_ctx(lens[cu.s], a.max_ctx);
+    cu.xe = cu.n;
+  }
 }
 
 // Move to the next pair that has steps; the caller knows there is one.
@@ -544,18 +644,26 @@ __device__ __forceinline__ void next_pair(Cursor& cu, const DecodeArgs& a,
                                           int max_ctx) {
   cu.P += cu.n;
   cu.x = 0;
-  if (++cu.kvh < hkv) return;
+  if (++cu.kvh < hkv) {
+    if constexpr (ROWS) seek_span(cu, a, lens);
+    return;
+  }
   cu.kvh = 0;
-  do {
-    ++cu.s;
-    if constexpr (ROWS) {
-      row_span(a, rows, lens, cu.s, cu.seq, cu.tb, cu.ctx, cu.M);
-    } else {
-      cu.seq = cu.s;
+  if constexpr (ROWS) {
+    do {
+      ++cu.s;
+      cu.n = unit_load(a, rows[cu.s], lens, cu.seq0, cu.M, cu.T);
+    } while (cu.n == 0);
+    seek_span(cu, a, lens);
+  } else {
+    do {
+      ++cu.s;
+      cu.seq = cu.seq0 = cu.s;
       cu.ctx = clamp_ctx(lens[cu.s], max_ctx);
-    }
-  } while (cu.ctx == 0);
-  cu.n = ctx_steps(cu.ctx);
+    } while (cu.ctx == 0);
+    cu.n = ctx_steps(cu.ctx);
+    cu.xe = cu.n;
+  }
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
@@ -573,14 +681,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Steps of row (or sequence) i, for the scan in find_start.
+// Steps of unit (or sequence) i, for the scan in find_start.
 template <bool ROWS>
 __device__ __forceinline__ int unit_steps(const DecodeArgs& a, const int4* __restrict__ rows,
                                           const int32_t* __restrict__ lens, int i) {
   if constexpr (ROWS) {
-    int seq, tb, ctx, M;
-    row_span(a, rows, lens, i, seq, tb, ctx, M);
-    return ctx_steps(ctx);
+    int seq0, M, T;
+    return unit_load(a, rows[i], lens, seq0, M, T);
   } else {
     return ctx_steps(clamp_ctx(lens[i], a.max_ctx));
   }
@@ -597,20 +704,18 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
                                            int& total, int& q, Cursor& cu) {
   const int S = ROWS ? a.num_rows : a.num_seqs, hkv = a.num_kv_heads;
   int sum = 0;
+  int v[4];   // steps of the units of the last chunk (all of them when S <= 256)
   for (int s0 = 0; s0 < S; s0 += 256) {
     // every load of the chunk is requested before any is used
-    int v[4];
     if constexpr (ROWS) {
       int4 d[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) d[u] = rows[min(s0 + 64 * u + lane, S - 1)];  // unconditional
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = lens[row_seq(a, d[u])];
-#pragma unroll
       for (int u = 0; u < 4; ++u) {
-        int seq, tb, ctx, M;
-        row_span_of(a, d[u], v[u], seq, tb, ctx, M);
-        v[u] = s0 + 64 * u + lane < S ? ctx_steps(ctx) : 0;
+        int seq0, M, T;
+        const int n = unit_load(a, d[u], lens, seq0, M, T);
+        v[u] = s0 + 64 * u + lane < S ? n : 0;
       }
     } else {
 #pragma unroll
@@ -626,10 +731,12 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
   q = max(max(1, a.part_tokens >> 5), (total + a.workers - 1) / a.workers);
   if (int64_t(w) * q >= total) return false;
   const int target = w * q;
-  int base = 0;  // steps of one KV head of the rows before the chunk
+  int base = 0;  // steps of one KV head of the units before the chunk
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int s = s0 + lane;
-    const int n = s < S ? unit_steps<ROWS>(a, rows, lens, s) : 0;
+    // a batch of one chunk reuses the counts above (the selects keep v in registers)
+    const int n = S <= 256 ? (s0 == 0 ? v[0] : s0 == 64 ? v[1] : s0 == 128 ? v[2] : v[3])
+                           : s < S ? unit_steps<ROWS>(a, rows, lens, s) : 0;
     const int incl = wave_inclusive_scan(n, lane);
     const uint64_t hit = __ballot(hkv * (base + incl) > target);
     if (hit) {
@@ -641,14 +748,7 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
       cu.x = target - first - cu.kvh * ns;
       cu.n = ns;
       cu.P = first + cu.kvh * ns;
-      if constexpr (ROWS) {
-        row_span(a, rows, lens, cu.s, cu.seq, cu.tb, cu.ctx, cu.M);
-      } else {
-        cu.seq = cu.s;
-        cu.tb = 0;
-        cu.M = 1;
-        cu.ctx = clamp_ctx(lens[cu.s], a.max_ctx);
-      }
+      enter_unit<ROWS>(cu, a, rows, lens);
       return true;
     }
     base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
@@ -702,8 +802,9 @@ __device__ __forceinline__ void flush_recs(const DecodeArgs& a, OutStage<D>& st,
 }
 
 // Columns of a pair with a query behind them, and the workspace rows per
-// partial-segment slot: the head group (plain decode), or up to 16 columns of
-// M member sequences (shared-prefix decode, whose slots are 16 rows apart).
+// partial-segment slot: the head group (plain decode), or the head groups of
+// the unit's M members side by side (shared-prefix decode, whose slots are 16
+// rows apart).
 template <bool ROWS>
 __device__ __forceinline__ int pair_cols(const DecodeArgs& a, const Cursor& cu) {
   return ROWS ? cu.M * a.group : a.group;
@@ -733,14 +834,13 @@ __device__ __forceinline__ void store_piece(const DecodeArgs& a, int64_t row0, i
 }
 
 // End of a worker's share of a pair.  A pair that lies inside the worker's
-// range [lo, lo + q) has its output staged; otherwise the share is a partial
-// segment, for the worker's slot 0 (the pair began before the range, staged)
-// or slot 1 (it goes on past the range: the end of the range, stored now).
-// In the shared-prefix decode, pairs of a shared prefix and of the spans after
-// it are pieces of their sequences' contexts: one that lies inside the range
-// goes to the pair's own workspace rows instead of the output.  The worker
-// that holds a pair's first step also records {first worker, workers} of the
-// pair for the merge.
+// range [lo, lo + q) has its outputs staged (one head group per member);
+// otherwise the share is a partial segment, for the worker's slot 0 (the pair
+// began before the range, staged) or slot 1 (it goes on past the range: the
+// end of the range, stored now).  The worker that holds a pair's first step
+// also records {first worker, workers} of the pair for the merge.  A column
+// that saw no token (a member whose span lies outside the segment) has sum 0:
+// its partial row is stored as zeros.
 template <int D, bool ROWS>
 __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
                                               const floatx4_t (&acc)[D / 16],
@@ -752,7 +852,6 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
   const int lo = w * q;
   const bool head = cu.P >= lo;                  // the pair starts in this range
   const bool whole = head && cu.P + cu.n <= lo + q;
-  const bool direct = !ROWS || (cu.tb == 0 && cu.M == 1);
   if (head) {
     if (n_rec == OutStage<D>::kMaxRecs) flush_recs<D>(a, st, n_rec, lane);
     if (lane == 0) {
@@ -762,11 +861,12 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
     ++n_rec;
   }
   const float l = lsum[0];
-  const float inv = a.v_scale / l;
-  if (whole && direct) {
-    if ((n_out + 1) * g > OutStage<D>::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
-    if (lane == 0) st.out_row[n_out] = cu.seq * a.num_q_heads + cu.kvh * g;
-    if (c < g) {
+  const float inv = ROWS ? (l > 0.f ? a.v_scale / l : 0.f) : a.v_scale / l;
+  if (whole) {
+    const int ne = ROWS ? cu.M : 1;              // staged entries: one head group each
+    if ((n_out + ne) * g > OutStage<D>::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
+    if (lane < ne) st.out_row[n_out + lane] = (cu.seq0 + lane) * a.num_q_heads + cu.kvh * g;
+    if (c < ncols) {
       uint2* o = st.out + (n_out * g + c) * (D / 4);
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
@@ -776,10 +876,7 @@ __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor&
         o[4 * j + r] = v;
       }
     }
-    ++n_out;
-  } else if (whole) {
-    store_piece<D>(a, a.whole_base + (int64_t(cu.s) * a.num_kv_heads + cu.kvh) * kMaxGroup,
-                   ncols, acc, m, l, inv, r, c);
+    n_out += ne;
   } else if (!head) {
     if (c < ncols) {
 #pragma unroll
@@ -859,14 +956,17 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   Cursor la = cu;                                  // load cursor
   int la_left = rem;                               // steps the load cursor still has to load
   int la_pbs[NB];
-  step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks, la.tb + 32 * la.x,
-                  la.tb + la.ctx, a.num_blocks);
+  step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks,
+                  ROWS ? la.tb + 32 * (la.x - la.x0) : 32 * la.x, ROWS ? la.tb + la.ctx : la.ctx,
+                  a.num_blocks);
 
   floatx4_t acc[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
+  // a finite start: a shared-prefix column that sees no token keeps exp2(-inf - m) = 0
+  constexpr float kMStart = ROWS ? -1e30f : -INFINITY;
+  float m = kMStart;
   StepRegs<KV, D> buf[NS];
   uint4 qc[D / 32];                 // query of the compute cursor's pair
   __shared__ OutStage<D> stage;
@@ -874,7 +974,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
   int seg0_cols = 0;                // columns of the staged slot-0 segment (0: none)
   bool la_first = true, cu_first = true;   // the next step is the worker's first
 
-  // query column c of the load cursor's pair: head c % g of member c / g
+  // query column c of a pair: head c % g of member c / g
   const int cm = c / g, ch = c - cm * g;
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
@@ -882,14 +982,16 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
     issue_step<KV, D, BS, NT>(                                                                 \
         R, k_pool + int64_t(la.kvh) * head_stride, v_pool + int64_t(la.kvh) * head_stride,     \
         la_pbs, blk_stride, L, la_first || la.x == 0, qrsrc,                                   \
-        uint32_t(((la.seq + cm) * a.num_q_heads + la.kvh * g + ch) * D * 2),                   \
+        uint32_t(((la.seq0 + cm) * a.num_q_heads + la.kvh * g + ch) * D * 2),                  \
         c < pair_cols<ROWS>(a, la), qbytes, r);                                                \
     la_first = false;                                                                          \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
       if (++la.x == la.n) next_pair<ROWS>(la, a, rows, lens, hkv, max_ctx);                    \
-      step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks, la.tb + 32 * la.x,      \
-                      la.tb + la.ctx, a.num_blocks);                                           \
+      else if (ROWS && la.x == la.xe) next_span(la, a, lens);                                  \
+      step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks,                         \
+                      ROWS ? la.tb + 32 * (la.x - la.x0) : 32 * la.x,                          \
+                      ROWS ? la.tb + la.ctx : la.ctx, a.num_blocks);                           \
     }                                                                                          \
   } while (0)
 
@@ -911,7 +1013,9 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
           for (int i = 0; i < D / 32; ++i) qc[i] = buf[st].q[i];
           cu_first = false;
         }
-        compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2, 32 * cu.x, cu.ctx, r);
+        compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2,
+                            ROWS ? 32 * (cu.x - cu.x0) : 32 * cu.x, cu.ctx, r,
+                            !ROWS || cu.sub < 0 || cm == cu.sub);
         --rem;
         if (++cu.x == cu.n || rem == 0) {
           write_segment<D, ROWS>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec,
@@ -921,8 +1025,10 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            m = -INFINITY;
+            m = kMStart;
           }
+        } else if (ROWS && cu.x == cu.xe) {
+          next_span(cu, a, lens);
         }
       }
     }
@@ -952,37 +1058,6 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeFewPairs = 512;
 constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
-// The pieces of one (row, KV head) pair in the shared-prefix decode: a pair
-// inside one worker's range has its own workspace rows; a split pair's pieces
-// are the slots of workers u0 .. u0 + count - 1 (slot 1 of the first, slot 0
-// after), 16 rows a slot.  Column col of piece k is workspace row at(k).
-struct PieceRange {
-  int64_t whole;
-  int u0, count, col;
-  bool direct;       // a plain row (first token 0, one member): written directly when whole
-  __device__ int64_t at(int k) const {
-    if (count == 1) return whole + col;
-    return (k == 0 ? int64_t(2 * u0 + 1) : int64_t(2 * (u0 + k))) * kMaxGroup + col;
-  }
-};
-
-// Row r of the shared-prefix decode as a piece range of KV head kvh at column
-// col; no pieces when the row has no tokens.
-__device__ __forceinline__ PieceRange row_pieces(const DecodeArgs& a, int r, int kvh, int col) {
-  PieceRange p{0, 0, 0, col, false};
-  if (r < 0 || r >= a.num_rows) return p;
-  int seq, tb, ctx, M;
-  row_span(a, a.rows, a.context_lens, r, seq, tb, ctx, M);
-  p.direct = tb == 0 && M == 1;
-  if (ctx == 0) return p;
-  const int64_t pr = int64_t(r) * a.num_kv_heads + kvh;
-  const int2 rec = a.recs[pr];
-  p.whole = a.whole_base + pr * kMaxGroup;
-  p.u0 = rec.x;
-  p.count = rec.y;
-  return p;
-}
-
 template <typename QT, int D, int NT, bool ROWS>
 __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   constexpr int kMergeThreads = NT;
@@ -1002,18 +1077,20 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   // piece k of head hg is row first(hg) + k * stride (+ fix for k > 0)
   int count = 0;
   int64_t first0 = 0, head_step = 0, stride = 0, fix = 0;
-  // shared-prefix decode: the sequence's own row, then the members' prefix row
-  PieceRange own{0, 0, 0, 0, false}, pre{0, 0, 0, 0, false};
   if constexpr (ROWS) {
+    // shared-prefix decode: the segments of the sequence's unit, in its member's columns
+    // (16-row slots); a sequence outside every unit is left alone
     const int4 sr = a.seq_rows[s];
-    own = row_pieces(a, sr.x, kvh, 0);
-    // a member index past the 16 columns is cut (it has no prefix piece)
-    pre = sr.y >= 0 && sr.z >= 0 && (sr.z + 1) * g <= kMaxGroup
-              ? row_pieces(a, sr.y, kvh, sr.z * g)
-              : PieceRange{0, 0, 0, 0, false};
-    // a plain row inside one worker's range was written directly by the decode kernel
-    if (pre.count == 0 && own.direct && own.count <= 1) return;
-    count = own.count + pre.count;
+    const int u = sr.x, mem = sr.y;
+    if (u < 0 || u >= a.num_rows || mem < 0 || (mem + 1) * g > kMaxGroup) return;
+    const int2 rec = a.recs[int64_t(u) * a.num_kv_heads + kvh];
+    const int u0 = min(max(rec.x, 0), kMaxWorkers - 1);
+    count = min(rec.y, kMaxWorkers - u0);
+    if (count <= 1) return;                          // written directly by the decode kernel
+    first0 = int64_t(2 * u0 + 1) * kMaxGroup + mem * g;
+    head_step = 1;
+    stride = 2 * kMaxGroup;
+    fix = -kMaxGroup;
   } else {
     const int proto = a.hdr[0];
     const int2 rec = a.recs[pair];
@@ -1043,12 +1120,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
     for (int k = pg; k < count; k += groups) {
-      int64_t pc;
-      if constexpr (ROWS) {
-        pc = k < own.count ? own.at(k) + hg : pre.at(k - own.count) + hg;
-      } else {
-        pc = first + k * stride + (k ? fix : 0);
-      }
+      const int64_t pc = first + k * stride + (k ? fix : 0);
       const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + pc * 2);
       const float4 o = acc4[pc * (D / 4) + d4];
       const float Mn = fmaxf(M, ml.x);
@@ -1138,16 +1210,15 @@ static WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
   return w;
 }
 
-// Shared-prefix decode workspace: header | records of the (row, KV head) pairs |
-// partial rows: the workers' slots (16 rows each) and then 16 rows per pair for
-// pairs that lie inside one worker's range.
+// Shared-prefix decode workspace: header | records of the (unit, KV head) pairs |
+// partial rows: the workers' two slots of 16 rows each.
 static WsLayout ws_layout_rows(int32_t num_rows, int32_t num_kv_heads, int32_t head_dim) {
   WsLayout w;
   w.parts = 1;
   w.pairs = int64_t(num_rows) * num_kv_heads;
   w.recs_off = 256;
   w.ml_off = w.recs_off + align256(size_t(w.pairs) * sizeof(int2));
-  w.rows = 2 * int64_t(kMaxWorkers) * kMaxGroup + w.pairs * kMaxGroup;
+  w.rows = 2 * int64_t(kMaxWorkers) * kMaxGroup;
   w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
   w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
   return w;
@@ -1324,7 +1395,7 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   a->rows = nullptr;
   a->seq_rows = nullptr;
   a->num_rows = 0;
-  a->whole_base = int32_t(2 * int64_t(kMaxWorkers) * kMaxGroup);
+  a->block_size = c->block_size;
   return PKV_OK;
 }
 

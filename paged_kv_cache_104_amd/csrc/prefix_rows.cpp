@@ -1,5 +1,5 @@
-// Rows of the shared-prefix decode: which sequences of a batch attend a run of
-// shared leading blocks together.  Sequences forked from one prompt share the
+// Units of the shared-prefix decode: which sequences of a batch attend a run
+// of shared leading blocks together.  Sequences forked from one prompt share the
 // prompt's full blocks through their block tables (ithome article 10417389,
 // section 4, "Physical block sharing"; glossary "PagedAttention", "Sharing
 // blocks between sequences"): their keys and values are the same bytes, so
@@ -9,9 +9,8 @@
 // them, the matrix-core kernel's query columns) whose tables start with the
 // same nb >= min_shared_blocks block ids; nb is also kept below every
 // member's last block, so each member has tokens after the shared part.  A
-// group becomes one prefix row (tokens [0, nb * B) of the first member's
-// table, queries of all members) and one row per member for the rest of its
-// context; any other sequence is one row for its whole context.
+// group becomes one unit {first member, nb * B shared tokens, members, 0};
+// any other sequence is a unit of its own {seq, 0, 1, 0}.
 #include <algorithm>
 #include <cstdint>
 
@@ -44,13 +43,20 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
     return k;
   };
   int nr = 0;
-  auto put_row = [&](int seq, int tb, int te, int m) {
+  auto put_unit = [&](int seq, int shared_tokens, int members) {
     int32_t* r = rows + int64_t(nr) * 4;
     r[0] = seq;
-    r[1] = tb;
-    r[2] = te;
-    r[3] = m;
-    return nr++;
+    r[1] = shared_tokens;
+    r[2] = members;
+    r[3] = 0;
+    for (int m = 0; m < members; ++m) {
+      int32_t* sr = seq_rows + int64_t(seq + m) * 4;
+      sr[0] = nr;
+      sr[1] = m;
+      sr[2] = 0;
+      sr[3] = 0;
+    }
+    ++nr;
   };
   for (int i = 0; i < num_seqs;) {
     int nb = shareable(i);
@@ -62,23 +68,10 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
       ++n;
     }
     if (n >= 2 && nb >= min_nb) {
-      const int pre = put_row(i, 0, nb * block_size, n);
-      for (int m = 0; m < n; ++m) {
-        const int own = put_row(i + m, nb * block_size, -1, 1);
-        int32_t* sr = seq_rows + int64_t(i + m) * 4;
-        sr[0] = own;
-        sr[1] = pre;
-        sr[2] = m;
-        sr[3] = 0;
-      }
+      put_unit(i, nb * block_size, n);
       i += n;
     } else {
-      const int own = put_row(i, 0, -1, 1);
-      int32_t* sr = seq_rows + int64_t(i) * 4;
-      sr[0] = own;
-      sr[1] = -1;
-      sr[2] = 0;
-      sr[3] = 0;
+      put_unit(i, 0, 1);
       ++i;
     }
   }

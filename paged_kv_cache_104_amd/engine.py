@@ -243,9 +243,9 @@ class DecodeBatch:
         return int(self.host_lens.max()) if len(self.host_lens) else 0
 
     def shared_prefix_rows(self, group: int, min_shared_blocks: int = 1):
-        """Rows of the shared-prefix decode for the batch as it stands, uploaded:
+        """Units of the shared-prefix decode for the batch as it stands, uploaded:
         ``(rows, seq_rows)`` device int32.  Sequences that share leading blocks must be
-        consecutive in the batch.  The rows stay valid while no shared block is replaced
+        consecutive in the batch.  The units stay valid while no shared block is replaced
         (appends only grow the contexts after the shared part)."""
         import torch
 

@@ -1,7 +1,7 @@
-"""GPU parity of the shared-prefix decode (rows): forked samples attend their shared
-prompt blocks once for all members' queries, then their own tokens; the result must
-match the fp64 oracle within the dtype tolerance and the plain decode of the same
-state, and with no shared run it must be the plain decode bit for bit."""
+"""GPU parity of the shared-prefix decode: forked samples form units that read their
+shared prompt blocks once for all members' queries, then each member's own tokens; the
+result must match the fp64 oracle within the dtype tolerance and the plain decode of the
+same state, and with no shared run it must be the plain decode bit for bit."""
 import numpy as np
 import pytest
 
@@ -55,14 +55,12 @@ def test_rows_match_oracle_and_plain_decode(case):
     ref = oracle_decode(st)
     group = wl.num_q_heads // wl.num_kv_heads
     rows, seq_rows, rows_d, sr_d = _rows(g, group)
-    # every prompt's samples form one group sharing the prompt's full blocks (the half-full
+    # every prompt's samples form one unit sharing the prompt's full blocks (the half-full
     # last prompt block was copied on the first divergent write)
     n, B = case["n"], wl.block_size
-    prefix_rows = rows[rows[:, 3] > 1]
-    assert len(prefix_rows) == case["prompts"], rows
-    nb = case["prefix"] // B
-    assert (prefix_rows[:, 2] == nb * B).all(), rows
-    assert (prefix_rows[:, 3] == min(n, 16 // group)).all()
+    assert n <= 16 // group
+    assert len(rows) == case["prompts"], rows
+    assert (rows[:, 1] == (case["prefix"] // B) * B).all() and (rows[:, 2] == n).all(), rows
     tol = TOL[wl.kv_dtype]
     plain = out_host(g.decode(0, 2))
     for ps in (0, 32, 256):
@@ -77,9 +75,9 @@ def test_no_shared_run_is_the_plain_decode_bit_for_bit():
     wl = _shared_prefix_small(410, prompts=2, n=4, prefix=100, D=128, Hkv=2, g=4)
     g = GpuState(wl)
     group = wl.num_q_heads // wl.num_kv_heads
-    # a minimum longer than the prompt: every row is a plain sequence
+    # a minimum longer than the prompt: every unit is a plain sequence
     rows, seq_rows, rows_d, sr_d = _rows(g, group, min_blocks=100)
-    assert len(rows) == len(g.seqs) and (rows[:, 1] == 0).all() and (seq_rows[:, 1] == -1).all()
+    assert len(rows) == len(g.seqs) and (rows[:, 1] == 0).all() and (rows[:, 2] == 1).all()
     for ps in (0, 64):
         a = _rows_decode(g, rows_d, sr_d, ps)
         b = g.decode(ps, 2)
@@ -98,7 +96,7 @@ def test_interleaved_families_are_not_grouped():
     t = g.tables.cpu().numpy()[order]
     ln = g.lens.cpu().numpy()[order]
     rows, seq_rows = pkv.prefix_rows(t, ln, wl.block_size, 2, 1)
-    assert (rows[:, 3] == 1).all()
+    assert (rows[:, 2] == 1).all()
     st = oracle_run(wl)
     ref = oracle_decode(st)[order]
     q = g.q[order].contiguous()
@@ -130,3 +128,31 @@ def test_split_phases_equal_the_single_call():
         torch.cuda.synchronize()
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("kv_dtype,D", [("bf16", 128), ("fp8", 64)])
+def test_hand_built_units(kv_dtype, D):
+    """Units the builder would not make but the kernel accepts: members that share no
+    tokens (every member reads its own table), one-member units whose context is cut in
+    two spans, and a last unit of a single sequence.  Each equals the oracle."""
+    import workloads
+
+    torch = torch_mod()
+    wl = workloads.random_small(421, S=9, Hq=8, Hkv=2, D=D, B=16, max_ctx=700,
+                                kv_dtype=kv_dtype, in_dtype="bf16", min_ctx=40)
+    g = GpuState(wl)
+    ref = oracle_decode(oracle_run(wl))
+    lens = g.lens.cpu().numpy()
+    units = np.array([[0, 0, 3, 0],                        # 0, 1, 2: no shared tokens
+                      [3, 32, 1, 0],                       # 3: [0, 32) then [32, len)
+                      [4, (int(lens[4]) // 16) * 16, 1, 0],  # 4: all full blocks, then the rest
+                      [5, 0, 2, 0], [7, 0, 1, 0], [8, 16, 1, 0]], dtype=np.int32)
+    seq_rows = np.zeros((9, 4), dtype=np.int32)
+    for u, (s0, T, M, _) in enumerate(units):
+        for m in range(M):
+            seq_rows[s0 + m, :2] = [u, m]
+    rows_d = torch.from_numpy(units).cuda()
+    sr_d = torch.from_numpy(seq_rows).cuda()
+    for ps in (0, 32, 128):
+        out = out_host(_rows_decode(g, rows_d, sr_d, ps))
+        assert np.abs(out - ref).max() <= TOL[kv_dtype], ps
