@@ -125,6 +125,17 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     # the batch's block tables and lengths stay on the device: uploaded once here, then each
     # step's append writes the new tokens and updates them in the same launch
     from paged_kv_cache_104_amd.engine import DecodeBatch
+    st = cache.bm.stats()
+    shared = st["logical_blocks"] > st["physical_blocks"]
+    use_rows = shared and rows_mode != "off"
+    if use_rows:
+        # a serving batch's order is free: sequences that share leading blocks go next to
+        # each other, so that the shared-prefix units can group them
+        t_h, l_h = cache.bm.block_tables(seqs, max_blocks)
+        order = pkv.prefix_order(t_h, l_h, B)
+        seqs = [seqs[i] for i in order]
+        idx = torch.from_numpy(order.astype(np.int64)).to(dev)
+        q, k_new, v_new = q[idx].contiguous(), k_new[idx].contiguous(), v_new[idx].contiguous()
     batch = DecodeBatch(cache, seqs, max_blocks)
     out = torch.empty_like(q)
     ws_bytes = pkv.decode_workspace_bytes(S, wl.num_q_heads, wl.head_dim, max_ctx, partition_size)
@@ -138,11 +149,8 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     for e in [x for row in ev for x in row]:
         e.record(stream)
     torch.cuda.synchronize()
-    st = cache.bm.stats()
-    shared = st["logical_blocks"] > st["physical_blocks"]
     # forked samples share blocks: read them once for all sharers (shared-prefix units), or
     # per sequence with the shared blocks kept cached
-    use_rows = shared and rows_mode != "off"
     if use_rows:
         rows_d, seq_rows_d = batch.shared_prefix_rows(wl.group, 1)
         n_rows = int(rows_d.shape[0])

@@ -304,6 +304,18 @@ int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, int32_t num_
                         int32_t max_blocks, int32_t block_size, int32_t group,
                         int32_t min_shared_blocks, int32_t* rows, int32_t* seq_rows);
 
+/* A batch order that makes sharers consecutive, for batches whose sharers are
+ * interleaved: order[k] = the batch index of the sequence that goes k-th.
+ * Sequences are sorted by the block ids of their full blocks before their last
+ * token, compared lexicographically (equal ones keep their batch order), so
+ * every run of shared leading blocks is one contiguous range.  Reordering the
+ * batch (q rows, tables, lengths, and reading the outputs back in that order)
+ * is the caller's.
+ *   tables, lens as pkv_prefix_rows; order host int32 [num_seqs] out
+ * Returns PKV_OK or a negative pkv_status. */
+int32_t pkv_prefix_order(const int32_t* tables, const int32_t* lens, int32_t num_seqs,
+                         int32_t max_blocks, int32_t block_size, int32_t* order);
+
 /* Workspace bytes of pkv_paged_attn_decode_rows for num_rows units (0 on
  * invalid arguments): a header, one record per (unit, KV head) and the
  * persistent workers' partial-segment slots (two of 16 rows each). */

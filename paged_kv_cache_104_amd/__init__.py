@@ -72,6 +72,7 @@ _SIGNATURES = {
     "pkv_paged_attn_merge": (ctypes.c_int, [_i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _vp, _sz, _vp, _vp]),
     "pkv_prefix_rows": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pkv_prefix_order": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32]),
     "pkv_rows_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32]),
     "pkv_paged_attn_decode_rows": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
                                                   _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
@@ -449,6 +450,19 @@ def prefix_rows(tables: np.ndarray, lens: np.ndarray, block_size: int, group: in
                                 rows.ctypes.data_as(_pi32), seq_rows.ctypes.data_as(_pi32)))
     _check(min(n, 0))
     return rows[:n].copy(), seq_rows[:S].copy()
+
+
+def prefix_order(tables: np.ndarray, lens: np.ndarray, block_size: int) -> np.ndarray:
+    """Batch order (host int32 [S]) that puts sequences sharing leading blocks next to
+    each other; order[k] is the batch index of the k-th sequence."""
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    S = int(t.shape[0])
+    order = np.zeros(max(1, S), dtype=np.int32)
+    _check(lib.pkv_prefix_order(t.ctypes.data_as(_pi32), ln.ctypes.data_as(_pi32), S,
+                                int(t.shape[1]) if t.ndim == 2 else 0, int(block_size),
+                                order.ctypes.data_as(_pi32)))
+    return order[:S].copy()
 
 
 def rows_workspace_bytes(desc: CacheDesc, num_rows: int) -> int:

@@ -13,6 +13,7 @@
 // any other sequence is a unit of its own {seq, 0, 1, 0}.
 #include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -76,4 +77,33 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
     }
   }
   return nr;
+}
+
+// A batch order that puts sharers next to each other: sequences sorted by the
+// block ids of their shareable blocks, compared as sequences (lexicographic,
+// a shorter run of ids first when it is the other's start), equal ones in
+// batch order.  Sequences with a common run of leading blocks then form one
+// contiguous range, which pkv_prefix_rows can group.
+extern "C" int32_t pkv_prefix_order(const int32_t* tables, const int32_t* lens, int32_t num_seqs,
+                                    int32_t max_blocks, int32_t block_size, int32_t* order) {
+  clear_error();
+  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0)
+    return fail(PKV_E_INVAL, "bad sizes (num_seqs %d, max_blocks %d, block_size %d)", num_seqs,
+                max_blocks, block_size);
+  if (num_seqs > 0 && (!tables || !lens || !order)) return fail(PKV_E_INVAL, "NULL pointer");
+  std::vector<int> n(num_seqs);
+  for (int i = 0; i < num_seqs; ++i) {
+    const int64_t full = lens[i] > 0 ? (int64_t(lens[i]) - 1) / block_size : 0;
+    const int32_t* row = tables + int64_t(i) * max_blocks;
+    int k = 0;
+    while (k < std::min<int64_t>(full, max_blocks) && row[k] >= 0) ++k;
+    n[i] = k;
+    order[i] = i;
+  }
+  std::stable_sort(order, order + num_seqs, [&](int32_t a, int32_t b) {
+    const int32_t* ra = tables + int64_t(a) * max_blocks;
+    const int32_t* rb = tables + int64_t(b) * max_blocks;
+    return std::lexicographical_compare(ra, ra + n[a], rb, rb + n[b]);
+  });
+  return PKV_OK;
 }

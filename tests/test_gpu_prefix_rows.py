@@ -109,6 +109,34 @@ def test_interleaved_families_are_not_grouped():
     assert np.abs(out_host(out) - ref).max() <= TOL["bf16"]
 
 
+def test_interleaved_families_regrouped_by_prefix_order():
+    """The same interleaved batch, put in the library's prefix order: the families become
+    consecutive, form units, and every sequence's output is the oracle's."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = _shared_prefix_small(413, prompts=3, n=4, prefix=150, D=128, Hkv=2, g=4)
+    g = GpuState(wl)
+    inter = np.array([0, 4, 8, 1, 5, 9, 2, 6, 10, 3, 7, 11])
+    t = g.tables.cpu().numpy()[inter]
+    ln = g.lens.cpu().numpy()[inter]
+    assert (pkv.prefix_rows(t, ln, wl.block_size, 4, 1)[0][:, 2] == 1).all()
+    order = inter[pkv.prefix_order(t, ln, wl.block_size)]
+    rows, seq_rows = pkv.prefix_rows(g.tables.cpu().numpy()[order], g.lens.cpu().numpy()[order],
+                                     wl.block_size, 4, 1)
+    assert len(rows) == 3 and (rows[:, 2] == 4).all()
+    ref = oracle_decode(oracle_run(wl))[order]
+    idx = torch.from_numpy(order).cuda()
+    q = g.q[idx].contiguous()
+    out = torch.empty_like(q)
+    pkv.paged_attn_decode_rows(q, g.cache.k_pool, g.cache.v_pool, g.tables[idx].contiguous(),
+                               g.lens[idx].contiguous(), wl.scale, out, g.desc,
+                               wl.max_context_len, 0, torch.from_numpy(rows).cuda(),
+                               torch.from_numpy(seq_rows).cuda())
+    torch.cuda.synchronize()
+    assert np.abs(out_host(out) - ref).max() <= TOL["bf16"]
+
+
 def test_split_phases_equal_the_single_call():
     import paged_kv_cache_104_amd as pkv
 
