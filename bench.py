@@ -140,12 +140,13 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     out = torch.empty_like(q)
     ws_bytes = pkv.decode_workspace_bytes(S, wl.num_q_heads, wl.head_dim, max_ctx, partition_size)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
-    # Every event_every-th timed step records one event pair, around the decode
-    # kernel: an event record keeps the device idle for about 6 us, which the other
-    # timed steps do not pay.  The diagnostic steps after the timed ones also time
-    # the cache write and the merge.  Every event is recorded once here so none is
-    # created inside the timed loop.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    # Every event_every-th timed step times its decode kernel: the launch itself records
+    # the kernel's start and end in an event pair (pkv_time_next_decode), so the pair
+    # holds the kernel alone; separate event records around it would add the idle time
+    # they leave on the device (about 6 us each).  The diagnostic steps after the timed
+    # ones also time the cache write and the merge.  Every event is recorded once here
+    # so none is created inside the timed loop.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
     for e in [x for row in ev for x in row]:
         e.record(stream)
     torch.cuda.synchronize()
@@ -174,10 +175,12 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         if all_events:
             e[0].record(stream)
         _, pairs = batch.append(k_new, v_new)      # block manager, copies, write + tables
+        if all_events:
+            e[4].record(stream)
         n_pairs += len(pairs)
         kv_bytes[i] = float(batch.host_lens.sum()) * bytes_per_token
         if sampled(i):
-            e[1].record(stream)
+            pkv.time_next_decode(e[1], e[2])       # the decode kernel's own start and end
         if use_rows:
             pkv.paged_attn_decode_rows(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                        wl.scale, out, desc, max_ctx, partition_size, rows_d,
@@ -185,8 +188,6 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         else:
             pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                     wl.scale, out, desc, max_ctx, partition_size, workspace, impl)
-        if sampled(i):
-            e[2].record(stream)
         if use_rows:
             pkv.paged_attn_decode_rows(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                        wl.scale, out, desc, max_ctx, partition_size, rows_d,
@@ -217,7 +218,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     timed_ev = [i for i in timed if sampled(i)]
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed_ev]) * 1e-3
     kv_attn = kv_bytes[timed_ev]
-    t_write = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in diag]) * 1e-3
+    t_write = np.array([ev[i][0].elapsed_time(ev[i][4]) for i in diag]) * 1e-3
     t_merge = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in diag]) * 1e-3
     t_attn_diag = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in diag]) * 1e-3
     kvb = kv_bytes[warmup:warmup + steps]
@@ -425,6 +426,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 vector, 2 mfma")
     ap.add_argument("--workers", type=int, default=16)
+    ap.add_argument("--event-every", type=int, default=EVENT_EVERY,
+                    help="time the decode kernel of every n-th timed step")
     ap.add_argument("--rows", choices=("auto", "off"), default="auto",
                     help="shared-prefix (unit) decode for batches whose sequences share blocks "
                          "(auto), or the per-sequence decode (off)")
@@ -462,7 +465,8 @@ def main() -> int:
         return 0
     wl.cache_sequences = True          # keep the drawn inputs for the oracle's sample
     ps = wl.partition_size if args.partition_size is None else args.partition_size
-    r = run_gpu(wl, args.steps, args.warmup, ps, args.impl, args.workers, rows_mode=args.rows)
+    r = run_gpu(wl, args.steps, args.warmup, ps, args.impl, args.workers,
+                event_every=max(1, args.event_every), rows_mode=args.rows)
     wall = r["wall"]
     total_bytes = float(r["kv_bytes"].sum())
     value = total_bytes / wall / 1e9

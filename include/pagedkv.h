@@ -268,6 +268,15 @@ int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t n
                          int32_t max_context_len, int32_t partition_size, const void* workspace,
                          size_t workspace_bytes, void* out, void* stream);
 
+/* Timing hook for benchmarks: the calling thread's next decode-kernel launch
+ * (the first phase of any decode entry point on this thread) records its own
+ * start and end in these events, through hipExtLaunchKernel, so that their
+ * elapsed time is the kernel's alone, without the idle time that separate
+ * event records leave around it.  Both events are the caller's hipEvent_t,
+ * created with timing enabled; (NULL, NULL) cancels.  Returns PKV_OK, or
+ * PKV_E_INVAL when only one event is given. */
+int pkv_time_next_decode(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------------ shared-prefix decode
  *
  * Sequences forked from one prompt point their block tables at the same

@@ -73,6 +73,7 @@ _SIGNATURES = {
                                             _vp, _sz, _vp, _vp]),
     "pkv_prefix_rows": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
     "pkv_prefix_order": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32]),
+    "pkv_time_next_decode": (ctypes.c_int, [_vp, _vp]),
     "pkv_rows_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32]),
     "pkv_paged_attn_decode_rows": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
                                                   _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
@@ -450,6 +451,13 @@ def prefix_rows(tables: np.ndarray, lens: np.ndarray, block_size: int, group: in
                                 rows.ctypes.data_as(_pi32), seq_rows.ctypes.data_as(_pi32)))
     _check(min(n, 0))
     return rows[:n].copy(), seq_rows[:S].copy()
+
+
+def time_next_decode(start=None, stop=None):
+    """The calling thread's next decode kernel records its own start and end in these
+    torch.cuda.Event objects (created beforehand, timing enabled); no arguments cancels."""
+    _check(lib.pkv_time_next_decode(ctypes.c_void_p(start.cuda_event if start else 0),
+                                    ctypes.c_void_p(stop.cuda_event if stop else 0)))
 
 
 def prefix_order(tables: np.ndarray, lens: np.ndarray, block_size: int) -> np.ndarray:

@@ -23,6 +23,7 @@
 //  * decode_vector_kernel (any pool dtype): a plain, fp32-arithmetic kernel
 //    with LDS staging, one workgroup per (sequence, KV head, partition of
 //    partition_size tokens); the f32 path and a cross-check of the MFMA kernel.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1233,6 +1234,24 @@ static int launch(K kernel, dim3 grid, dim3 block, hipStream_t s, const DecodeAr
   return PKV_OK;
 }
 
+// Events that the calling thread's next decode kernel records its start and end
+// in (pkv_time_next_decode); that launch clears them.
+static thread_local hipEvent_t t_time_start = nullptr, t_time_stop = nullptr;
+
+// A decode kernel's launch: through hipExtLaunchKernel when timing events are
+// set, so that the events hold the kernel's own start and end.
+template <typename K, typename... Extra>
+static int launch_decode(K kernel, dim3 grid, dim3 block, hipStream_t s, const DecodeArgs& a,
+                         Extra... extra) {
+  if (!t_time_start) return launch(kernel, grid, block, s, a, "decode", extra...);
+  hipEvent_t t0 = t_time_start, t1 = t_time_stop;
+  t_time_start = t_time_stop = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, a, extra...);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_E_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 // Workers that fit on the current device at once for a one-wave kernel.
 template <typename K>
 static int64_t resident_workers(K kernel) {
@@ -1263,11 +1282,11 @@ static int dispatch_vector(const DecodeArgs& a, int kv, int qd, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads * a.max_parts));
   const dim3 block(kVecThreads);
   if (kv == PKV_F32 && qd == PKV_F32)
-    return launch(decode_vector_kernel<KV_F32, float, D, BS>, grid, block, s, a, "decode");
+    return launch_decode(decode_vector_kernel<KV_F32, float, D, BS>, grid, block, s, a);
   if (kv == PKV_BF16 && qd == PKV_BF16)
-    return launch(decode_vector_kernel<KV_BF16, uint16_t, D, BS>, grid, block, s, a, "decode");
+    return launch_decode(decode_vector_kernel<KV_BF16, uint16_t, D, BS>, grid, block, s, a);
   if (kv == PKV_FP8_E4M3 && qd == PKV_BF16)
-    return launch(decode_vector_kernel<KV_FP8, uint16_t, D, BS>, grid, block, s, a, "decode");
+    return launch_decode(decode_vector_kernel<KV_FP8, uint16_t, D, BS>, grid, block, s, a);
   return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(qd), dtype_name(kv));
 }
 
@@ -1276,8 +1295,8 @@ static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
   auto kernel = decode_mfma_kernel<KV, D, BS, NT, ROWS>;
   DecodeArgs a = a0;
   a.workers = int32_t(std::min<int64_t>(kMaxWorkers, resident_workers(kernel)));
-  return launch(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a, "decode",
-                a.context_lens, a.block_tables, a.rows);
+  return launch_decode(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a,
+                       a.context_lens, a.block_tables, a.rows);
 }
 
 // The shared-prefix decode reads each shared block once, so it always streams.
@@ -1547,6 +1566,15 @@ extern "C" int pkv_paged_attn_decode(const void* q, int32_t q_dtype, const void*
                                   context_lens, num_seqs, num_q_heads, scale, out, max_context_len,
                                   partition_size, workspace, workspace_bytes, stream,
                                   PKV_IMPL_AUTO);
+}
+
+extern "C" int pkv_time_next_decode(void* start_event, void* stop_event) {
+  clear_error();
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PKV_E_INVAL, "give both events or neither");
+  t_time_start = static_cast<hipEvent_t>(start_event);
+  t_time_stop = static_cast<hipEvent_t>(stop_event);
+  return PKV_OK;
 }
 
 extern "C" size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows) {

@@ -124,3 +124,12 @@ def test_host_pair_check():
     for bad in ([[1, 1]], [[1, 2], [3, 2]], [[1, 2], [2, 3]], [[1, 8]], [[-1, 0]]):
         with pytest.raises(ValueError):
             pkv.check_pairs(np.array(bad), 8)
+
+
+def test_timing_hook_validation():
+    import paged_kv_cache_104_amd as pkv
+
+    L = pkv.lib
+    assert L.pkv_time_next_decode(None, None) == 0
+    assert L.pkv_time_next_decode(16, None) == pkv.PKV_E_INVAL
+    assert L.pkv_time_next_decode(None, 16) == pkv.PKV_E_INVAL

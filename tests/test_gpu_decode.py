@@ -300,3 +300,29 @@ def test_many_pairs_per_worker(case):
         out = out_host(g.decode(ps, IMPLS["mfma"]))
         err = np.abs(out - ref).max()
         assert err <= tol, (ps, err)
+
+
+@pytest.mark.parametrize("impl", [1, 2])
+def test_timing_events_hold_the_kernel(impl):
+    """With the timing hook the decode launch records its own start and end: the pair's
+    elapsed time is positive and bounded, the output is unchanged, and the hook applies to
+    one launch only."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = workloads.random_small(60, S=16, Hq=8, Hkv=2, D=128, B=16, max_ctx=2000,
+                                kv_dtype="bf16", in_dtype="bf16")
+    g = GpuState(wl)
+    ref = g.decode(0, impl)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for x in e:
+        x.record()
+    torch.cuda.synchronize()
+    pkv.time_next_decode(e[0], e[1])
+    out = g.decode(0, impl)
+    ms = e[0].elapsed_time(e[1])
+    assert 0 < ms < 1000
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    out2 = g.decode(0, impl)                 # no events this time
+    assert e[0].elapsed_time(e[1]) == ms
+    assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
