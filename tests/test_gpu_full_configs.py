@@ -96,3 +96,29 @@ def test_full_config(name):
     print(f"config {name}: sampled rows {rows}, max abs err {err:.3g}", flush=True)
     assert err <= TOL[wl.kv_dtype], err
     assert np.isfinite(out).all()
+
+    # batches whose sequences share blocks: the shared-prefix unit decode as bench.py runs it
+    # (batch put in prefix order, units from the tables), on the same sampled rows, and
+    # within the tolerance of the per-sequence decode on every row
+    st = g.cache.bm.stats()
+    if st["logical_blocks"] > st["physical_blocks"]:
+        import paged_kv_cache_104_amd as pkv
+
+        t_h, l_h = g.tables.cpu().numpy(), g.lens.cpu().numpy()
+        order = pkv.prefix_order(t_h, l_h, wl.block_size)
+        units, seq_rows = pkv.prefix_rows(t_h[order], l_h[order], wl.block_size, wl.group, 1)
+        assert (units[:, 2] > 1).any()
+        idx = torch.from_numpy(order.astype(np.int64)).cuda()
+        ou = torch.empty_like(g.q)
+        pkv.paged_attn_decode_rows(g.q[idx].contiguous(), g.cache.k_pool, g.cache.v_pool,
+                                   g.tables[idx].contiguous(), g.lens[idx].contiguous(), wl.scale,
+                                   ou, g.desc, wl.max_context_len, wl.partition_size,
+                                   torch.from_numpy(units).cuda(),
+                                   torch.from_numpy(seq_rows).cuda())
+        torch.cuda.synchronize()
+        out_u = np.empty_like(out)
+        out_u[order] = out_host(ou)
+        err_u = np.abs(out_u[rows] - ref[rows]).max()
+        print(f"config {name}: {len(units)} units, sampled max abs err {err_u:.3g}", flush=True)
+        assert err_u <= TOL[wl.kv_dtype], err_u
+        assert np.abs(out_u - out).max() <= TOL[wl.kv_dtype]
