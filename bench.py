@@ -258,7 +258,7 @@ def cpu_baseline(wl, seconds: float):
     k_scale, v_scale = wl.kv_scales()
     q = wl.q_input()
     q64 = codec.bf16_to_f64(q) if wl.in_dtype == "bf16" else q.astype(np.float64)
-    done_bytes, done_tokens, spent, n = 0.0, 0, 0.0, 0
+    done_bytes, done_tokens, spent, cpu, n = 0.0, 0, 0.0, 0.0, 0
     for i in range(wl.num_seqs):
         ctx = int(wl.ctx_lens[i])
         nb = -(-ctx // wl.block_size)
@@ -269,10 +269,11 @@ def cpu_baseline(wl, seconds: float):
         ocache.reshape_and_cache(kp, vp, k, v, a.slots(0, 0, ctx), wl.in_dtype, wl.kv_dtype,
                                  k_scale, v_scale)
         tables, lens = a.block_tables([0], nb)
-        t = time.perf_counter()
+        t, c = time.perf_counter(), time.process_time()
         oattn.paged_decode(q64[i:i + 1], kp, vp, tables, lens, wl.scale, wl.kv_dtype,
                            k_scale, v_scale)
         spent += time.perf_counter() - t
+        cpu += time.process_time() - c
         done_bytes += ctx * wl.kv_bytes_per_token()
         done_tokens += 1
         n += 1
@@ -284,7 +285,8 @@ def cpu_baseline(wl, seconds: float):
         "tokens_per_s": done_tokens / spent, "cores": int(threads), "kind": "oracle",
         "sample": f"first {n} of {wl.num_seqs} sequences of {wl.name} "
                   f"({int(sum(wl.ctx_lens[:n]))} cached tokens), decode attention only, "
-                  f"{spent:.1f}s of CPU time, numpy float64 with {threads} BLAS thread(s)",
+                  f"{spent:.1f} s wall ({cpu:.1f} s of CPU time over all threads), numpy "
+                  f"float64 with {threads} BLAS thread(s)",
     }
 
 
