@@ -184,3 +184,40 @@ def test_hand_built_units(kv_dtype, D):
     for ps in (0, 32, 128):
         out = out_host(_rows_decode(g, rows_d, sr_d, ps))
         assert np.abs(out - ref).max() <= TOL[kv_dtype], ps
+
+
+def test_units_with_empty_and_single_token_members():
+    """A unit of three members without shared tokens, one of them empty, and a unit whose
+    members share one block and have one own token each: the empty member gets zeros, a
+    one-token context returns its value row exactly."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    D, B, H = 128, 16, 2
+    desc = pkv.cache_desc(8, H, B, D, "bf16")
+    kp, vp = pkv.alloc_pools(desc)
+    x = torch.randn(5, H, D, device="cuda").to(torch.bfloat16)
+    # blocks 1..3 hold one token each; block 4 holds 16 shared tokens, blocks 5, 6 one each
+    slots = [16, 32, 48] + list(range(64, 80))
+    xs = torch.randn(len(slots), H, D, device="cuda").to(torch.bfloat16)
+    xs[:3] = x[:3]
+    pkv.reshape_and_cache(xs, xs, torch.tensor(slots, device="cuda"), kp, vp, desc)
+    pkv.reshape_and_cache(x[3:], x[3:], torch.tensor([80, 96], device="cuda"), kp, vp, desc)
+    q = torch.randn(5, 4 * H, D, device="cuda").to(torch.bfloat16)
+    tables = torch.tensor([[1, -1], [-1, -1], [3, -1], [4, 5], [4, 6]], dtype=torch.int32,
+                          device="cuda")
+    lens = torch.tensor([1, 0, 1, 17, 17], dtype=torch.int32, device="cuda")
+    units = torch.tensor([[0, 0, 3, 0], [3, 16, 2, 0]], dtype=torch.int32, device="cuda")
+    seq_rows = torch.tensor([[0, 0, 0, 0], [0, 1, 0, 0], [0, 2, 0, 0], [1, 0, 0, 0],
+                             [1, 1, 0, 0]], dtype=torch.int32, device="cuda")
+    ref = torch.empty_like(q)
+    pkv.paged_attn_decode(q, kp, vp, tables, lens, 0.1, ref, desc, 32, 0, impl=2)
+    for ps in (0, 32):
+        out = torch.full_like(q, 7.0)
+        pkv.paged_attn_decode_rows(q, kp, vp, tables, lens, 0.1, out, desc, 32, ps, units,
+                                   seq_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(out[1].float(), torch.zeros_like(out[1].float()))
+        for s in (0, 2):
+            assert torch.equal(out[s].float(), x[s].float().repeat_interleave(4, dim=0))
+        assert (out[3:].float() - ref[3:].float()).abs().max().item() <= TOL["bf16"]
