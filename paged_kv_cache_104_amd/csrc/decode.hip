@@ -593,6 +593,30 @@ __device__ __forceinline__ void next_span(Cursor& cu, const DecodeArgs& a,
   } while (cu.x >= cu.xe);
 }
 
+// The unit fields and the span of pair step cu.x, from the unit's descriptor
+// and its members' lengths (len[m] of sequence d.x + m).
+__device__ __forceinline__ void walk_unit(Cursor& cu, const DecodeArgs& a, int4 d,
+                                          const int (&len)[kMaxGroup]) {
+  unit_of(a, d, len[0], cu.seq0, cu.M, cu.T);
+  cu.sub = -1;
+  cu.seq = cu.seq0;
+  cu.tb = 0;
+  cu.ctx = cu.T;
+  cu.x0 = 0;
+  cu.xe = ctx_steps(cu.T);
+#pragma unroll
+  for (int m = 0; m < kMaxGroup; ++m) {
+    if (m < cu.M && cu.x >= cu.xe) {
+      cu.sub = m;
+      cu.seq = cu.seq0 + m;
+      cu.tb = cu.T;
+      cu.ctx = max(0, clamp_ctx(len[m], a.max_ctx) - cu.T);
+      cu.x0 = cu.xe;
+      cu.xe += ctx_steps(cu.ctx);
+    }
+  }
+}
+
 // The cursor at step x of the pair of unit s, KV head kvh (fields s, kvh, x,
 // P, n already set).
 template <bool ROWS>
@@ -607,24 +631,7 @@ __device__ __forceinline__ void enter_unit(Cursor& cu, const DecodeArgs& a,
     int len[kMaxGroup];
 #pragma unroll
     for (int m = 0; m < kMaxGroup; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
-    unit_of(a, d, len[0], cu.seq0, cu.M, cu.T);
-    cu.sub = -1;
-    cu.seq = cu.seq0;
-    cu.tb = 0;
-    cu.ctx = cu.T;
-    cu.x0 = 0;
-    cu.xe = ctx_steps(cu.T);
-#pragma unroll
-    for (int m = 0; m < kMaxGroup; ++m) {
-      if (m < cu.M && cu.x >= cu.xe) {
-        cu.sub = m;
-        cu.seq = cu.seq0 + m;
-        cu.tb = cu.T;
-        cu.ctx = max(0, clamp_ctx(len[m], a.max_ctx) - cu.T);
-        cu.x0 = cu.xe;
-        cu.xe += ctx_steps(cu.ctx);
-      }
-    }
+    walk_unit(cu, a, d, len);
   } else {
     cu.seq0 = cu.seq = cu.s;
     cu.M = 1;
@@ -706,7 +713,28 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
   const int S = ROWS ? a.num_rows : a.num_seqs, hkv = a.num_kv_heads;
   int sum = 0;
   int v[4];   // steps of the units of the last chunk (all of them when S <= 256)
-  for (int s0 = 0; s0 < S; s0 += 256) {
+  // Shared-prefix decode with at most 64 units: lane i's unit and its members'
+  // lengths stay in registers, and the worker's cursor is read from the lane
+  // that holds its unit instead of loading them again.
+  int4 dk = make_int4(0, 0, 0, 0);
+  int lk[kMaxGroup];
+  const bool few = ROWS && S <= 64;
+  if (few) {
+    dk = rows[min(lane, S - 1)];
+    const int first = row_seq(a, dk);
+#pragma unroll
+    for (int m = 0; m < kMaxGroup; ++m) lk[m] = lens[min(first + m, a.num_seqs - 1)];
+    int seq0, M, T;
+    unit_of(a, dk, lk[0], seq0, M, T);
+    int n = ctx_steps(T);
+#pragma unroll
+    for (int m = 0; m < kMaxGroup; ++m)
+      n += m < M ? ctx_steps(max(0, clamp_ctx(lk[m], a.max_ctx) - T)) : 0;
+    v[0] = lane < S ? n : 0;
+    v[1] = v[2] = v[3] = 0;
+    sum = v[0];
+  }
+  for (int s0 = 0; s0 < (few ? 0 : S); s0 += 256) {
     // every load of the chunk is requested before any is used
     if constexpr (ROWS) {
       int4 d[4];
@@ -749,7 +777,18 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
       cu.x = target - first - cu.kvh * ns;
       cu.n = ns;
       cu.P = first + cu.kvh * ns;
-      enter_unit<ROWS>(cu, a, rows, lens);
+      if (few) {
+        const int4 d = make_int4(__builtin_amdgcn_readlane(dk.x, l),
+                                 __builtin_amdgcn_readlane(dk.y, l),
+                                 __builtin_amdgcn_readlane(dk.z, l),
+                                 __builtin_amdgcn_readlane(dk.w, l));
+        int len[kMaxGroup];
+#pragma unroll
+        for (int m = 0; m < kMaxGroup; ++m) len[m] = __builtin_amdgcn_readlane(lk[m], l);
+        walk_unit(cu, a, d, len);
+      } else {
+        enter_unit<ROWS>(cu, a, rows, lens);
+      }
       return true;
     }
     base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
