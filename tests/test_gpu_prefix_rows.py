@@ -221,3 +221,21 @@ def test_units_with_empty_and_single_token_members():
         for s in (0, 2):
             assert torch.equal(out[s].float(), x[s].float().repeat_interleave(4, dim=0))
         assert (out[3:].float() - ref[3:].float()).abs().max().item() <= TOL["bf16"]
+
+
+def test_timing_hook_covers_the_unit_decode():
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = _shared_prefix_small(414, prompts=2, n=4, prefix=200, D=128, Hkv=2, g=4)
+    g = GpuState(wl)
+    rows, seq_rows, rows_d, sr_d = _rows(g, 4)
+    ref = _rows_decode(g, rows_d, sr_d, 0)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for x in e:
+        x.record()
+    torch.cuda.synchronize()
+    pkv.time_next_decode(e[0], e[1])
+    out = _rows_decode(g, rows_d, sr_d, 0)
+    assert 0 < e[0].elapsed_time(e[1]) < 1000
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
