@@ -99,6 +99,35 @@ constexpr int kVecThreads = 256;
 constexpr int kVecChunk = 256;  // tokens per LDS chunk
 constexpr int kMaxGroup = 16;
 
+// Four consecutive pool elements as floats, with one 16-, 8- or 4-byte load (p is
+// 4-element aligned; fp8 without its scale).
+template <int KV>
+__device__ __forceinline__ float4 load4_f32(const typename KvTraits<KV>::T* p) {
+  if constexpr (KV == KV_F32) {
+    return *reinterpret_cast<const float4*>(p);
+  } else if constexpr (KV == KV_BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                       bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+  } else {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    return make_float4(e4m3_to_f32(u & 0xffu), e4m3_to_f32((u >> 8) & 0xffu),
+                       e4m3_to_f32((u >> 16) & 0xffu), e4m3_to_f32(u >> 24));
+  }
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <int KV, typename QT, int D, int BS>
 __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a) {
   typedef typename KvTraits<KV>::T T;
@@ -159,11 +188,17 @@ __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a
       if (ok) {
         const T* krow = kp + (int64_t(pb) * a.num_kv_heads + kvh) * head_stride +
                         int64_t((cs + tid) % BS) * D;
-        for (int d = 0; d < D; ++d) {
-          const float kv = kv_to_f32<KV>(krow[d]);
+        for (int d = 0; d < D; d += 4) {
+          const float4 kv = load4_f32<KV>(krow + d);
 #pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h)
-            if (h < g) dots[h] = fmaf(q_s[h][d], kv, dots[h]);
+          for (int h = 0; h < kMaxGroup; ++h) {
+            if (h < g) {
+              dots[h] = fmaf(q_s[h][d], kv.x, dots[h]);
+              dots[h] = fmaf(q_s[h][d + 1], kv.y, dots[h]);
+              dots[h] = fmaf(q_s[h][d + 2], kv.z, dots[h]);
+              dots[h] = fmaf(q_s[h][d + 3], kv.w, dots[h]);
+            }
+          }
         }
       }
 #pragma unroll
@@ -171,33 +206,47 @@ __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a
         if (h < g) p_s[h][tid] = ok ? dots[h] * a.qk_scale_log2 : -INFINITY;
     }
     __syncthreads();
-    // running max and weights, one thread per head
-    if (tid < g) {
-      float mx = m_s[tid];
-      for (int i = 0; i < n; ++i) mx = fmaxf(mx, p_s[tid][i]);
-      const float alpha = mx == -INFINITY ? 1.f : exp2f(m_s[tid] - mx);
-      float sum = 0.f;
-      for (int i = 0; i < n; ++i) {
-        const float w = mx == -INFINITY ? 0.f : exp2f(p_s[tid][i] - mx);
-        p_s[tid][i] = w;
-        sum += w;
+    // running max and weights: one wave per head, the chunk's tokens over its lanes
+    {
+      const int wv = tid >> 6, ln = tid & 63;
+      for (int h = wv; h < g; h += kVecThreads / 64) {
+        const float m0 = m_s[h];
+        float lm = -INFINITY;
+        for (int i = ln; i < n; i += 64) lm = fmaxf(lm, p_s[h][i]);
+        const float mx = fmaxf(m0, wave_max_f(lm));
+        const float alpha = mx == -INFINITY ? 1.f : exp2f(m0 - mx);
+        float sum = 0.f;
+        for (int i = ln; i < n; i += 64) {
+          const float w = mx == -INFINITY ? 0.f : exp2f(p_s[h][i] - mx);
+          p_s[h][i] = w;
+          sum += w;
+        }
+        sum = wave_sum_f(sum);
+        if (ln == 0) {
+          l_s[h] = l_s[h] * alpha + sum;
+          m_s[h] = mx;
+          alpha_s[h] = alpha;
+        }
       }
-      l_s[tid] = l_s[tid] * alpha + sum;
-      m_s[tid] = mx;
-      alpha_s[tid] = alpha;
     }
     __syncthreads();
-    // P.V: thread per (head, dimension)
+    // P.V: thread per (head, dimension), four tokens of the dimension's row per load
+    // (cs and i are multiples of 4 and the block size is); a token with weight 0 (masked,
+    // or past the chunk) adds nothing, whatever its slot holds
     for (int idx = tid; idx < g * D; idx += kVecThreads) {
       const int h = idx / D, d = idx % D;
       float acc = acc_s[h][d] * alpha_s[h];
-      for (int i = 0; i < n; ++i) {
-        const float w = p_s[h][i];
+      for (int i = 0; i < n; i += 4) {
         const int pb = blk_s[i / BS];
-        if (w != 0.f && pb >= 0 && pb < a.num_blocks) {
-          const T* vcol = vp + (int64_t(pb) * a.num_kv_heads + kvh) * head_stride +
-                          int64_t(d) * BS + (cs + i) % BS;
-          acc = fmaf(w, kv_to_f32<KV>(*vcol), acc);
+        if (pb >= 0 && pb < a.num_blocks) {
+          const float4 v4 = load4_f32<KV>(vp + (int64_t(pb) * a.num_kv_heads + kvh) * head_stride +
+                                          int64_t(d) * BS + (cs + i) % BS);
+          const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = i + e < n ? p_s[h][i + e] : 0.f;
+            acc = w != 0.f ? fmaf(w, vv[e], acc) : acc;
+          }
         }
       }
       acc_s[h][d] = acc;
