@@ -1141,26 +1141,28 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 // thread runs the merge as one online pass over its pieces, loading a
 // piece's (max, sum) and its partial row together, so a workgroup waits for
 // memory twice: for the context length and piece record, then for the pieces.
-// The groups' partial results are combined through LDS.
-// 256 threads, or 512 for batches of few pairs (long contexts, many pieces each).
+// The groups' partial results are combined through LDS.  Batches of few pairs
+// (long contexts, many pieces each) get a workgroup per (pair, query head).
 constexpr int kMergeThreads = 256;
-constexpr int kMergeFewPairs = 512;
 constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
-template <typename QT, int D, int NT, bool ROWS>
+template <typename QT, int D, int NT, bool ROWS, bool SPLIT>
 __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   constexpr int kMergeThreads = NT;
   __shared__ float4 part_o[kMergeThreads];
   __shared__ float part_m[kMergeThreads], part_l[kMergeThreads];
-  const int pair = blockIdx.x;                       // s * Hkv + kvh
-  const int s = pair / a.num_kv_heads, kvh = pair - s * a.num_kv_heads;
   const int g = a.group;
-  const int nchunks = g * D / 4;                     // float4 chunks of the pair's g rows
+  // SPLIT: one workgroup per (pair, query head) instead of per pair
+  const int hs = SPLIT ? int(blockIdx.x) % g : 0;
+  const int pair = SPLIT ? int(blockIdx.x) / g : int(blockIdx.x);   // s * Hkv + kvh
+  const int s = pair / a.num_kv_heads, kvh = pair - s * a.num_kv_heads;
+  const int gw = SPLIT ? 1 : g;                      // query heads this workgroup merges
+  const int nchunks = gw * D / 4;                    // float4 chunks of those rows
   const int tid = threadIdx.x;
   const int ctx = max(0, min(a.context_lens[s], a.max_ctx));
-  QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + int64_t(kvh) * g) * D;
+  QT* out = static_cast<QT*>(a.out) + (int64_t(s) * a.num_q_heads + int64_t(kvh) * g + hs) * D;
   if (ctx == 0) {
-    for (int e = tid; e < g * D; e += kMergeThreads) store_out(out + e, 0.f);
+    for (int e = tid; e < gw * D; e += kMergeThreads) store_out(out + e, 0.f);
     return;
   }
   // piece k of head hg is row first(hg) + k * stride (+ fix for k > 0)
@@ -1198,6 +1200,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
     }
     if (count <= 1) return;                          // written directly by the decode kernel
   }
+  first0 += hs * head_step;
   const int groups = nchunks >= kMergeThreads ? 1 : kMergeThreads / nchunks;
   const int pg = tid / min(nchunks, kMergeThreads);  // piece group of this thread
   const int c0 = tid - pg * min(nchunks, kMergeThreads);
@@ -1531,33 +1534,35 @@ static int launch_partials(const DecodeArgs& a0, const pkv_cache_desc* c, int32_
              : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, mfma, shared, false, s);
 }
 
-template <int NT, bool ROWS>
+template <bool ROWS, bool SPLIT>
 static int launch_merge_nt(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s) {
-  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads));
+  constexpr int NT = kMergeThreads;
+  const dim3 mgrid(static_cast<unsigned>(int64_t(a.num_seqs) * a.num_kv_heads *
+                                         (SPLIT ? a.group : 1)));
   const dim3 block(NT);
   if (ROWS)  // bf16 q / out only (the matrix-core kernel)
     return head_dim == 64
-               ? launch(merge_kernel<uint16_t, 64, NT, true>, mgrid, block, s, a, "merge")
-               : launch(merge_kernel<uint16_t, 128, NT, true>, mgrid, block, s, a, "merge");
+               ? launch(merge_kernel<uint16_t, 64, NT, true, SPLIT>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 128, NT, true, SPLIT>, mgrid, block, s, a, "merge");
   if (head_dim == 64)
     return q_dtype == PKV_F32
-               ? launch(merge_kernel<float, 64, NT, false>, mgrid, block, s, a, "merge")
-               : launch(merge_kernel<uint16_t, 64, NT, false>, mgrid, block, s, a, "merge");
+               ? launch(merge_kernel<float, 64, NT, false, SPLIT>, mgrid, block, s, a, "merge")
+               : launch(merge_kernel<uint16_t, 64, NT, false, SPLIT>, mgrid, block, s, a, "merge");
   return q_dtype == PKV_F32
-             ? launch(merge_kernel<float, 128, NT, false>, mgrid, block, s, a, "merge")
-             : launch(merge_kernel<uint16_t, 128, NT, false>, mgrid, block, s, a, "merge");
+             ? launch(merge_kernel<float, 128, NT, false, SPLIT>, mgrid, block, s, a, "merge")
+             : launch(merge_kernel<uint16_t, 128, NT, false, SPLIT>, mgrid, block, s, a, "merge");
 }
 
 // A batch of few (sequence, KV head) pairs has long contexts in many pieces each:
-// wider workgroups split those pieces into more groups.
+// a workgroup per (pair, query head) splits those pieces into more groups.
 static int launch_merge(const DecodeArgs& a, int32_t head_dim, int32_t q_dtype, hipStream_t s,
                         bool rows = false) {
   const bool few = int64_t(a.num_seqs) * a.num_kv_heads < 256;
   if (rows)
-    return few ? launch_merge_nt<kMergeFewPairs, true>(a, head_dim, q_dtype, s)
-               : launch_merge_nt<kMergeThreads, true>(a, head_dim, q_dtype, s);
-  return few ? launch_merge_nt<kMergeFewPairs, false>(a, head_dim, q_dtype, s)
-             : launch_merge_nt<kMergeThreads, false>(a, head_dim, q_dtype, s);
+    return few ? launch_merge_nt<true, true>(a, head_dim, q_dtype, s)
+               : launch_merge_nt<true, false>(a, head_dim, q_dtype, s);
+  return few ? launch_merge_nt<false, true>(a, head_dim, q_dtype, s)
+             : launch_merge_nt<false, false>(a, head_dim, q_dtype, s);
 }
 
 extern "C" int pkv_paged_attn_partials(const void* q, int32_t q_dtype, const void* k_pool,
