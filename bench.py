@@ -246,9 +246,10 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
                 unique_ratio=unique_bytes / float(kvb[-1]))
 
 
-def cpu_baseline(wl, seconds: float):
-    """The oracle, as it stands, on a bounded sample of the workload's sequences."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(wl, seconds: float, seconds_one: float = 5.0):
+    """The oracle, as it stands, on a bounded sample of the workload's sequences: with all of
+    its BLAS threads, and (a smaller sample) with one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import allocator as oalloc
     from oracle import attention as oattn
@@ -258,8 +259,22 @@ def cpu_baseline(wl, seconds: float):
     k_scale, v_scale = wl.kv_scales()
     q = wl.q_input()
     q64 = codec.bf16_to_f64(q) if wl.in_dtype == "bf16" else q.astype(np.float64)
-    done_bytes, done_tokens, spent, cpu, n = 0.0, 0, 0.0, 0.0, 0
+    # per setting: [wall seconds, KV bytes, sequences]
+    acc = {"all": [0.0, 0.0, 0], "one": [0.0, 0.0, 0]}
+    budget = {"all": seconds, "one": seconds_one}
+
+    def timed(i, kp, vp, tables, lens, key):
+        t = time.perf_counter()
+        oattn.paged_decode(q64[i:i + 1], kp, vp, tables, lens, wl.scale, wl.kv_dtype,
+                           k_scale, v_scale)
+        a_ = acc[key]
+        a_[0] += time.perf_counter() - t
+        a_[1] += int(wl.ctx_lens[i]) * wl.kv_bytes_per_token()
+        a_[2] += 1
+
     for i in range(wl.num_seqs):
+        if all(acc[k][0] >= budget[k] for k in acc):
+            break
         ctx = int(wl.ctx_lens[i])
         nb = -(-ctx // wl.block_size)
         a = oalloc.BlockAllocator(nb, wl.block_size)
@@ -269,24 +284,27 @@ def cpu_baseline(wl, seconds: float):
         ocache.reshape_and_cache(kp, vp, k, v, a.slots(0, 0, ctx), wl.in_dtype, wl.kv_dtype,
                                  k_scale, v_scale)
         tables, lens = a.block_tables([0], nb)
-        t, c = time.perf_counter(), time.process_time()
-        oattn.paged_decode(q64[i:i + 1], kp, vp, tables, lens, wl.scale, wl.kv_dtype,
-                           k_scale, v_scale)
-        spent += time.perf_counter() - t
-        cpu += time.process_time() - c
-        done_bytes += ctx * wl.kv_bytes_per_token()
-        done_tokens += 1
-        n += 1
-        if spent >= seconds:
-            break
+        if acc["all"][0] < budget["all"]:
+            timed(i, kp, vp, tables, lens, "all")
+        if acc["one"][0] < budget["one"]:
+            with threadpool_limits(limits=1):
+                timed(i, kp, vp, tables, lens, "one")
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+    def desc(key, nthreads):
+        wall, nbytes, n = acc[key]
+        return (f"first {n} of {wl.num_seqs} sequences of {wl.name} "
+                f"({int(sum(wl.ctx_lens[:n]))} cached tokens), decode attention only, "
+                f"{wall:.1f} s wall, numpy float64 with {nthreads} BLAS thread(s)")
+
+    wall, nbytes, n = acc["all"]
+    wall1, nbytes1, n1 = acc["one"]
     return {
-        "value": done_bytes / spent / 1e9, "unit": "GB/s",
-        "tokens_per_s": done_tokens / spent, "cores": int(threads), "kind": "oracle",
-        "sample": f"first {n} of {wl.num_seqs} sequences of {wl.name} "
-                  f"({int(sum(wl.ctx_lens[:n]))} cached tokens), decode attention only, "
-                  f"{spent:.1f} s wall ({cpu:.1f} s of CPU time over all threads), numpy "
-                  f"float64 with {threads} BLAS thread(s)",
+        "value": nbytes / wall / 1e9, "unit": "GB/s",
+        "tokens_per_s": n / wall, "cores": int(threads), "kind": "oracle",
+        "sample": desc("all", threads),
+        "one_thread": {"value": nbytes1 / wall1 / 1e9, "unit": "GB/s",
+                       "tokens_per_s": n1 / wall1, "cores": 1, "sample": desc("one", 1)},
     }
 
 
@@ -505,6 +523,8 @@ def main() -> int:
             "reshape_and_cache+copy_blocks": round(float(r["t_write"].mean()) * 1e3, 4),
             "merge": round(float(r["t_merge"].mean()) * 1e3, 4),
             "decode_attention_diag": round(float(r["t_attn_diag"].mean()) * 1e3, 4),
+            "decode_attention_p10_p50_p90": [round(float(np.percentile(r["t_attn"], p)) * 1e3, 4)
+                                             for p in (10, 50, 90)],
         },
         "host_ms_per_step": round(float(r["host_s"].mean()) * 1e3, 4),
         "roofline": {
