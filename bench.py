@@ -23,6 +23,7 @@ import gc
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -38,7 +39,10 @@ DEFAULT_CONFIG = "8b-gqa-bf16"
 DOMINANT_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DIAG_STEPS = 10        # untimed steps after the timed ones, with every kernel bracketed
-EVENT_EVERY = 5        # timed steps between two that bracket the decode kernel with events
+FLUSH_STEPS = 10       # untimed steps after those, each after a read that evicts the KV
+FLUSH_BYTES = 512 << 20
+EVENT_EVERY = 1        # timed steps between two whose decode kernel records its own events
+READ_REF_BYTES = 4 << 30
 
 
 def kernel_source_hash() -> str:
@@ -116,7 +120,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.num_seqs} seqs, "
         f"{int(wl.ctx_lens.sum())} cached tokens, pool {wl.num_blocks} blocks")
     S, B = len(seqs), wl.block_size
-    total = warmup + steps + DIAG_STEPS
+    total = warmup + steps + DIAG_STEPS + FLUSH_STEPS
     max_ctx = wl.max_context_len + total
     max_blocks = -(-max_ctx // B)
     bytes_per_token = wl.kv_bytes_per_token()
@@ -144,8 +148,10 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     # the kernel's start and end in an event pair (pkv_time_next_decode), so the pair
     # holds the kernel alone; separate event records around it would add the idle time
     # they leave on the device (about 6 us each).  The diagnostic steps after the timed
-    # ones also time the cache write and the merge.  Every event is recorded once here
-    # so none is created inside the timed loop.
+    # ones also time the cache write and the merge; the flushed steps after those first
+    # read a 512 MB scratch buffer (untimed), so that no KV line is left in the 256 MB
+    # last-level cache or the L2s when the decode starts.  Every event is recorded once
+    # here so none is created inside the timed loop.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
     for e in [x for row in ev for x in row]:
         e.record(stream)
@@ -164,6 +170,12 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     kv_bytes = np.zeros(total)
     host_s = np.zeros(total)
     n_pairs = 0
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_buf.fill_(1)
+    flush_sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+
+    def flush():
+        pkv.read_probe(flush_buf, 4096, None, FLUSH_BYTES // 4096, flush_sink, 2048)
 
     def sampled(i):
         return i >= warmup + steps or (i - warmup) % event_every == 0
@@ -209,18 +221,25 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for i in range(warmup + steps, total):
+    for i in range(warmup + steps, warmup + steps + DIAG_STEPS):
+        step(i, all_events=True)
+    for i in range(warmup + steps + DIAG_STEPS, total):
+        flush()
         step(i, all_events=True)
     torch.cuda.synchronize()
     gc.enable()
     timed = range(warmup, warmup + steps)
-    diag = range(warmup + steps, total)
+    diag = range(warmup + steps, warmup + steps + DIAG_STEPS)
+    flushed = range(warmup + steps + DIAG_STEPS, total)
     timed_ev = [i for i in timed if sampled(i)]
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in timed_ev]) * 1e-3
     kv_attn = kv_bytes[timed_ev]
     t_write = np.array([ev[i][0].elapsed_time(ev[i][4]) for i in diag]) * 1e-3
     t_merge = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in diag]) * 1e-3
     t_attn_diag = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in diag]) * 1e-3
+    t_attn_flush = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in flushed]) * 1e-3
+    t_merge_flush = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in flushed]) * 1e-3
+    kv_flush = kv_bytes[list(flushed)]
     kvb = kv_bytes[warmup:warmup + steps]
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     # the device tables the steps kept up to date equal the block manager's
@@ -241,6 +260,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
                 t_merge=t_merge,
                 cache_stats=cache_stats,
                 t_attn_diag=t_attn_diag, host_s=host_s[warmup:warmup + steps],
+                t_attn_flush=t_attn_flush, t_merge_flush=t_merge_flush, kv_flush=kv_flush,
                 max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs, shared=shared,
                 rows=use_rows,
                 unique_ratio=unique_bytes / float(kvb[-1]))
@@ -290,6 +310,12 @@ def cpu_baseline(wl, seconds: float, seconds_one: float = 5.0):
             with threadpool_limits(limits=1):
                 timed(i, kp, vp, tables, lens, "one")
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True).stdout.strip())
+    except (OSError, ValueError):
+        nproc = None
+    host = {"nproc": nproc, "sched_getaffinity": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count()}
 
     def desc(key, nthreads):
         wall, nbytes, n = acc[key]
@@ -302,10 +328,43 @@ def cpu_baseline(wl, seconds: float, seconds_one: float = 5.0):
     return {
         "value": nbytes / wall / 1e9, "unit": "GB/s",
         "tokens_per_s": n / wall, "cores": int(threads), "kind": "oracle",
-        "sample": desc("all", threads),
+        "sample": desc("all", threads), "host_cores": host,
         "one_thread": {"value": nbytes1 / wall1 / 1e9, "unit": "GB/s",
                        "tokens_per_s": n1 / wall1, "cores": 1, "sample": desc("one", 1)},
     }
+
+
+def read_reference(tile_bytes: int, total_bytes: int = READ_REF_BYTES, reps: int = 5):
+    """The library's plain read probe over a buffer far larger than the last-level cache:
+    a sequential stream, and tiles of the workload's (block, KV head) tile size read in a
+    random order (as the decode reads its blocks).  Best of a few launch widths, median of
+    ``reps`` launches each (GB/s)."""
+    import torch
+
+    import paged_kv_cache_104_amd as pkv
+
+    buf = torch.empty(total_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    n = total_bytes // tile_bytes
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(0)).to("cuda")
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {}
+    for name, ids in (("sequential", None), ("random_tiles", perm)):
+        best = 0.0
+        for wgs in (1024, 2048, 4096):
+            ts = []
+            for r in range(reps + 1):
+                ev[0].record()
+                pkv.read_probe(buf, tile_bytes, ids, n, sink, wgs)
+                ev[1].record()
+                torch.cuda.synchronize()
+                if r:
+                    ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            best = max(best, n * tile_bytes / float(np.median(ts)) / 1e9)
+        res[name] = round(best, 1)
+    del buf, perm, sink
+    return res
 
 
 def copy_calibration(n_bytes: int, reps: int) -> None:
@@ -453,6 +512,8 @@ def main() -> int:
                          "(auto), or the per-sequence decode (off)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-reference", action="store_true",
+                    help="skip the plain read probe (sequential and random tiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--swap-sweep", type=int, default=0, metavar="BYTES",
                     help="measure swapping rates moving BYTES of K+V each way, then exit")
@@ -525,6 +586,8 @@ def main() -> int:
             "decode_attention_diag": round(float(r["t_attn_diag"].mean()) * 1e3, 4),
             "decode_attention_p10_p50_p90": [round(float(np.percentile(r["t_attn"], p)) * 1e3, 4)
                                              for p in (10, 50, 90)],
+            "decode_attention_flushed": round(float(r["t_attn_flush"].mean()) * 1e3, 4),
+            "merge_flushed": round(float(r["t_merge_flush"].mean()) * 1e3, 4),
         },
         "host_ms_per_step": round(float(r["host_s"].mean()) * 1e3, 4),
         "roofline": {
@@ -539,6 +602,8 @@ def main() -> int:
             "timed_launches": int(len(r["t_attn"])),
         },
     }
+    flush_gbs = float((r["kv_flush"] / r["t_attn_flush"]).mean()) / 1e9
+    result["roofline"]["achieved_flushed"] = round(flush_gbs, 1)
     if r["shared"]:
         # blocks read by several sequences: the HBM roofline is judged on distinct bytes
         ub = attn_gbs * r["unique_ratio"]
@@ -548,6 +613,16 @@ def main() -> int:
         result["roofline"]["frac"] = round(ub / HBM_PEAK_GBS, 4)
         result["roofline"]["algorithmic_bytes_per_launch"] = int(r["kv_attn"].mean()
                                                                  * r["unique_ratio"])
+        result["roofline"]["achieved_flushed"] = round(flush_gbs * r["unique_ratio"], 1)
+    result["roofline"]["frac_flushed"] = round(result["roofline"]["achieved_flushed"]
+                                               / HBM_PEAK_GBS, 4)
+    if not args.no_read_reference:
+        log("timing the read probe")
+        tile = wl.block_size * wl.head_dim * {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+        ref = read_reference(tile)
+        result["roofline"]["read_probe_GBps"] = {"tile_bytes": tile, **ref}
+        result["roofline"]["stream_frac"] = round(result["roofline"]["achieved"]
+                                                  / ref["sequential"], 4)
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -74,7 +74,8 @@ typedef struct {
 
 /*
  * reshape_and_cache -- write new tokens' keys and values into their slots.
- * Glossary code example: key_pool[block_table[pos // B], pos % B] = key.
+ * Ultralytics glossary, "How paging works": position pos of a sequence is row
+ * pos mod B of the block that its table lists at entry pos div B.
  *
  *   k, v          device [num_tokens][H][D] of in_dtype (f32 for an f32 pool;
  *                 bf16 for a bf16 pool; bf16 or f32 for an fp8 pool, encoded
@@ -425,6 +426,31 @@ int pkv_quest_decode(const void* q, int32_t q_dtype, const void* k_pool, const v
                      int32_t num_q_heads, float scale, void* out, int32_t max_context_len,
                      int32_t partition_size, int32_t budget_blocks, void* workspace,
                      size_t workspace_bytes, void* stream, int32_t impl);
+
+/* ------------------------------------------------------------------ measurement aid
+ *
+ * read_probe -- a plain HBM read of num_tiles tiles of tile_bytes bytes each:
+ * the rate a bare read stream reaches on the device, the reference beside the
+ * decode kernel's KV-read rate (the decode reads the pools block by block
+ * through the tables: ithome article, section 3; glossary, "How paging works").
+ *
+ *   buf          device, buf_bytes bytes, 16-byte aligned; only read
+ *   tile_bytes   power of two >= 16 (4096 = one bf16 (block, KV head) tile of the
+ *                key pool at B = 16, D = 128)
+ *   tile_ids     device int64 [num_tiles]: tile i is read at byte offset
+ *                tile_ids[i] * tile_bytes (ids outside the buffer read tile 0);
+ *                NULL reads tiles 0 .. num_tiles - 1 in order (a sequential
+ *                stream; then num_tiles * tile_bytes <= buf_bytes)
+ *   sink         device uint32 [workgroups * 256], 16-byte aligned: one word per
+ *                thread, the XOR of what it read (keeps the loads live)
+ *   workgroups   256-thread workgroups of the launch (the grid strides over
+ *                the tiles; 2048 fills the device eight deep)
+ * Not part of the paged path.  Errors: PKV_E_INVAL for a NULL or misaligned
+ * pointer, a tile size that is no power of two, or a sequential read past
+ * the buffer; PKV_E_HIP if the launch fails.
+ */
+int pkv_read_probe(const void* buf, size_t buf_bytes, int64_t tile_bytes, const int64_t* tile_ids,
+                   int64_t num_tiles, uint32_t* sink, int32_t workgroups, void* stream);
 
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pkv_last_error(void);

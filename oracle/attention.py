@@ -6,9 +6,10 @@ What it follows:
 
 * The attention kernel reads a request's keys and values back block by block
   through its block table, so the cache need not be contiguous (ultralytics
-  glossary "PagedAttention", section "How paging works", and its code example
-  ``key_pool[block_table].reshape(-1, head_dim)[:len(keys)]``; optiverse
-  article, "Block table and non-contiguous allocation").  Paging changes only
+  glossary "PagedAttention", section "How paging works", whose code example
+  reads the keys back by indexing the pool with the whole table, flattening
+  the blocks and keeping the first ctx rows; optiverse article, "Block table
+  and non-contiguous allocation").  Paging changes only
   where the bytes live: the result is plain softmax attention of the query over
   the sequence's cached keys and values.  FlashAttention-style tiling (glossary,
   "Related techniques") reorders the same sum and gives the same result.

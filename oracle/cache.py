@@ -1,8 +1,7 @@
 """Cache operations of the oracle (test infrastructure only).
 
-Pool layout (a convention of this library; the pages show only a key pool
-``key_pool[num_blocks, block_size, head_dim]`` in the ultralytics glossary's
-code example):
+Pool layout (a convention of this library; the ultralytics glossary's code
+example shows only a key pool of shape (blocks, block size, head dim)):
 
 * key pool   ``[num_blocks, num_kv_heads, block_size, head_dim]`` -- a token's
   key for one head is a contiguous row, as in the glossary example;
@@ -13,8 +12,9 @@ code example):
 Storage is fp32 (float32), bf16 (raw uint16 bits) or fp8 (E4M3FN codes, uint8).
 
 ``reshape_and_cache`` writes token i's key and value to the slot
-``slot_mapping[i]``: block ``slot // B``, position ``slot % B`` (glossary code
-example: ``key_pool[block_table[pos // block_size], pos % block_size] = key``).
+``slot_mapping[i]``: block ``slot // B``, position ``slot % B`` (glossary, "How
+paging works": position pos of a sequence is row pos mod B of the block that
+its table lists at entry pos div B).
 A negative slot means "skip this token".  Every other byte of the pools is left
 as it was.
 

@@ -181,6 +181,18 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _on(stream=None):
+    """Context in which a wrapper allocates its temporaries and uploads its arguments: with
+    ``stream`` current, so that the caching allocator ties their memory to that stream (it is
+    not handed out again before the library's work on ``stream`` is done) and the uploads are
+    ordered before that work."""
+    import contextlib
+
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -292,9 +304,10 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, desc: CacheDesc, method: str 
         raise ValueError("duplicate destination")
     args = (_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v))
     if method == "kernel":
-        dev = torch.from_numpy(p).to("cuda")
-        _check(lib.pkv_swap_blocks(*args, _ptr(dev), len(p), ns, nd, ctypes.byref(desc),
-                                   _stream(stream)))
+        with _on(stream):
+            dev = torch.from_numpy(p).to("cuda")
+            _check(lib.pkv_swap_blocks(*args, _ptr(dev), len(p), ns, nd, ctypes.byref(desc),
+                                       _stream(stream)))
     elif method == "dma":
         _check(lib.pkv_swap_blocks_dma(*args, p.ctypes.data, len(p), ns, nd, ctypes.byref(desc),
                                        _stream(stream)))
@@ -362,12 +375,14 @@ def copy_blocks(k_pool, v_pool, pairs, desc: CacheDesc, stream=None) -> None:
         host = check_pairs(host, desc.num_blocks)
         if len(host) == 0:
             return
-        dev = torch.from_numpy(host).to(k_pool.device, non_blocking=False)
+        with _on(stream):
+            dev = torch.from_numpy(host).to(k_pool.device, non_blocking=False)
     n = int(dev.numel() // 2)
     if n == 0:
         return
-    _check(lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(dev), n, ctypes.byref(desc),
-                               _stream(stream)))
+    with _on(stream):
+        _check(lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(dev), n, ctypes.byref(desc),
+                                   _stream(stream)))
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
@@ -395,15 +410,16 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _ptr(workspace) if workspace is not None else 0
-    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
-    _check(lib.pkv_paged_attn_decode_ex(
-        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
-        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
-        float(scale), _ptr(out), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
-        _stream(stream), int(impl)))
+    with _on(stream):
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = _ptr(workspace) if workspace is not None else 0
+        ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+        _check(lib.pkv_paged_attn_decode_ex(
+            _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+            float(scale), _ptr(out), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+            _stream(stream), int(impl)))
     return out
 
 
@@ -491,15 +507,16 @@ def paged_attn_decode_rows(q, k_pool, v_pool, block_tables, context_lens, scale:
     if not (rows.is_contiguous() and seq_rows.is_contiguous()):
         raise ValueError("rows and seq_rows must be contiguous")
     R = int(rows.shape[0])
-    if workspace is None:
-        workspace = torch.empty(rows_workspace_bytes(desc, R), dtype=torch.uint8,
-                                device=q.device)
-    ws_bytes = int(workspace.numel() * workspace.element_size())
-    _check(lib.pkv_paged_attn_decode_rows(
-        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
-        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
-        float(scale), _ptr(out), int(max_context_len), int(partition_size), _ptr(rows), R,
-        _ptr(seq_rows), _ptr(workspace), ws_bytes, _stream(stream), int(phases)))
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(rows_workspace_bytes(desc, R), dtype=torch.uint8,
+                                    device=q.device)
+        ws_bytes = int(workspace.numel() * workspace.element_size())
+        _check(lib.pkv_paged_attn_decode_rows(
+            _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+            float(scale), _ptr(out), int(max_context_len), int(partition_size), _ptr(rows), R,
+            _ptr(seq_rows), _ptr(workspace), ws_bytes, _stream(stream), int(phases)))
     return out
 
 
@@ -538,13 +555,14 @@ def quest_update_blocks(k_pool, meta, blocks, counts, desc: CacheDesc, stream=No
     ks, _ = pool_shapes(desc)
     _check_pool(k_pool, ks, desc, "k_pool")
     _check_meta(meta, desc)
-    b, c = _dev_i32(blocks, k_pool.device), _dev_i32(counts, k_pool.device)
-    if b.numel() != c.numel():
-        raise ValueError("one count per block")
-    if b.numel() == 0:
-        return
-    _check(lib.pkv_quest_update_blocks(_ptr(k_pool), ctypes.byref(desc), _ptr(meta), _ptr(b),
-                                       _ptr(c), int(b.numel()), _stream(stream)))
+    with _on(stream):
+        b, c = _dev_i32(blocks, k_pool.device), _dev_i32(counts, k_pool.device)
+        if b.numel() != c.numel():
+            raise ValueError("one count per block")
+        if b.numel() == 0:
+            return
+        _check(lib.pkv_quest_update_blocks(_ptr(k_pool), ctypes.byref(desc), _ptr(meta),
+                                           _ptr(b), _ptr(c), int(b.numel()), _stream(stream)))
 
 
 def quest_blocks_of_slots(slots, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -616,14 +634,15 @@ def quest_select(q, meta, desc: CacheDesc, block_tables, context_lens, max_conte
         raise ValueError("q must be a contiguous [S, Hq, D] with one table row per sequence")
     H = desc.num_kv_heads
     width = max(1, min(int(block_tables.shape[1]), int(budget_blocks)))
-    sel_t = torch.full((S * H, width), -1, dtype=torch.int32, device=q.device)
-    sel_l = torch.zeros(S * H, dtype=torch.int32, device=q.device)
-    ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, 0, budget_blocks)
-    _check(lib.pkv_quest_select(_ptr(q), dtype_code(q), _ptr(meta), ctypes.byref(desc),
-                                _ptr(block_tables), int(block_tables.shape[1]),
-                                _ptr(context_lens), S, Hq, int(max_context_len),
-                                int(budget_blocks), _ptr(sel_t), _ptr(sel_l), _ptr(ws), wsb,
-                                _stream(stream)))
+    with _on(stream):
+        sel_t = torch.full((S * H, width), -1, dtype=torch.int32, device=q.device)
+        sel_l = torch.zeros(S * H, dtype=torch.int32, device=q.device)
+        ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, 0, budget_blocks)
+        _check(lib.pkv_quest_select(_ptr(q), dtype_code(q), _ptr(meta), ctypes.byref(desc),
+                                    _ptr(block_tables), int(block_tables.shape[1]),
+                                    _ptr(context_lens), S, Hq, int(max_context_len),
+                                    int(budget_blocks), _ptr(sel_t), _ptr(sel_l), _ptr(ws), wsb,
+                                    _stream(stream)))
     return sel_t, sel_l
 
 
@@ -642,14 +661,15 @@ def quest_decode(q, k_pool, v_pool, meta, desc: CacheDesc, block_tables, context
         raise ValueError("q / out shapes or dtypes do not match")
     if not (q.is_contiguous() and out.is_contiguous()) or block_tables.shape[0] != S:
         raise ValueError("q and out must be contiguous, one table row per sequence")
-    ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, partition_size,
-                        budget_blocks)
-    _check(lib.pkv_quest_decode(_ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), _ptr(meta),
-                                ctypes.byref(desc), _ptr(block_tables),
-                                int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
-                                float(scale), _ptr(out), int(max_context_len),
-                                int(partition_size), int(budget_blocks), _ptr(ws), wsb,
-                                _stream(stream), int(impl)))
+    with _on(stream):
+        ws, wsb = _quest_ws(workspace, desc, q, block_tables, max_context_len, partition_size,
+                            budget_blocks)
+        _check(lib.pkv_quest_decode(_ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(meta), ctypes.byref(desc), _ptr(block_tables),
+                                    int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+                                    float(scale), _ptr(out), int(max_context_len),
+                                    int(partition_size), int(budget_blocks), _ptr(ws), wsb,
+                                    _stream(stream), int(impl)))
     return out
 
 
@@ -671,13 +691,17 @@ class BlockManager:
         if not h:
             raise PagedKVError(PKV_E_INVAL, lib.pkv_last_error().decode())
         self._h = ctypes.c_void_p(h)
+        # kept on the instance: at interpreter shutdown the module's globals (lib among
+        # them) may already be gone when __del__ runs
+        self._destroy = lib.pkv_bm_destroy
         self.num_blocks = num_blocks
         self.block_size = block_size
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib.pkv_bm_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     def add_seq(self, seq: int, num_tokens: int) -> None:

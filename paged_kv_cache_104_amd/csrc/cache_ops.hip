@@ -1,8 +1,9 @@
 // Cache operations: the write of new tokens into their (block, slot) and the
 // whole-block copy of copy-on-write.
 //
-// reshape_and_cache follows the ultralytics glossary code example
-// (key_pool[block_table[pos // B], pos % B] = key): slot = block * B + pos.
+// reshape_and_cache follows the ultralytics glossary ("How paging works"): the
+// token at position pos of a sequence lives in row pos mod B of the block its
+// table lists at entry pos div B, i.e. slot = table[pos / B] * B + pos % B.
 // copy_blocks is the copy step of copy-on-write (ithome article 10417389,
 // section 4): the writer's new block receives the whole shared block.
 // swap_blocks moves whole blocks between the device pool and a host pool of

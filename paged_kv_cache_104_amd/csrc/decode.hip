@@ -402,8 +402,11 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
     sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(qv[i]), sa, 0, 0, 0);
     sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, as_bf16x8(qv[i]), sb, 0, 0, 0);
   }
-  // lane (r, c): x[e] = raw score of head c for token 8r + e of the step
-  float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  // lane (r, c): x[e] = score of head c for token 8r + e of the step, in log2
+  // units (scaled first, so the running max below is the max of the scaled
+  // scores whatever the sign of the scale)
+  float x[8] = {sa[0] * sl2, sa[1] * sl2, sa[2] * sl2, sa[3] * sl2,
+                sb[0] * sl2, sb[1] * sl2, sb[2] * sl2, sb[3] * sl2};
   const bool tail = tt + 32 > t1;
   if (tail) {
 #pragma unroll
@@ -419,10 +422,10 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
 #pragma unroll
   for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, x[e]);
   // raise the reference max (and rescale what was summed so far) only when needed
-  if (__builtin_amdgcn_ballot_w64(lmax * sl2 > m + kRescaleLog2)) {
+  if (__builtin_amdgcn_ballot_w64(lmax > m + kRescaleLog2)) {
     float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m, cmax * sl2);
+    const float m_new = fmaxf(m, cmax);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
@@ -432,8 +435,7 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
   uint32_t pw[4];
 #pragma unroll
   for (int e = 0; e < 8; e += 2)
-    pw[e / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[e], sl2, -m)),
-                            __builtin_amdgcn_exp2f(fmaf(x[e + 1], sl2, -m)));
+    pw[e / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(x[e] - m), __builtin_amdgcn_exp2f(x[e + 1] - m));
   const bf16x8_t pb = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
   // invalid tokens have p = 0, but 0 * NaN is NaN: zero their V elements
   uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};

@@ -45,7 +45,7 @@ def check_glossary_example():
     k_pool, v_pool = ocache.new_pools(N, 1, B, D, "f32")
     slots = a.slots(0, 0, g["num_keys"])
     ocache.reshape_and_cache(k_pool, v_pool, keys, keys, slots, "f32", "f32")
-    # the example's own indexing: key_pool[block_table[pos // B], pos % B] == key
+    # position pos sits in row pos mod B of the block listed at table entry pos div B
     for pos in range(g["num_keys"]):
         assert np.array_equal(k_pool[table[pos // B], 0, pos % B], keys[pos, 0])
     gathered = oattn.gather_keys(k_pool, table, g["num_keys"], 0)
@@ -201,16 +201,16 @@ def _sdpa_reference(wl, st):
     for i in range(wl.num_seqs):
         k, v = wl.seq_kv_input(i)
         if wl.kv_dtype == "fp8":
-            kf = codec.bf16_to_f32(k) if wl.in_dtype == "bf16" else k
-            vf = codec.bf16_to_f32(v) if wl.in_dtype == "bf16" else v
-            # torch's own fp8 cast of x / scale; values within range need no saturation
-            kq = (torch.from_numpy(kf) / torch.tensor(st.k_scale, dtype=torch.float32))
-            vq = (torch.from_numpy(vf) / torch.tensor(st.v_scale, dtype=torch.float32))
+            # torch's own widening and fp8 cast of x / scale (within range: no saturation)
+            kf = _torch_bf16(k).to(torch.float32) if wl.in_dtype == "bf16" else torch.from_numpy(k)
+            vf = _torch_bf16(v).to(torch.float32) if wl.in_dtype == "bf16" else torch.from_numpy(v)
+            kq = kf / torch.tensor(st.k_scale, dtype=torch.float32)
+            vq = vf / torch.tensor(st.v_scale, dtype=torch.float32)
             K = kq.to(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(st.k_scale))
             V = vq.to(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(st.v_scale))
         elif wl.in_dtype == "bf16":
-            K = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).to(torch.float64)
-            V = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+            K = _torch_bf16(k).to(torch.float64)
+            V = _torch_bf16(v).to(torch.float64)
         else:
             K = torch.from_numpy(k).to(torch.float64)
             V = torch.from_numpy(v).to(torch.float64)
@@ -353,12 +353,43 @@ def check_gqa_is_repeated_mha():
 
 # ------------------------------------------------------------------ number formats
 
+def _torch_bf16(bits: np.ndarray):
+    """Raw bfloat16 patterns as a torch bfloat16 tensor (a reinterpretation, no arithmetic)."""
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(
+        torch.bfloat16)
+
+
 def check_bf16_widening():
+    """Both widenings of the oracle against torch's bfloat16 casts, on all 65536 patterns:
+    to float64 by value, to float32 bit for bit (torch keeps NaN payloads too)."""
     bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
-    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ref = _torch_bf16(bits).to(torch.float64).numpy()
     got = codec.bf16_to_f64(bits)
     same = (got == ref) | (np.isnan(got) & np.isnan(ref))
     assert same.all()
+    ref32 = _torch_bf16(bits).to(torch.float32).numpy()
+    got32 = codec.bf16_to_f32(bits)
+    assert got32.dtype == np.float32 and got32.shape == bits.shape
+    assert np.array_equal(got32.view(np.uint32), ref32.view(np.uint32))
+
+
+def check_fp8_cache_encode():
+    """The oracle's cache write of bf16 inputs into an fp8 pool (widen, divide by the scale in
+    fp32, round) against torch on every finite bf16 pattern: torch widens, divides and casts to
+    float8_e4m3fn itself.  Scales are chosen so that |x / scale| stays below 464, where torch's
+    cast rounds to nearest-even without overflowing; past that the oracle saturates (a reading
+    torch cannot confirm)."""
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    x32 = _torch_bf16(bits).to(torch.float32)
+    finite = torch.isfinite(x32).numpy()
+    bits, x32 = bits[finite], x32[torch.from_numpy(finite)]
+    amax = float(x32.abs().max())
+    for scale in (np.float32(amax / 448.0), np.float32(amax / 400.0), np.float32(amax / 300.0)):
+        y = x32 / torch.tensor(float(scale), dtype=torch.float32)
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert float(y.abs().max()) < 464.0
+        got = ocache.encode(bits, "bf16", "fp8", float(scale))
+        assert np.array_equal(got, ref), int(np.count_nonzero(got != ref))
 
 
 def check_e4m3_decode():
@@ -413,5 +444,5 @@ ALL = [
     check_attention_vs_sdpa, check_single_token_context, check_identical_keys,
     check_empty_context, check_placement_invariance, check_sharing_invariance,
     check_gqa_is_repeated_mha, check_bf16_widening, check_e4m3_decode, check_e4m3_encode,
-    check_fp8_pool_is_half_of_bf16,
+    check_fp8_cache_encode, check_fp8_pool_is_half_of_bf16,
 ]

@@ -326,3 +326,67 @@ def test_timing_events_hold_the_kernel(impl):
     out2 = g.decode(0, impl)                 # no events this time
     assert e[0].elapsed_time(e[1]) == ms
     assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_negative_and_zero_scale(kv):
+    """The softmax scale is the caller's: a negative scale favours the smallest dot products
+    and a zero scale gives the mean of the values.  Both kernel families against the oracle
+    at the same scale."""
+    from oracle import attention as oattn
+
+    wl = workloads.random_small(330, S=5, Hq=8, Hkv=2, D=128, B=16, max_ctx=900,
+                                kv_dtype=kv, in_dtype="bf16")
+    st = oracle_run(wl)
+    g = GpuState(wl)
+    torch = torch_mod()
+    for scale in (-wl.scale, -3.0 * wl.scale, 0.0):
+        print(f"scale {scale}", flush=True)
+        ref = oattn.paged_decode(st.q64(), st.k_pool, st.v_pool, st.tables, st.ctx, scale,
+                                 wl.kv_dtype, st.k_scale, st.v_scale)
+        for impl in (1, 2):
+            for ps in (0, 64):
+                out = torch.empty_like(g.q)
+                g.cache.decode(g.q, out, g.tables, g.lens, scale, wl.max_context_len, ps,
+                               impl=impl)
+                torch.cuda.synchronize()
+                err = np.abs(out_host(out) - ref).max()
+                assert err <= TOL[kv], (scale, impl, ps, err)
+
+
+def test_side_stream_matches_default_stream():
+    """A decode (and a copy of blocks) launched on a side stream, with the wrapper allocating
+    its workspace and uploading its pairs there, gives the default stream's output."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = workloads.random_small(331, S=6, Hq=8, Hkv=2, D=128, B=16, max_ctx=2500, min_ctx=900,
+                                kv_dtype="bf16", in_dtype="bf16")
+    g = GpuState(wl)
+    ref = g.decode(0, IMPLS["mfma"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(g.q)
+        out.record_stream(side)
+        pkv.paged_attn_decode(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens, wl.scale,
+                              out, g.desc, wl.max_context_len, 0, impl=IMPLS["mfma"],
+                              stream=side)
+        outs.append(out)
+        # the freed workspace must not be handed to this allocation while the decode runs
+        junk = torch.full((1 << 22,), 7, dtype=torch.int32, device="cuda")
+        del junk
+    side.synchronize()
+    for out in outs:
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    # copy_blocks with host pairs uploaded on the side stream
+    k0 = g.cache.k_pool.clone()
+    used = set(g.tables.cpu().numpy().ravel().tolist()) - {-1}
+    free = [b for b in range(wl.num_blocks) if b not in used]
+    src = sorted(used)[:2]
+    pairs = [(src[0], free[0]), (src[1], free[1])]
+    pkv.copy_blocks(g.cache.k_pool, g.cache.v_pool, pairs, g.desc, stream=side)
+    side.synchronize()
+    for s_, d_ in pairs:
+        assert torch.equal(g.cache.k_pool[d_].view(torch.int16), k0[s_].view(torch.int16))

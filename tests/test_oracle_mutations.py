@@ -103,6 +103,20 @@ def _encode_truncate(y):
     return code | (np.signbit(y).astype(np.uint8) << np.uint8(7))
 
 
+def _bf16_to_f32_shift15(bits):
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(15)).view(np.float32)
+
+
+def _bf16_to_f32_by_value(bits):
+    return np.asarray(bits, dtype=np.uint16).astype(np.float32)
+
+
+def _bf16_to_f32_low_half(bits):
+    # the 16 bits placed in the low half of the word (a byte-order / view mistake)
+    return np.asarray(bits, dtype=np.uint16).astype(np.uint32).view(np.float32)
+
+
 class _PopTail(oalloc.BlockAllocator):
     def _pop(self):
         b = self.free.pop()
@@ -187,6 +201,17 @@ MUTATIONS = {
                                           pins.check_cache_write_only_touches_slots]),
     "fp8 decoded with the FNUZ bias": (codec, "E4M3_TABLE", _e4m3_table_fnuz(),
                                        [pins.check_e4m3_decode]),
+    "bf16 widened with a 15-bit shift": (codec, "bf16_to_f32", _bf16_to_f32_shift15,
+                                         [pins.check_bf16_widening, pins.check_fp8_cache_encode,
+                                          pins.check_attention_vs_sdpa]),
+    "bf16 patterns converted as integers": (codec, "bf16_to_f32", _bf16_to_f32_by_value,
+                                            [pins.check_bf16_widening,
+                                             pins.check_fp8_cache_encode,
+                                             pins.check_attention_vs_sdpa]),
+    "bf16 patterns in the low half of the word": (codec, "bf16_to_f32", _bf16_to_f32_low_half,
+                                                  [pins.check_bf16_widening,
+                                                   pins.check_fp8_cache_encode,
+                                                   pins.check_attention_vs_sdpa]),
     "fp8 ties rounded away from zero": (codec, "e4m3_encode_f32", _encode_ties_away,
                                         [pins.check_e4m3_encode]),
     "fp8 truncated": (codec, "e4m3_encode_f32", _encode_truncate, [pins.check_e4m3_encode]),
