@@ -41,7 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DIAG_STEPS = 10        # untimed steps after the timed ones, with every kernel bracketed
 FLUSH_STEPS = 10       # untimed steps after those, each after a read that evicts the KV
 FLUSH_BYTES = 512 << 20
-EVENT_EVERY = 1        # timed steps between two whose decode kernel records its own events
+EVENT_EVERY = 2        # timed steps between two whose decode kernel records its own events
 READ_REF_BYTES = 4 << 30
 
 
@@ -172,7 +172,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     n_pairs = 0
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush_buf.fill_(1)
-    flush_sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    flush_sink = torch.empty(2048 * 64, dtype=torch.int32, device=dev)
 
     def flush():
         pkv.read_probe(flush_buf, 4096, None, FLUSH_BYTES // 4096, flush_sink, 2048)
@@ -347,7 +347,7 @@ def read_reference(tile_bytes: int, total_bytes: int = READ_REF_BYTES, reps: int
     buf.fill_(1)
     n = total_bytes // tile_bytes
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(0)).to("cuda")
-    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    sink = torch.empty(4096 * 64, dtype=torch.int32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     res = {}
     for name, ids in (("sequential", None), ("random_tiles", perm)):

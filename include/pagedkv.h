@@ -384,6 +384,14 @@ int pkv_quest_update_blocks(const void* k_pool, const pkv_cache_desc* c, void* m
                             const int32_t* blocks, const int32_t* counts, int32_t n,
                             void* stream);
 
+/* Blocks touched by a cache write to host slots[0 .. n) (negative slots skipped), for
+ * pkv_quest_update_blocks: the distinct blocks slot / block_size in ascending order, each
+ * with the fill its highest written slot implies (slot % block_size + 1; a block's slots
+ * fill in order).  Writes min(count, cap) entries to blocks / fills (host int32) and
+ * returns the count, or a negative pkv_status (PKV_E_INVAL on bad arguments). */
+int32_t pkv_quest_blocks_of_slots(const int64_t* slots, int64_t n, int32_t block_size,
+                                  int32_t* blocks, int32_t* fills, int32_t cap);
+
 /* The decode step's update, from device-resident tables: for every row, the block
  * holding its last token (context_lens - 1) over its first (context_lens - 1) % B + 1
  * slots.  Rows that share that block must agree on its fill (they do whenever the
@@ -441,10 +449,11 @@ int pkv_quest_decode(const void* q, int32_t q_dtype, const void* k_pool, const v
  *                tile_ids[i] * tile_bytes (ids outside the buffer read tile 0);
  *                NULL reads tiles 0 .. num_tiles - 1 in order (a sequential
  *                stream; then num_tiles * tile_bytes <= buf_bytes)
- *   sink         device uint32 [workgroups * 256], 16-byte aligned: one word per
- *                thread, the XOR of what it read (keeps the loads live)
- *   workgroups   256-thread workgroups of the launch (the grid strides over
- *                the tiles; 2048 fills the device eight deep)
+ *   sink         device uint32 [workgroups * 64], 16-byte aligned: one word per
+ *                lane, the XOR of what it read (keeps the loads live)
+ *   workgroups   one-wave (64-lane) workgroups of the launch; the tiles, in
+ *                list order, are cut into equal contiguous shares, one per wave
+ *                (1024 puts one wave on every SIMD of a 256-CU device)
  * Not part of the paged path.  Errors: PKV_E_INVAL for a NULL or misaligned
  * pointer, a tile size that is no power of two, or a sequential read past
  * the buffer; PKV_E_HIP if the launch fails.
@@ -601,6 +610,15 @@ int pkv_bm_swap_stats(pkv_bm* bm, int64_t* out);
 int32_t pkv_bm_host_refcount(pkv_bm* bm, int32_t block);
 int32_t pkv_bm_host_free_list(pkv_bm* bm, int32_t* out, int32_t cap);
 int pkv_bm_seq_blocks(pkv_bm* bm, int64_t seq, int32_t* out, int32_t cap);
+
+/* The distinct device blocks of sequences seqs[0 .. n) (none swapped out), in order of
+ * first appearance, each with its filled slots: logical block j of a sequence of len
+ * tokens holds min(B, len - j * B) of them, and a block shared by several sequences
+ * takes the largest such count.  This is what the QUEST metadata of those blocks must
+ * cover (pkv_quest_update_blocks).  Writes min(count, cap) entries to blocks / fills and
+ * returns the count; a negative pkv_status on error (unknown or swapped-out sequence). */
+int32_t pkv_bm_block_fills(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* blocks,
+                           int32_t* fills, int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -97,6 +97,7 @@ _SIGNATURES = {
     "pkv_quest_decode": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, ctypes.POINTER(CacheDesc),
                                         _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32, _i32,
                                         _i32, _vp, _sz, _vp, _i32]),
+    "pkv_read_probe": (ctypes.c_int, [_vp, _sz, _i64, _vp, _i64, _vp, _i32, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_bm_create": (_vp, [_i32, _i32, _pi32, _i32]),
@@ -127,10 +128,34 @@ _SIGNATURES = {
     "pkv_bm_host_refcount": (_i32, [_vp, _i32]),
     "pkv_bm_host_free_list": (_i32, [_vp, _pi32, _i32]),
     "pkv_bm_seq_blocks": (ctypes.c_int, [_vp, _i64, _pi32, _i32]),
+    "pkv_bm_block_fills": (_i32, [_vp, _pi64, _i32, _pi32, _pi32, _i32]),
+    "pkv_quest_blocks_of_slots": (_i32, [_pi64, _i64, _i32, _pi32, _pi32, _i32]),
 }
 
 
+# Host calls: what the host-only library (no device code) exports.
+_HOST_ONLY = ("pkv_bm_", "pkv_prefix_rows", "pkv_prefix_order", "pkv_quest_blocks_of_slots",
+              "pkv_last_error", "pkv_version")
+
+
+def _load_host_only(path: str):
+    """The host-only library (the block manager and the shared-prefix unit builder, e.g. the
+    sanitizer build of build_lib.build_host_sanitized): host calls bound, device calls
+    absent, so any device wrapper fails loudly."""
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        if not name.startswith(_HOST_ONLY):
+            continue
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def _load():
+    host_lib = os.environ.get("PKV_HOST_LIB")
+    if host_lib:
+        return _load_host_only(host_lib)
     # torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading torch
     # first makes this library bind to that same runtime instead of bringing a
     # second copy into the process.
@@ -566,17 +591,17 @@ def quest_update_blocks(k_pool, meta, blocks, counts, desc: CacheDesc, stream=No
 
 
 def quest_blocks_of_slots(slots, block_size: int) -> Tuple[np.ndarray, np.ndarray]:
-    """(distinct blocks, fill counts) touched by a write to ``slots`` (slots fill a block in
-    order, so the highest slot written gives its fill)."""
-    sl = np.asarray(slots, dtype=np.int64).ravel()
-    sl = sl[sl >= 0]
-    if len(sl) == 0:
-        return np.zeros(0, np.int32), np.zeros(0, np.int32)
-    blk = sl // block_size
-    order = np.lexsort((sl, blk))
-    blk, sl = blk[order], sl[order]
-    last = np.r_[blk[1:] != blk[:-1], True]
-    return blk[last].astype(np.int32), (sl[last] % block_size + 1).astype(np.int32)
+    """(distinct blocks, fill counts) touched by a write to host ``slots``, computed by the
+    library (pkv_quest_blocks_of_slots)."""
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int64).ravel())
+    cap = len(sl)
+    blocks = np.empty(max(1, cap), np.int32)
+    fills = np.empty(max(1, cap), np.int32)
+    n = int(lib.pkv_quest_blocks_of_slots(sl.ctypes.data_as(_pi64), len(sl), int(block_size),
+                                          blocks.ctypes.data_as(_pi32),
+                                          fills.ctypes.data_as(_pi32), cap))
+    _check(min(n, 0))
+    return blocks[:n].copy(), fills[:n].copy()
 
 
 def quest_update_tails(k_pool, meta, block_tables, context_lens, desc: CacheDesc,
@@ -671,6 +696,27 @@ def quest_decode(q, k_pool, v_pool, meta, desc: CacheDesc, block_tables, context
                                     int(partition_size), int(budget_blocks), _ptr(ws), wsb,
                                     _stream(stream), int(impl)))
     return out
+
+
+# ---------------------------------------------------------------------------- measurement aid
+
+def read_probe(buf, tile_bytes: int, tile_ids, num_tiles: int, sink, workgroups: int = 2048,
+               stream=None) -> None:
+    """Plain HBM read of ``num_tiles`` tiles of ``buf`` (a device tensor): tile i at
+    ``tile_ids[i] * tile_bytes`` (device int64), or tiles 0.. in order when ``tile_ids`` is
+    None.  ``sink`` is a device tensor of ``workgroups * 64`` 32-bit words (one per lane of
+    the one-wave workgroups)."""
+    torch = _torch()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink.numel() * sink.element_size() < workgroups * 64 * 4 or not sink.is_cuda:
+        raise ValueError(f"sink must be a device tensor of at least {workgroups * 64} words")
+    if tile_ids is not None:
+        if not tile_ids.is_cuda or tile_ids.dtype != torch.int64 or tile_ids.numel() < num_tiles:
+            raise ValueError("tile_ids must be a device int64 tensor of num_tiles ids")
+    _check(lib.pkv_read_probe(_ptr(buf), int(buf.numel() * buf.element_size()), int(tile_bytes),
+                              _ptr(tile_ids) if tile_ids is not None else 0, int(num_tiles),
+                              _ptr(sink), int(workgroups), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------- host side
@@ -855,6 +901,19 @@ class BlockManager:
         _check(lib.pkv_bm_swap_stats(self._h, _np_ptr(out, ctypes.c_int64)))
         return {"host_free_blocks": int(out[0]), "host_blocks": int(out[1]),
                 "swapped_seqs": int(out[2])}
+
+    def block_fills(self, seqs) -> Tuple[np.ndarray, np.ndarray]:
+        """(distinct blocks, filled slots) of the sequences' blocks (pkv_bm_block_fills)."""
+        s = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        n = int(lib.pkv_bm_block_fills(self._h, _np_ptr(s, ctypes.c_int64), len(s), None, None, 0))
+        _check(min(n, 0))
+        blocks = np.empty(max(1, n), np.int32)
+        fills = np.empty(max(1, n), np.int32)
+        m = int(lib.pkv_bm_block_fills(self._h, _np_ptr(s, ctypes.c_int64), len(s),
+                                       _np_ptr(blocks, ctypes.c_int32),
+                                       _np_ptr(fills, ctypes.c_int32), n))
+        _check(min(m, 0))
+        return blocks[:n].copy(), fills[:n].copy()
 
     def host_refcount(self, block: int) -> int:
         return int(lib.pkv_bm_host_refcount(self._h, block))

@@ -717,6 +717,67 @@ int pkv_bm_seq_blocks(pkv_bm* bm, int64_t seq, int32_t* out, int32_t cap) {
   return n;
 }
 
+int32_t pkv_bm_block_fills(pkv_bm* bm, const int64_t* seqs, int32_t n, int32_t* blocks,
+                           int32_t* fills, int32_t cap) {
+  if (!bm || n < 0 || cap < 0 || (n > 0 && !seqs) || (cap > 0 && (!blocks || !fills)))
+    return fail(PKV_E_INVAL, "bad block_fills arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end() || it->second.swapped)
+      return fail(PKV_E_INVAL, "unknown or swapped-out sequence %lld", (long long)seqs[i]);
+  }
+  // position of each block in the output, in order of first appearance
+  std::unordered_map<int32_t, int32_t> at;
+  std::vector<int32_t> order, fill;
+  const int64_t B = bm->block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.find(seqs[i])->second;
+    for (size_t j = 0; j < s.blocks.size(); ++j) {
+      // logical block j holds tokens [j * B, min(len, (j + 1) * B))
+      const int32_t f = int32_t(std::max<int64_t>(0, std::min<int64_t>(B, s.len - int64_t(j) * B)));
+      auto ins = at.emplace(s.blocks[j], int32_t(order.size()));
+      if (ins.second) {
+        order.push_back(s.blocks[j]);
+        fill.push_back(f);
+      } else {
+        fill[ins.first->second] = std::max(fill[ins.first->second], f);
+      }
+    }
+  }
+  const int32_t m = int32_t(order.size());
+  for (int32_t k = 0; k < m && k < cap; ++k) {
+    blocks[k] = order[k];
+    fills[k] = fill[k];
+  }
+  return m;
+}
+
+int32_t pkv_quest_blocks_of_slots(const int64_t* slots, int64_t n, int32_t block_size,
+                                  int32_t* blocks, int32_t* fills, int32_t cap) {
+  pkv::clear_error();
+  if (n < 0 || block_size <= 0 || cap < 0 || (n > 0 && !slots) ||
+      (cap > 0 && (!blocks || !fills)))
+    return fail(PKV_E_INVAL, "bad blocks_of_slots arguments");
+  // highest slot written in each block; a block's slots fill in order, so it gives the fill
+  std::vector<std::pair<int64_t, int64_t>> hit;   // (block, slot)
+  hit.reserve(size_t(n));
+  for (int64_t i = 0; i < n; ++i)
+    if (slots[i] >= 0) hit.emplace_back(slots[i] / block_size, slots[i]);
+  std::sort(hit.begin(), hit.end());
+  int32_t m = 0;
+  for (size_t i = 0; i < hit.size(); ++i) {
+    if (i + 1 < hit.size() && hit[i + 1].first == hit[i].first) continue;   // not the highest
+    if (hit[i].first > INT32_MAX) return fail(PKV_E_INVAL, "slot %lld beyond int32 blocks",
+                                              (long long)hit[i].second);
+    if (m < cap) {
+      blocks[m] = int32_t(hit[i].first);
+      fills[m] = int32_t(hit[i].second % block_size) + 1;
+    }
+    ++m;
+  }
+  return m;
+}
+
 int32_t pkv_bm_evictable_list(pkv_bm* bm, int32_t* out, int32_t cap) {
   if (!bm) return -1;
   int32_t i = 0;

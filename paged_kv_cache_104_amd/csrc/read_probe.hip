@@ -5,13 +5,13 @@
 // table), so its ceiling is a read stream, either sequential or of scattered
 // tiles the size of one (block, KV head) tile of the pools.
 //
-// Work split: the buffer is read in 16-byte chunks; chunk c belongs to tile
-// c / chunks_per_tile, which sits at tile_ids[tile] (or at its own index for a
-// sequential read).  Consecutive threads take consecutive chunks (a tile is
-// read by consecutive lanes, 16 bytes each), every thread keeps U loads in
-// flight, and the grid strides over the chunks.  Loads are non-temporal, as
-// the decode kernel's; everything read is XOR-folded into one word per thread,
-// stored at the end, so the loads cannot be dropped.
+// Work split: one wave64 per workgroup, as the decode kernel's workers.  The
+// tiles to read, taken in list order as one run of 16-byte chunks, are cut
+// into equal contiguous shares, one per wave; a wave reads its share 1 KB per
+// load instruction (64 lanes x 16 bytes, consecutive), U instructions in
+// flight, so a sequential read streams one contiguous region per wave.  Loads
+// are non-temporal, as the decode kernel's; everything read is XOR-folded into
+// one word per lane, stored at the end, so the loads cannot be dropped.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -19,24 +19,26 @@
 
 namespace pkv {
 
-constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 8;
+constexpr int kProbeLanes = 64;
+constexpr int kProbeUnroll = 16;
 
 typedef unsigned probe_u32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(
+__global__ __launch_bounds__(kProbeLanes) void read_probe_kernel(
     const probe_u32x4_t* __restrict__ buf, int tile_shift, int64_t num_buf_tiles,
-    const int64_t* __restrict__ tile_ids, int64_t total_chunks, uint32_t* __restrict__ sink) {
-  const int64_t nthreads = int64_t(gridDim.x) * kProbeThreads;
-  const int64_t tid = int64_t(blockIdx.x) * kProbeThreads + threadIdx.x;
+    const int64_t* __restrict__ tile_ids, int64_t num_tiles, uint32_t* __restrict__ sink) {
+  const int64_t W = gridDim.x, w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t chunks = num_tiles << tile_shift;
+  const int64_t lo = chunks * w / W, hi = chunks * (w + 1) / W;   // this wave's share
   const int64_t in_tile = (int64_t(1) << tile_shift) - 1;
   uint32_t acc = 0;
-  for (int64_t c0 = tid; c0 < total_chunks; c0 += kProbeUnroll * nthreads) {
+  for (int64_t c0 = lo + lane; c0 < hi; c0 += kProbeUnroll * kProbeLanes) {
     probe_u32x4_t v[kProbeUnroll];
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) {
-      const int64_t c = c0 + u * nthreads;
-      if (c < total_chunks) {
+      const int64_t c = c0 + u * kProbeLanes;
+      if (c < hi) {
         const int64_t t = c >> tile_shift;
         int64_t id = tile_ids ? tile_ids[t] : t;
         if (id < 0 || id >= num_buf_tiles) id = 0;       // ids outside the buffer read tile 0
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  sink[tid] = acc;
+  sink[w * kProbeLanes + lane] = acc;
 }
 
 }  // namespace pkv
@@ -75,10 +77,9 @@ extern "C" int pkv_read_probe(const void* buf, size_t buf_bytes, int64_t tile_by
   if (num_tiles == 0) return PKV_OK;
   int shift = 0;
   while ((int64_t(16) << shift) < tile_bytes) ++shift;
-  const int64_t chunks = num_tiles << shift;
-  read_probe_kernel<<<dim3(unsigned(workgroups)), dim3(kProbeThreads), 0,
+  read_probe_kernel<<<dim3(unsigned(workgroups)), dim3(kProbeLanes), 0,
                       static_cast<hipStream_t>(stream)>>>(
-      static_cast<const probe_u32x4_t*>(buf), shift, buf_tiles, tile_ids, chunks, sink);
+      static_cast<const probe_u32x4_t*>(buf), shift, buf_tiles, tile_ids, num_tiles, sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_E_HIP, "read probe launch: %s", hipGetErrorString(e));
   return PKV_OK;

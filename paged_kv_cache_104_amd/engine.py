@@ -90,16 +90,11 @@ class PagedKVCache:
 
     def quest_refresh(self, seqs) -> None:
         """Recompute the metadata of every block of ``seqs`` from the key pool."""
-        B = self.desc.block_size
-        fill = {}
-        for s in seqs:
-            n = self.bm.seq_len(int(s))
-            for j, b in enumerate(self.bm.seq_blocks(int(s))):
-                fill[b] = max(fill.get(b, 0), min(B, n - j * B))
-        if fill:
-            blocks = np.fromiter(fill.keys(), dtype=np.int32, count=len(fill))
-            counts = np.fromiter(fill.values(), dtype=np.int32, count=len(fill))
-            quest_update_blocks(self.k_pool, self.quest_meta, blocks, counts, self.desc)
+        blocks, counts = self.bm.block_fills(seqs)
+        keep = counts > 0
+        if keep.any():
+            quest_update_blocks(self.k_pool, self.quest_meta, blocks[keep], counts[keep],
+                                self.desc)
 
     def quest_decode(self, q, out, tables, lens, scale: float, max_context_len: int,
                      budget_blocks: int, partition_size: int = 0, workspace=None,
