@@ -278,6 +278,35 @@ int pkv_paged_attn_merge(int32_t q_dtype, const int32_t* context_lens, int32_t n
  * PKV_E_INVAL when only one event is given. */
 int pkv_time_next_decode(void* start_event, void* stop_event);
 
+/*
+ * paged_attn_decode_noalloc -- pkv_paged_attn_decode without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The call allocates
+ * nothing (no hipMalloc, no library allocation); the partial results and piece
+ * records live in a static device array of pkv_decode_scratch_bytes() bytes
+ * (40 MiB) that every device the library runs on holds until the process ends.
+ *
+ * Arguments, layouts and results as pkv_paged_attn_decode_ex (impl as there;
+ * the same kernels run, so the output is the same bit for bit).  The scratch
+ * a batch needs is the piece rows of the kernel that runs: two head groups of
+ * (head_dim + 2) floats per persistent worker for the matrix-core kernel (for
+ * instance 4.3 MB with 1024 workers at 4 query heads per KV head and
+ * head_dim 128), or one row per (sequence, query head, partition) for the
+ * vector kernel with partitions, plus 8 bytes per (sequence, query head).  A
+ * batch needing more returns PKV_E_INVAL (use the workspace entry point); the
+ * other errors are pkv_paged_attn_decode_ex's.  Every call on a device shares
+ * that device's array and overwrites it: calls that overlap on one device (on
+ * two streams, or from two threads) race and must be serialised by the caller.
+ */
+size_t pkv_decode_scratch_bytes(void);
+int pkv_paged_attn_decode_noalloc(const void* q, int32_t q_dtype, const void* k_pool,
+                                  const void* v_pool, const pkv_cache_desc* c,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, void* out,
+                                  int32_t max_context_len, int32_t partition_size, void* stream,
+                                  int32_t impl);
+
 /* ------------------------------------------------------------------ shared-prefix decode
  *
  * Sequences forked from one prompt point their block tables at the same

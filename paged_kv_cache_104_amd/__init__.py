@@ -74,6 +74,11 @@ _SIGNATURES = {
     "pkv_prefix_rows": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]),
     "pkv_prefix_order": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32]),
     "pkv_time_next_decode": (ctypes.c_int, [_vp, _vp]),
+    "pkv_decode_scratch_bytes": (_sz, []),
+    "pkv_paged_attn_decode_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _vp,
+                                                     ctypes.POINTER(CacheDesc), _vp, _i32, _vp,
+                                                     _i32, _i32, _f32, _vp, _i32, _i32, _vp,
+                                                     _i32]),
     "pkv_rows_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32]),
     "pkv_paged_attn_decode_rows": (ctypes.c_int, [_vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc),
                                                   _vp, _i32, _vp, _i32, _i32, _f32, _vp, _i32,
@@ -446,6 +451,36 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
             float(scale), _ptr(out), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
             _stream(stream), int(impl)))
     return out
+
+
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
+                              desc: CacheDesc, max_context_len: int, partition_size: int = 0,
+                              impl: int = IMPL_AUTO, stream=None):
+    """paged_attn_decode with the library's static scratch instead of a workspace: nothing
+    is allocated (no tensor is created here either).  Calls that overlap on one device
+    race on the scratch."""
+    ks, vs = pool_shapes(desc)
+    _check_pool(k_pool, ks, desc, "k_pool")
+    _check_pool(v_pool, vs, desc, "v_pool")
+    S, Hq, D = q.shape
+    if D != desc.head_dim or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("q / out shapes or dtypes do not match")
+    if not (q.is_contiguous() and out.is_contiguous() and block_tables.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("q, out, block_tables and context_lens must be contiguous")
+    _check_tables(block_tables, context_lens)
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    _check(lib.pkv_paged_attn_decode_noalloc(
+        _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
+        float(scale), _ptr(out), int(max_context_len), int(partition_size), _stream(stream),
+        int(impl)))
+    return out
+
+
+def decode_scratch_bytes() -> int:
+    return int(lib.pkv_decode_scratch_bytes())
 
 
 def paged_attn_partials(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,

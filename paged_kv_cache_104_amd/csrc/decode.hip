@@ -1387,9 +1387,30 @@ template <int KV, int D, int BS, bool NT, bool ROWS>
 static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
   auto kernel = decode_mfma_kernel<KV, D, BS, NT, ROWS>;
   DecodeArgs a = a0;
-  a.workers = int32_t(std::min<int64_t>(kMaxWorkers, resident_workers(kernel)));
+  // a preset count (the no-allocation entry point sized its scratch for it) is a cap
+  const int64_t resident = std::min<int64_t>(kMaxWorkers, resident_workers(kernel));
+  a.workers = int32_t(a0.workers > 0 ? std::min<int64_t>(a0.workers, resident) : resident);
   return launch_decode(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a,
                        a.context_lens, a.block_tables, a.rows);
+}
+
+// Persistent workers a plain (not shared-prefix) matrix-core decode launches.
+template <int KV, int D, int BS>
+static int64_t mfma_workers_of(bool shared) {
+  return std::min<int64_t>(kMaxWorkers,
+                           shared ? resident_workers(decode_mfma_kernel<KV, D, BS, false, false>)
+                                  : resident_workers(decode_mfma_kernel<KV, D, BS, true, false>));
+}
+
+template <int D>
+static int64_t mfma_workers_d(int kv, int bs, bool shared) {
+  if (kv == PKV_FP8_E4M3)
+    return bs == 8 ? mfma_workers_of<KV_FP8, D, 8>(shared)
+           : bs == 16 ? mfma_workers_of<KV_FP8, D, 16>(shared)
+                      : mfma_workers_of<KV_FP8, D, 32>(shared);
+  return bs == 8 ? mfma_workers_of<KV_BF16, D, 8>(shared)
+         : bs == 16 ? mfma_workers_of<KV_BF16, D, 16>(shared)
+                    : mfma_workers_of<KV_BF16, D, 32>(shared);
 }
 
 // The shared-prefix decode reads each shared block once, so it always streams.
@@ -1442,7 +1463,8 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                    int32_t num_q_heads, float scale, void* out, int32_t max_context_len,
                    int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   DecodeArgs* a, WsLayout* lay, int32_t num_rows = -1) {
+                   DecodeArgs* a, WsLayout* lay, int32_t num_rows = -1,
+                   const WsLayout* fixed = nullptr) {
   int rc = check_desc(c);
   if (rc) return rc;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -1468,9 +1490,10 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
   if ((c->kv_dtype == PKV_F32) != (q_dtype == PKV_F32))
     return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(q_dtype),
                 dtype_name(c->kv_dtype));
-  *lay = num_rows >= 0 ? ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim)
-                       : ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim,
-                                   max_context_len, partition_size);
+  *lay = fixed ? *fixed
+        : num_rows >= 0 ? ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim)
+                        : ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim,
+                                    max_context_len, partition_size);
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return fail(PKV_E_INVAL, "NULL pointer");
@@ -1712,4 +1735,118 @@ extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const 
   }
   if (phases & 2) return launch_merge(a, c->head_dim, q_dtype, s, true);
   return PKV_OK;
+}
+
+// ------------------------------------------------------------------------ no-allocation variant
+//
+// pkv_paged_attn_decode without a workspace argument, for callers that cannot
+// allocate device memory.  The partial rows, piece records and header live in
+// `scratch`, a file-scope device array of kScratchBytes that each device holds
+// for the life of the process.  Host code never passes the array's name to a
+// kernel (in host code it is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, and is kept.  The
+// kernels write every scratch byte they later read, so nothing is cleared
+// between calls; calls that overlap on one device (two streams) race on it.
+
+constexpr size_t kScratchBytes = size_t(40) << 20;
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr and a message on failure).
+static void* scratch_ptr() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(PKV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kScratchMaxDevices) {
+    fail(PKV_E_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+         kScratchMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(PKV_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Scratch layout of one call: header | records of the (sequence, head) pairs | partial
+// rows, sized for the kernel family and worker count that will run (the generic
+// workspace is sized without them).
+static WsLayout ws_layout_noalloc(int32_t num_seqs, int32_t num_q_heads, int32_t group,
+                                  int32_t head_dim, int32_t max_ctx, int32_t part, bool mfma,
+                                  int64_t workers) {
+  WsLayout w;
+  w.parts = max_parts_for(max_ctx, part);
+  w.pairs = int64_t(num_seqs) * num_q_heads;
+  w.recs_off = 256;
+  w.ml_off = w.recs_off + align256(size_t(w.pairs) * sizeof(int2));
+  w.rows = mfma ? 2 * workers * group : (w.parts > 1 ? w.pairs * w.parts : 0);
+  w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
+  w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
+  return w;
+}
+
+extern "C" size_t pkv_decode_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int pkv_paged_attn_decode_noalloc(const void* q, int32_t q_dtype, const void* k_pool,
+                                             const void* v_pool, const pkv_cache_desc* c,
+                                             const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_q_heads, float scale, void* out,
+                                             int32_t max_context_len, int32_t partition_size,
+                                             void* stream, int32_t impl) {
+  clear_error();
+  int rc = check_desc(c);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size < 0)
+    return fail(PKV_E_INVAL, "negative size");
+  if (num_q_heads % c->num_kv_heads || num_q_heads / c->num_kv_heads > kMaxGroup)
+    return fail(PKV_E_INVAL, "num_q_heads %d is not a multiple (at most %d) of num_kv_heads %d",
+                num_q_heads, kMaxGroup, c->num_kv_heads);
+  if (num_seqs == 0) return PKV_OK;
+  const int family = impl & PKV_IMPL_FAMILY_MASK;
+  const bool shared = (impl & PKV_IMPL_SHARED_BLOCKS) != 0;
+  const bool mfma = family == PKV_IMPL_MFMA || (family == PKV_IMPL_AUTO && c->kv_dtype != PKV_F32);
+  const int64_t workers =
+      mfma && c->kv_dtype != PKV_F32
+          ? (c->head_dim == 64 ? mfma_workers_d<64>(c->kv_dtype, c->block_size, shared)
+                               : mfma_workers_d<128>(c->kv_dtype, c->block_size, shared))
+          : 0;
+  const WsLayout lay = ws_layout_noalloc(num_seqs, num_q_heads, num_q_heads / c->num_kv_heads,
+                                         c->head_dim, max_context_len, partition_size, mfma,
+                                         workers);
+  if (lay.total > kScratchBytes)
+    return fail(PKV_E_INVAL,
+                "the batch needs %zu bytes of scratch, more than the %zu the no-allocation "
+                "decode holds (use pkv_paged_attn_decode with a workspace)",
+                lay.total, kScratchBytes);
+  void* ws = scratch_ptr();
+  if (!ws) return PKV_E_HIP;
+  DecodeArgs a;
+  WsLayout got;
+  rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, scale, out, max_context_len, partition_size, ws,
+               kScratchBytes, &a, &got, -1, &lay);
+  if (rc) return rc;
+  a.workers = int32_t(workers);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool merge = false;
+  rc = launch_partials(a, c, q_dtype, lay, impl, s, &merge);
+  if (rc || !merge) return rc;
+  DecodeArgs m = a;
+  if (lay.parts <= 1) m.part_tokens = 0;
+  return launch_merge(m, c->head_dim, q_dtype, s);
 }
