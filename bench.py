@@ -347,12 +347,12 @@ def read_reference(tile_bytes: int, total_bytes: int = READ_REF_BYTES, reps: int
     buf.fill_(1)
     n = total_bytes // tile_bytes
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(0)).to("cuda")
-    sink = torch.empty(4096 * 64, dtype=torch.int32, device="cuda")
+    sink = torch.empty(8192 * 64, dtype=torch.int32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     res = {}
     for name, ids in (("sequential", None), ("random_tiles", perm)):
         best = 0.0
-        for wgs in (1024, 2048, 4096):
+        for wgs in (1024, 2048, 4096, 8192):
             ts = []
             for r in range(reps + 1):
                 ev[0].record()

@@ -483,9 +483,11 @@ int pkv_quest_decode(const void* q, int32_t q_dtype, const void* k_pool, const v
  *   workgroups   one-wave (64-lane) workgroups of the launch; the tiles, in
  *                list order, are cut into equal contiguous shares, one per wave
  *                (1024 puts one wave on every SIMD of a 256-CU device)
- * Not part of the paged path.  Errors: PKV_E_INVAL for a NULL or misaligned
- * pointer, a tile size that is no power of two, or a sequential read past
- * the buffer; PKV_E_HIP if the launch fails.
+ * The tiles must add up to whole 1 KB rows (one load instruction of a wave),
+ * and tiles read through ids must hold at least 1 KB.  Not part of the paged
+ * path.  Errors: PKV_E_INVAL for a NULL or misaligned pointer, a tile size
+ * that is no power of two, tiles that break those rules, or a sequential read
+ * past the buffer; PKV_E_HIP if the launch fails.
  */
 int pkv_read_probe(const void* buf, size_t buf_bytes, int64_t tile_bytes, const int64_t* tile_ids,
                    int64_t num_tiles, uint32_t* sink, int32_t workgroups, void* stream);

@@ -11,7 +11,7 @@ from gpu_util import torch_mod
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("tile_bytes,workgroups", [(4096, 8), (2048, 3), (16, 5), (65536, 2),
+@pytest.mark.parametrize("tile_bytes,workgroups", [(4096, 8), (2048, 3), (1024, 5), (65536, 2),
                                                   (4096, 1000)])
 def test_read_probe_reads_every_tile_once(tile_bytes, workgroups):
     import paged_kv_cache_104_amd as pkv
@@ -48,3 +48,8 @@ def test_read_probe_rejects_bad_arguments():
         pkv.read_probe(buf, 3000, None, 4, sink, 1)            # not a power of two
     with pytest.raises(pkv.PagedKVError):
         pkv.read_probe(buf, 4096, None, 17, sink, 1)           # past the buffer
+    ids = torch.zeros(4, dtype=torch.int64, device="cuda")
+    with pytest.raises(pkv.PagedKVError):
+        pkv.read_probe(buf, 512, ids, 4, sink, 1)              # tiles by id below 1 KB
+    with pytest.raises(pkv.PagedKVError):
+        pkv.read_probe(buf, 16, None, 3, sink, 1)              # not whole 1 KB rows
