@@ -463,9 +463,12 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
 }
 
 // Software pipeline depth (32-token steps whose loads are in flight while one
-// computes) and the waves per SIMD the register budget is sized for.
+// computes) and the waves per SIMD the register budget is sized for.  bf16: two
+// steps (32 KB per wave, 32 MB over 1024 waves); three or four steps in flight
+// ran 0.3% (8B-like layer) to 7% (one 32k context, the multi-query layer)
+// slower, and two waves per SIMD with two steps each slower still.
 #ifndef PKV_BF16_STAGES
-#define PKV_BF16_STAGES 3
+#define PKV_BF16_STAGES 2
 #endif
 #ifndef PKV_BF16_WAVES
 #define PKV_BF16_WAVES 1
