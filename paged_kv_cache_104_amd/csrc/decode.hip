@@ -98,6 +98,9 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) { *p =
 constexpr int kVecThreads = 256;
 constexpr int kVecChunk = 256;  // tokens per LDS chunk
 constexpr int kMaxGroup = 16;
+// Query columns of a shared-prefix unit: two 16-column matrix-core tiles, so
+// that up to 32 / group forked samples read their shared blocks once.
+constexpr int kUnitCols = 32;
 
 // Four consecutive pool elements as floats, with one 16-, 8- or 4-byte load (p is
 // 4-element aligned; fp8 without its scale).
@@ -273,14 +276,14 @@ __global__ __launch_bounds__(kVecThreads) void decode_vector_kernel(DecodeArgs a
 
 // ------------------------------------------------------------------------ MFMA kernel
 
-// Per-lane registers of one 32-token step.
-template <int KV, int D>
+// Per-lane registers of one 32-token step; NQ 16-column query tiles.
+template <int KV, int D, int NQ>
 struct StepRegs {
   static constexpr int NK = KV == KV_FP8 ? D / 64 : D / 32;  // 16-byte K loads per tile
   uint4 ka[NK];   // K rows, tile a (MFMA A operand of Q.K^T)
   uint4 kb[NK];   // K rows, tile b
   typename std::conditional<KV == KV_FP8, uint2, uint4>::type v[D / 16];  // V^T, 8 tokens x 1 dim
-  uint4 q[D / 32];  // Q^T of the pair's head group, loaded with a pair's first step only
+  uint4 q[NQ][D / 32];  // Q^T of the pair's columns, loaded with a pair's first step only
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -379,8 +382,8 @@ __device__ __forceinline__ uint2 ld8(const void* p) {
 // when a score exceeds it by more than this, so weights stay below 2^8.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int KV, int D>
-__device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uint4 (&qv)[D / 32],
+template <int KV, int D, class Regs>
+__device__ __forceinline__ void compute_step(const Regs& R, const uint4 (&qv)[D / 32],
                                              floatx4_t (&acc)[D / 16],
                                              floatx4_t& lsum, float& m, float sl2, int tt, int t1,
                                              int r, bool active) {
@@ -479,10 +482,14 @@ __device__ __forceinline__ void compute_step(const StepRegs<KV, D>& R, const uin
 #ifndef PKV_FP8_WAVES
 #define PKV_FP8_WAVES 2
 #endif
-template <int KV>
+// Two query tiles (the shared-prefix decode) need registers for a second set of
+// scores, weights, accumulators and queries: fp8 then runs one wave per SIMD,
+// with three steps in flight (four would spill registers).
+template <int KV, int NQ>
 struct MfmaTuning {
-  static constexpr int stages = KV == KV_FP8 ? PKV_FP8_STAGES : PKV_BF16_STAGES;
-  static constexpr int waves = KV == KV_FP8 ? PKV_FP8_WAVES : PKV_BF16_WAVES;
+  static constexpr int stages =
+      KV == KV_FP8 ? (NQ == 1 ? PKV_FP8_STAGES : 3) : PKV_BF16_STAGES;
+  static constexpr int waves = KV == KV_FP8 ? (NQ == 1 ? PKV_FP8_WAVES : 1) : PKV_BF16_WAVES;
 };
 
 // Physical blocks of the step at tokens tt .. tt+31 of a context of t1 tokens
@@ -523,21 +530,26 @@ __device__ __forceinline__ void load_query(uint4 (&qv)[D / 32], __amdgpu_buffer_
     qv[i] = ld16_q(qrsrc, qlane ? qoff + 2u * uint32_t(qk_dim0<KV>(i, r)) : qoob);
 }
 
-// Issue the loads of one step: the pair's query when the step is the first the
-// worker computes of that pair, then K rows, then V^T columns.
-template <int KV, int D, int BS, bool NT>
-__device__ __forceinline__ void issue_step(StepRegs<KV, D>& R, const typename KvTraits<KV>::T* kp,
+// Issue the loads of one step: the pair's query tiles when the step is the
+// first the worker computes of that pair, then K rows, then V^T columns.
+template <int KV, int D, int BS, bool NT, int NQ>
+__device__ __forceinline__ void issue_step(StepRegs<KV, D, NQ>& R,
+                                           const typename KvTraits<KV>::T* kp,
                                            const typename KvTraits<KV>::T* vp,
                                            const int (&pbs)[32 / BS], int64_t blk_stride,
                                            const LaneMap<KV, D, BS>& L, bool with_q,
-                                           __amdgpu_buffer_rsrc_t qrsrc, uint32_t qoff,
-                                           bool qlane, uint32_t qoob, int r) {
-  if (with_q) load_query<KV, D>(R.q, qrsrc, qoff, qlane, qoob, r);
+                                           __amdgpu_buffer_rsrc_t qrsrc,
+                                           const uint32_t (&qoff)[NQ], const bool (&qlane)[NQ],
+                                           uint32_t qoob, int r) {
+  if (with_q) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) load_query<KV, D>(R.q[t], qrsrc, qoff[t], qlane[t], qoob, r);
+  }
   const auto* ka = kp + int64_t(pick_block<BS>(pbs, L.ka_blk)) * blk_stride + L.ka_off;
   const auto* kb = kp + int64_t(pick_block<BS>(pbs, L.kb_blk)) * blk_stride + L.kb_off;
   const auto* vb = vp + int64_t(pick_block<BS>(pbs, L.v_blk)) * blk_stride + L.v_off;
 #pragma unroll
-  for (int i = 0; i < StepRegs<KV, D>::NK; ++i) {
+  for (int i = 0; i < StepRegs<KV, D, NQ>::NK; ++i) {
     // bf16: k-step i starts 32*i dimensions further; fp8: load i covers k-steps 2i, 2i+1
     const int di = KV == KV_FP8 ? 64 * i : 32 * i;
     R.ka[i] = ld16<NT>(ka + di);
@@ -588,25 +600,33 @@ __device__ __forceinline__ void unit_of(const DecodeArgs& a, int4 d, int len0, i
     return;
   }
   seq0 = d.x;
-  M = max(1, min(min(d.z, kMaxGroup / a.group), a.num_seqs - d.x));
+  M = max(1, min(min(d.z, kUnitCols / a.group), a.num_seqs - d.x));
   T = min(max(0, d.y), clamp_ctx(len0, a.max_ctx)) & ~(a.block_size - 1);
 }
 
 // Unit d's fields and the steps of one of its KV heads: the shared span, then
-// every member's own.  The members' lengths are all requested before any is
-// used (a loop over M would wait for each load in turn).
+// every member's own.  The members' lengths are requested eight at a time, all
+// of a batch before any is used (a loop over M would wait for each load in
+// turn); the first batch holds the first member's, which fixes the unit.
 __device__ __forceinline__ int unit_load(const DecodeArgs& a, int4 d,
                                          const int32_t* __restrict__ lens, int& seq0, int& M,
                                          int& T) {
+  constexpr int kBatch = 8;
   const int first = row_seq(a, d);
-  int len[kMaxGroup];
+  int len[kBatch];
 #pragma unroll
-  for (int m = 0; m < kMaxGroup; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
+  for (int k = 0; k < kBatch; ++k) len[k] = lens[min(first + k, a.num_seqs - 1)];
   unit_of(a, d, len[0], seq0, M, T);
   int n = ctx_steps(T);
+  for (int m0 = 0;;) {
 #pragma unroll
-  for (int m = 0; m < kMaxGroup; ++m)
-    n += m < M ? ctx_steps(max(0, clamp_ctx(len[m], a.max_ctx) - T)) : 0;
+    for (int k = 0; k < kBatch; ++k)
+      n += m0 + k < M ? ctx_steps(max(0, clamp_ctx(len[k], a.max_ctx) - T)) : 0;
+    m0 += kBatch;
+    if (m0 >= M) break;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) len[k] = lens[min(first + m0 + k, a.num_seqs - 1)];
+  }
   return n;
 }
 
@@ -650,7 +670,7 @@ __device__ __forceinline__ void next_span(Cursor& cu, const DecodeArgs& a,
 // The unit fields and the span of pair step cu.x, from the unit's descriptor
 // and its members' lengths (len[m] of sequence d.x + m).
 __device__ __forceinline__ void walk_unit(Cursor& cu, const DecodeArgs& a, int4 d,
-                                          const int (&len)[kMaxGroup]) {
+                                          const int (&len)[kUnitCols]) {
   unit_of(a, d, len[0], cu.seq0, cu.M, cu.T);
   cu.sub = -1;
   cu.seq = cu.seq0;
@@ -659,7 +679,7 @@ __device__ __forceinline__ void walk_unit(Cursor& cu, const DecodeArgs& a, int4 
   cu.x0 = 0;
   cu.xe = ctx_steps(cu.T);
 #pragma unroll
-  for (int m = 0; m < kMaxGroup; ++m) {
+  for (int m = 0; m < kUnitCols; ++m) {
     if (m < cu.M && cu.x >= cu.xe) {
       cu.sub = m;
       cu.seq = cu.seq0 + m;
@@ -682,9 +702,9 @@ __device__ __forceinline__ void enter_unit(Cursor& cu, const DecodeArgs& a,
     // (a walk span by span would wait for one length after another)
     const int4 d = rows[cu.s];
     const int first = row_seq(a, d);
-    int len[kMaxGroup];
+    int len[kUnitCols];
 #pragma unroll
-    for (int m = 0; m < kMaxGroup; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
+    for (int m = 0; m < kUnitCols; ++m) len[m] = lens[min(first + m, a.num_seqs - 1)];
     walk_unit(cu, a, d, len);
   } else {
     cu.seq0 = cu.seq = cu.s;
@@ -767,22 +787,23 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
   const int S = ROWS ? a.num_rows : a.num_seqs, hkv = a.num_kv_heads;
   int sum = 0;
   int v[4];   // steps of the units of the last chunk (all of them when S <= 256)
+  int cx[4] = {0, 0, 0, 0};   // plain decode: their context lengths (cut to max_ctx)
   // Shared-prefix decode with at most 64 units: lane i's unit and its members'
   // lengths stay in registers, and the worker's cursor is read from the lane
   // that holds its unit instead of loading them again.
   int4 dk = make_int4(0, 0, 0, 0);
-  int lk[kMaxGroup];
+  int lk[kUnitCols];
   const bool few = ROWS && S <= 64;
   if (few) {
     dk = rows[min(lane, S - 1)];
     const int first = row_seq(a, dk);
 #pragma unroll
-    for (int m = 0; m < kMaxGroup; ++m) lk[m] = lens[min(first + m, a.num_seqs - 1)];
+    for (int m = 0; m < kUnitCols; ++m) lk[m] = lens[min(first + m, a.num_seqs - 1)];
     int seq0, M, T;
     unit_of(a, dk, lk[0], seq0, M, T);
     int n = ctx_steps(T);
 #pragma unroll
-    for (int m = 0; m < kMaxGroup; ++m)
+    for (int m = 0; m < kUnitCols; ++m)
       n += m < M ? ctx_steps(max(0, clamp_ctx(lk[m], a.max_ctx) - T)) : 0;
     v[0] = lane < S ? n : 0;
     v[1] = v[2] = v[3] = 0;
@@ -804,7 +825,8 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int s = s0 + 64 * u + lane;
-        v[u] = s < S ? ctx_steps(clamp_ctx(lens[s], a.max_ctx)) : 0;
+        cx[u] = s < S ? clamp_ctx(lens[s], a.max_ctx) : 0;
+        v[u] = ctx_steps(cx[u]);
       }
     }
 #pragma unroll
@@ -831,14 +853,25 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
       cu.x = target - first - cu.kvh * ns;
       cu.n = ns;
       cu.P = first + cu.kvh * ns;
-      if (few) {
+      if (!ROWS && S <= 256) {
+        // the context length is in lane l's registers: no second load of it
+        const int c = s0 == 0 ? cx[0] : s0 == 64 ? cx[1] : s0 == 128 ? cx[2] : cx[3];
+        cu.seq0 = cu.seq = cu.s;
+        cu.M = 1;
+        cu.T = 0;
+        cu.sub = 0;
+        cu.tb = 0;
+        cu.x0 = 0;
+        cu.ctx = __builtin_amdgcn_readlane(c, l);
+        cu.xe = cu.n;
+      } else if (few) {
         const int4 d = make_int4(__builtin_amdgcn_readlane(dk.x, l),
                                  __builtin_amdgcn_readlane(dk.y, l),
                                  __builtin_amdgcn_readlane(dk.z, l),
                                  __builtin_amdgcn_readlane(dk.w, l));
-        int len[kMaxGroup];
+        int len[kUnitCols];
 #pragma unroll
-        for (int m = 0; m < kMaxGroup; ++m) len[m] = __builtin_amdgcn_readlane(lk[m], l);
+        for (int m = 0; m < kUnitCols; ++m) len[m] = __builtin_amdgcn_readlane(lk[m], l);
         walk_unit(cu, a, d, len);
       } else {
         enter_unit<ROWS>(cu, a, rows, lens);
@@ -857,7 +890,7 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
 // (bf16 rows), the piece records of the pairs it starts, and the partial
 // segment of the pair that began before its range.  A full buffer is written
 // out where it fills.
-template <int D>
+template <int D, int COLS>
 struct OutStage {
   static constexpr int kOutBytes = 8192;
   static constexpr int kMaxOut = kOutBytes / (D * 2);   // entries of a one-head group
@@ -866,12 +899,12 @@ struct OutStage {
   int out_row[kMaxOut];            // first q row (s * Hq + kvh * g) of each entry
   int rec_pair[kMaxRecs];
   int2 rec[kMaxRecs];
-  float seg[kMaxGroup * D];        // normalised rows of the slot-0 segment
-  float seg_ml[kMaxGroup * 2];
+  float seg[COLS * D];             // normalised rows of the slot-0 segment
+  float seg_ml[COLS * 2];
 };
 
-template <int D>
-__device__ __forceinline__ void flush_outputs(const DecodeArgs& a, OutStage<D>& st, int& n_out,
+template <int D, class Stage>
+__device__ __forceinline__ void flush_outputs(const DecodeArgs& a, Stage& st, int& n_out,
                                               int lane) {
   if (n_out == 0) return;
   __syncthreads();
@@ -885,9 +918,8 @@ __device__ __forceinline__ void flush_outputs(const DecodeArgs& a, OutStage<D>& 
   n_out = 0;
 }
 
-template <int D>
-__device__ __forceinline__ void flush_recs(const DecodeArgs& a, OutStage<D>& st, int& n_rec,
-                                           int lane) {
+template <class Stage>
+__device__ __forceinline__ void flush_recs(const DecodeArgs& a, Stage& st, int& n_rec, int lane) {
   if (n_rec == 0) return;
   __syncthreads();
   for (int i = lane; i < n_rec; i += 64) a.recs[st.rec_pair[i]] = st.rec[i];
@@ -897,15 +929,15 @@ __device__ __forceinline__ void flush_recs(const DecodeArgs& a, OutStage<D>& st,
 
 // Columns of a pair with a query behind them, and the workspace rows per
 // partial-segment slot: the head group (plain decode), or the head groups of
-// the unit's M members side by side (shared-prefix decode, whose slots are 16
-// rows apart).
+// the unit's M members side by side (shared-prefix decode, whose slots are
+// kUnitCols rows apart).
 template <bool ROWS>
 __device__ __forceinline__ int pair_cols(const DecodeArgs& a, const Cursor& cu) {
   return ROWS ? cu.M * a.group : a.group;
 }
 template <bool ROWS>
 __device__ __forceinline__ int slot_rows(const DecodeArgs& a) {
-  return ROWS ? kMaxGroup : a.group;
+  return ROWS ? kUnitCols : a.group;
 }
 
 // Normalised output rows of the pair's columns, or its partial segment, at
@@ -935,65 +967,72 @@ __device__ __forceinline__ void store_piece(const DecodeArgs& a, int64_t row0, i
 // also records {first worker, workers} of the pair for the merge.  A column
 // that saw no token (a member whose span lies outside the segment) has sum 0:
 // its partial row is stored as zeros.
-template <int D, bool ROWS>
+template <int D, bool ROWS, int NQ, class Stage>
 __device__ __forceinline__ void write_segment(const DecodeArgs& a, const Cursor& cu, int w, int q,
-                                              const floatx4_t (&acc)[D / 16],
-                                              const floatx4_t& lsum, float m, int r, int c,
-                                              int lane, OutStage<D>& st, int& n_out, int& n_rec,
-                                              int& seg0_cols) {
+                                              const floatx4_t (&acc)[NQ][D / 16],
+                                              const floatx4_t (&lsum)[NQ], const float (&m)[NQ],
+                                              int r, int c, int lane, Stage& st, int& n_out,
+                                              int& n_rec, int& seg0_cols) {
   const int g = a.group;
   const int ncols = pair_cols<ROWS>(a, cu), srows = slot_rows<ROWS>(a);
   const int lo = w * q;
   const bool head = cu.P >= lo;                  // the pair starts in this range
   const bool whole = head && cu.P + cu.n <= lo + q;
   if (head) {
-    if (n_rec == OutStage<D>::kMaxRecs) flush_recs<D>(a, st, n_rec, lane);
+    if (n_rec == Stage::kMaxRecs) flush_recs(a, st, n_rec, lane);
     if (lane == 0) {
       st.rec_pair[n_rec] = cu.s * a.num_kv_heads + cu.kvh;
       st.rec[n_rec] = make_int2(w, (cu.P + cu.n - 1) / q - w + 1);
     }
     ++n_rec;
   }
-  const float l = lsum[0];
-  const float inv = ROWS ? (l > 0.f ? a.v_scale / l : 0.f) : a.v_scale / l;
   if (whole) {
     const int ne = ROWS ? cu.M : 1;              // staged entries: one head group each
-    if ((n_out + ne) * g > OutStage<D>::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
+    if ((n_out + ne) * g > Stage::kMaxOut) flush_outputs<D>(a, st, n_out, lane);
     if (lane < ne) st.out_row[n_out + lane] = (cu.seq0 + lane) * a.num_q_heads + cu.kvh * g;
-    if (c < ncols) {
-      uint2* o = st.out + (n_out * g + c) * (D / 4);
-#pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-        uint2 v;
-        v.x = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
-        v.y = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
-        o[4 * j + r] = v;
-      }
-    }
-    n_out += ne;
-  } else if (!head) {
-    if (c < ncols) {
-#pragma unroll
-      for (int j = 0; j < D / 16; ++j)
-        *reinterpret_cast<float4*>(st.seg + c * D + 16 * j + 4 * r) =
-            make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-      if (r == 0) {
-        st.seg_ml[2 * c] = m;
-        st.seg_ml[2 * c + 1] = l;
-      }
-    }
-    seg0_cols = ncols;
-  } else {
-    store_piece<D>(a, int64_t(2 * w + 1) * srows, ncols, acc, m, l, inv, r, c);
   }
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const int col = 16 * t + c;                  // this lane's column of tile t
+    const float l = lsum[t][0];
+    const float inv = ROWS ? (l > 0.f ? a.v_scale / l : 0.f) : a.v_scale / l;
+    if (whole) {
+      if (col < ncols) {
+        uint2* o = st.out + (n_out * g + col) * (D / 4);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[t][j][0] * inv, acc[t][j][1] * inv);
+          v.y = pack_bf16x2(acc[t][j][2] * inv, acc[t][j][3] * inv);
+          o[4 * j + r] = v;
+        }
+      }
+    } else if (!head) {
+      if (col < ncols) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+          *reinterpret_cast<float4*>(st.seg + col * D + 16 * j + 4 * r) =
+              make_float4(acc[t][j][0] * inv, acc[t][j][1] * inv, acc[t][j][2] * inv,
+                          acc[t][j][3] * inv);
+        if (r == 0) {
+          st.seg_ml[2 * col] = m[t];
+          st.seg_ml[2 * col + 1] = l;
+        }
+      }
+    } else {
+      store_piece<D>(a, int64_t(2 * w + 1) * srows, ncols, acc[t], m[t], l, inv, r, col);
+    }
+  }
+  if (whole) n_out += ROWS ? cu.M : 1;
+  else if (!head) seg0_cols = ncols;
 }
 
 // The staged outputs, records and slot-0 segment, after the loop.
-template <int D, bool ROWS>
-__device__ __forceinline__ void flush_stage(const DecodeArgs& a, OutStage<D>& st, int w, int n_out,
+template <int D, bool ROWS, class Stage>
+__device__ __forceinline__ void flush_stage(const DecodeArgs& a, Stage& st, int w, int n_out,
                                             int n_rec, int seg0_cols, int lane) {
   flush_outputs<D>(a, st, n_out, lane);
-  flush_recs<D>(a, st, n_rec, lane);
+  flush_recs(a, st, n_rec, lane);
   if (seg0_cols > 0) {
     __syncthreads();
     const int64_t row0 = int64_t(2 * w) * slot_rows<ROWS>(a);
@@ -1020,11 +1059,13 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs& a, OutStage<D>& st
 // the kernel's stores cannot alias them, so their uniform loads stay scalar
 // and never wait on the vector-load counter.
 template <int KV, int D, int BS, bool NT, bool ROWS>
-__global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
+__global__ __launch_bounds__(64, (MfmaTuning<KV, ROWS ? 2 : 1>::waves)) void decode_mfma_kernel(
     DecodeArgs a, const int32_t* __restrict__ lens, const int32_t* __restrict__ tables,
     const int4* __restrict__ rows) {
   typedef typename KvTraits<KV>::T T;
-  constexpr int NS = MfmaTuning<KV>::stages;
+  // query tiles of 16 columns: the head group, or a shared-prefix unit's kUnitCols columns
+  constexpr int NQ = ROWS ? kUnitCols / 16 : 1;
+  constexpr int NS = MfmaTuning<KV, NQ>::stages;
   constexpr int NB = 32 / BS;
   const int lane = threadIdx.x;
   const int r = lane >> 4, c = lane & 15;
@@ -1054,30 +1095,44 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
                   ROWS ? la.tb + 32 * (la.x - la.x0) : 32 * la.x, ROWS ? la.tb + la.ctx : la.ctx,
                   a.num_blocks);
 
-  floatx4_t acc[D / 16];
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  floatx4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  floatx4_t acc[NQ][D / 16];
+  floatx4_t lsum[NQ];
   // a finite start: a shared-prefix column that sees no token keeps exp2(-inf - m) = 0
   constexpr float kMStart = ROWS ? -1e30f : -INFINITY;
-  float m = kMStart;
-  StepRegs<KV, D> buf[NS];
-  uint4 qc[D / 32];                 // query of the compute cursor's pair
-  __shared__ OutStage<D> stage;
+  float m[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[t][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m[t] = kMStart;
+  }
+  StepRegs<KV, D, NQ> buf[NS];
+  uint4 qc[NQ][D / 32];             // query of the compute cursor's pair
+  __shared__ OutStage<D, ROWS ? kUnitCols : kMaxGroup> stage;
   int n_out = 0, n_rec = 0;         // staged outputs and records
   int seg0_cols = 0;                // columns of the staged slot-0 segment (0: none)
   bool la_first = true, cu_first = true;   // the next step is the worker's first
 
-  // query column c of a pair: head c % g of member c / g
-  const int cm = c / g, ch = c - cm * g;
+  // query column 16 t + c of a pair (tile t): head (16 t + c) % g of member (16 t + c) / g
+  int cm[NQ], ch[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    cm[t] = (16 * t + c) / g;
+    ch[t] = 16 * t + c - cm[t] * g;
+  }
+  uint32_t qoff[NQ];
+  bool qlane[NQ];
   // issue the load cursor's step into R, then move the cursor on
 #define PKV_ISSUE(R)                                                                           \
   do {                                                                                         \
-    issue_step<KV, D, BS, NT>(                                                                 \
+    for (int t = 0; t < NQ; ++t) {                                                             \
+      qoff[t] = uint32_t(((la.seq0 + cm[t]) * a.num_q_heads + la.kvh * g + ch[t]) * D * 2);    \
+      qlane[t] = 16 * t + c < pair_cols<ROWS>(a, la);                                          \
+    }                                                                                          \
+    issue_step<KV, D, BS, NT, NQ>(                                                             \
         R, k_pool + int64_t(la.kvh) * head_stride, v_pool + int64_t(la.kvh) * head_stride,     \
-        la_pbs, blk_stride, L, la_first || la.x == 0, qrsrc,                                   \
-        uint32_t(((la.seq0 + cm) * a.num_q_heads + la.kvh * g + ch) * D * 2),                  \
-        c < pair_cols<ROWS>(a, la), qbytes, r);                                                \
+        la_pbs, blk_stride, L, la_first || la.x == 0, qrsrc, qoff, qlane, qbytes, r);          \
     la_first = false;                                                                          \
     if (la_left > 1) {                                                                         \
       --la_left;                                                                               \
@@ -1104,22 +1159,33 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
       if (rem > 0) {
         if (cu_first || cu.x == 0) {
 #pragma unroll
-          for (int i = 0; i < D / 32; ++i) qc[i] = buf[st].q[i];
+          for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) qc[t][i] = buf[st].q[t][i];
+          }
           cu_first = false;
         }
-        compute_step<KV, D>(buf[st], qc, acc, lsum, m, sl2,
-                            ROWS ? 32 * (cu.x - cu.x0) : 32 * cu.x, cu.ctx, r,
-                            !ROWS || cu.sub < 0 || cm == cu.sub);
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          // a tile past the pair's columns (a narrow unit) has nothing to compute
+          if (t > 0 && 16 * t >= pair_cols<ROWS>(a, cu)) continue;
+          compute_step<KV, D>(buf[st], qc[t], acc[t], lsum[t], m[t], sl2,
+                              ROWS ? 32 * (cu.x - cu.x0) : 32 * cu.x, cu.ctx, r,
+                              !ROWS || cu.sub < 0 || cm[t] == cu.sub);
+        }
         --rem;
         if (++cu.x == cu.n || rem == 0) {
-          write_segment<D, ROWS>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec,
-                                 seg0_cols);
+          write_segment<D, ROWS, NQ>(a, cu, w, q, acc, lsum, m, r, c, lane, stage, n_out, n_rec,
+                                     seg0_cols);
           if (rem > 0) {
             next_pair<ROWS>(cu, a, rows, lens, hkv, max_ctx);
 #pragma unroll
-            for (int j = 0; j < D / 16; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            lsum = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            m = kMStart;
+            for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+              for (int j = 0; j < D / 16; ++j) acc[t][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+              lsum[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+              m[t] = kMStart;
+            }
           }
         } else if (ROWS && cu.x == cu.xe) {
           next_span(cu, a, lens);
@@ -1141,7 +1207,7 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 // get zeros here.
 //
 // A thread owns 4 consecutive output elements (a float4 of one head's row) of
-// up to kMergeMaxChunks / kMergeThreads such chunks; when the pair has fewer
+// up to (16 x 128 / 4) / kMergeThreads such chunks; when the pair has fewer
 // chunks than threads, the spare threads split the pieces into groups.  Each
 // thread runs the merge as one online pass over its pieces, loading a
 // piece's (max, sum) and its partial row together, so a workgroup waits for
@@ -1149,7 +1215,6 @@ __global__ __launch_bounds__(64, MfmaTuning<KV>::waves) void decode_mfma_kernel(
 // The groups' partial results are combined through LDS.  Batches of few pairs
 // (long contexts, many pieces each) get a workgroup per (pair, query head).
 constexpr int kMergeThreads = 256;
-constexpr int kMergeMaxChunks = kMaxGroup * 128 / 4;   // 16 heads of 128 dimensions
 
 template <typename QT, int D, int NT, bool ROWS, bool SPLIT>
 __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
@@ -1178,15 +1243,15 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
     // (16-row slots); a sequence outside every unit is left alone
     const int4 sr = a.seq_rows[s];
     const int u = sr.x, mem = sr.y;
-    if (u < 0 || u >= a.num_rows || mem < 0 || (mem + 1) * g > kMaxGroup) return;
+    if (u < 0 || u >= a.num_rows || mem < 0 || (mem + 1) * g > kUnitCols) return;
     const int2 rec = a.recs[int64_t(u) * a.num_kv_heads + kvh];
     const int u0 = min(max(rec.x, 0), kMaxWorkers - 1);
     count = min(rec.y, kMaxWorkers - u0);
     if (count <= 1) return;                          // written directly by the decode kernel
-    first0 = int64_t(2 * u0 + 1) * kMaxGroup + mem * g;
+    first0 = int64_t(2 * u0 + 1) * kUnitCols + mem * g;
     head_step = 1;
-    stride = 2 * kMaxGroup;
-    fix = -kMaxGroup;
+    stride = 2 * kUnitCols;
+    fix = -kUnitCols;
   } else {
     const int proto = a.hdr[0];
     const int2 rec = a.recs[pair];
@@ -1308,14 +1373,16 @@ static WsLayout ws_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_di
 }
 
 // Shared-prefix decode workspace: header | records of the (unit, KV head) pairs |
-// partial rows: the workers' two slots of 16 rows each.
-static WsLayout ws_layout_rows(int32_t num_rows, int32_t num_kv_heads, int32_t head_dim) {
+// partial rows: the workers' two slots of kUnitCols rows each (for the workers
+// the shared-prefix kernel runs on the current device).
+static WsLayout ws_layout_rows(int32_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t workers) {
   WsLayout w;
   w.parts = 1;
   w.pairs = int64_t(num_rows) * num_kv_heads;
   w.recs_off = 256;
   w.ml_off = w.recs_off + align256(size_t(w.pairs) * sizeof(int2));
-  w.rows = 2 * int64_t(kMaxWorkers) * kMaxGroup;
+  w.rows = 2 * workers * kUnitCols;
   w.acc_off = w.ml_off + align256(size_t(w.rows) * 2 * sizeof(float));
   w.total = w.acc_off + size_t(w.rows) * head_dim * sizeof(float);
   return w;
@@ -1416,6 +1483,24 @@ static int64_t mfma_workers_d(int kv, int bs, bool shared) {
                     : mfma_workers_of<KV_BF16, D, 32>(shared);
 }
 
+// Persistent workers of the shared-prefix decode on the current device.
+template <int D>
+static int64_t rows_workers_d(int kv, int bs) {
+  auto w = [](auto kernel) { return std::min<int64_t>(kMaxWorkers, resident_workers(kernel)); };
+  if (kv == PKV_FP8_E4M3)
+    return bs == 8    ? w(decode_mfma_kernel<KV_FP8, D, 8, true, true>)
+           : bs == 16 ? w(decode_mfma_kernel<KV_FP8, D, 16, true, true>)
+                      : w(decode_mfma_kernel<KV_FP8, D, 32, true, true>);
+  return bs == 8    ? w(decode_mfma_kernel<KV_BF16, D, 8, true, true>)
+         : bs == 16 ? w(decode_mfma_kernel<KV_BF16, D, 16, true, true>)
+                    : w(decode_mfma_kernel<KV_BF16, D, 32, true, true>);
+}
+
+static int64_t rows_workers(const pkv_cache_desc* c) {
+  return c->head_dim == 64 ? rows_workers_d<64>(c->kv_dtype, c->block_size)
+                           : rows_workers_d<128>(c->kv_dtype, c->block_size);
+}
+
 // The shared-prefix decode reads each shared block once, so it always streams.
 template <int D, int BS>
 static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, bool rows, hipStream_t s) {
@@ -1468,6 +1553,7 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
                    int32_t partition_size, void* workspace, size_t workspace_bytes,
                    DecodeArgs* a, WsLayout* lay, int32_t num_rows = -1,
                    const WsLayout* fixed = nullptr) {
+  // num_rows >= 0: a shared-prefix decode, whose layout comes in `fixed`
   int rc = check_desc(c);
   if (rc) return rc;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -1494,9 +1580,8 @@ static int prepare(const void* q, int32_t q_dtype, const void* k_pool, const voi
     return fail(PKV_E_UNSUPPORTED, "q %s with a %s pool", dtype_name(q_dtype),
                 dtype_name(c->kv_dtype));
   *lay = fixed ? *fixed
-        : num_rows >= 0 ? ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim)
-                        : ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim,
-                                    max_context_len, partition_size);
+               : ws_layout(std::max(num_seqs, 1), num_q_heads, c->head_dim, max_context_len,
+                           partition_size);
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
     return fail(PKV_E_INVAL, "NULL pointer");
@@ -1699,8 +1784,8 @@ extern "C" int pkv_time_next_decode(void* start_event, void* stop_event) {
 }
 
 extern "C" size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows) {
-  if (check_desc(c) || num_rows < 0) return 0;
-  return ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim).total;
+  if (check_desc(c) || num_rows < 0 || c->kv_dtype == PKV_F32) return 0;
+  return ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim, rows_workers(c)).total;
 }
 
 extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const void* k_pool,
@@ -1715,14 +1800,19 @@ extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const 
   clear_error();
   if (num_rows < 0) return fail(PKV_E_INVAL, "negative num_rows");
   if (phases < 1 || phases > 3) return fail(PKV_E_INVAL, "phases must be 1, 2 or 3");
-  DecodeArgs a;
-  WsLayout lay;
-  int rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
-                   num_seqs, num_q_heads, scale, out, max_context_len, partition_size, workspace,
-                   workspace_bytes, &a, &lay, num_rows);
-  if (rc || num_seqs == 0) return rc;
+  int rc = check_desc(c);
+  if (rc) return rc;
   if (c->kv_dtype == PKV_F32)
     return fail(PKV_E_UNSUPPORTED, "the shared-prefix decode needs a bf16 or fp8 pool");
+  const int64_t workers = rows_workers(c);
+  const WsLayout rows_lay = ws_layout_rows(num_rows, c->num_kv_heads, c->head_dim, workers);
+  DecodeArgs a;
+  WsLayout lay;
+  rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
+               num_seqs, num_q_heads, scale, out, max_context_len, partition_size, workspace,
+               workspace_bytes, &a, &lay, num_rows, &rows_lay);
+  if (rc || num_seqs == 0) return rc;
+  a.workers = int32_t(workers);
   if (!rows || !seq_rows || num_rows == 0) return fail(PKV_E_INVAL, "no rows");
   if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(seq_rows)) & 15u)
     return fail(PKV_E_INVAL, "rows and seq_rows must be 16-byte aligned");

@@ -5,8 +5,8 @@
 // blocks between sequences"): their keys and values are the same bytes, so
 // the decode reads them once for all the sharers' queries.
 //
-// A group is a run of consecutive batch sequences (at most 16 / group size of
-// them, the matrix-core kernel's query columns) whose tables start with the
+// A group is a run of consecutive batch sequences (at most 32 / group size of
+// them, the shared-prefix kernel's two 16-column query tiles) whose tables start with the
 // same nb >= min_shared_blocks block ids; nb is also kept below every
 // member's last block, so each member has tokens after the shared part.  A
 // group becomes one unit {first member, nb * B shared tokens, members, 0};
@@ -29,7 +29,7 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
                 num_seqs, max_blocks, block_size, group);
   if (num_seqs > 0 && (!tables || !lens || !rows || !seq_rows))
     return fail(PKV_E_INVAL, "NULL pointer");
-  const int max_members = 16 / group;
+  const int max_members = 32 / group;   // query columns of a unit (two 16-column tiles)
   const int min_nb = std::max(1, min_shared_blocks);
   // full blocks of sequence i before its last token: the most it can share
   auto shareable = [&](int i) {

@@ -14,7 +14,7 @@ def _units(tables, lens, B, g, min_blocks=1):
 def _check(tables, lens, B, g, min_blocks, units, seq_rows):
     """Units tile the batch in order; a unit's members hold the same block ids over its
     shared tokens (whole blocks, at least min_blocks of them, short of every member's last
-    token); member counts obey the 16-column limit; seq_rows maps each sequence to its
+    token); member counts obey the 32-column limit; seq_rows maps each sequence to its
     unit and position."""
     tables = np.asarray(tables)
     S = len(lens)
@@ -22,7 +22,7 @@ def _check(tables, lens, B, g, min_blocks, units, seq_rows):
     assert (units[:, 3] == 0).all()
     nxt = 0
     for u, (s0, T, M, _) in enumerate(units):
-        assert s0 == nxt and 1 <= M <= max(1, 16 // g)
+        assert s0 == nxt and 1 <= M <= max(1, 32 // g)
         nxt += M
         assert T % B == 0
         if M == 1:
@@ -62,18 +62,25 @@ def test_shared_part_stays_below_every_members_last_block():
 
 
 def test_member_limit_splits_large_families():
-    B, g = 16, 4                                   # 16 / 4 = 4 members per unit
-    S = 10
+    B, g = 16, 4                                   # 32 / 4 = 8 members per unit
+    S = 19
     t = np.full((S, 4), -1, dtype=np.int32)
     t[:, :2] = [40, 41]
     t[:, 2] = np.arange(S)
     lens = np.full(S, 40, dtype=np.int32)
     units, sr = _units(t, lens, B, g)
-    assert units.tolist() == [[0, 32, 4, 0], [4, 32, 4, 0], [8, 32, 2, 0]]
+    assert units.tolist() == [[0, 32, 8, 0], [8, 32, 8, 0], [16, 32, 3, 0]]
     _check(t, lens, B, g, 1, units, sr)
-    # groups of 16 heads leave one column per member: no sharing at all
+    # groups of 16 heads: two members per unit (the two 16-column tiles)
     units, sr = _units(t, lens, B, 16)
-    assert len(units) == S and (units[:, 1] == 0).all() and (units[:, 2] == 1).all()
+    assert units[:, 2].tolist() == [2] * 9 + [1] and (units[:9, 1] == 32).all()
+    _check(t, lens, B, 16, 1, units, sr)
+    # one head per member: 32 members
+    t2 = np.full((40, 3), -1, dtype=np.int32)
+    t2[:, :2] = [7, 9]
+    t2[:, 2] = np.arange(100, 140)
+    units, sr = _units(t2, np.full(40, 33, dtype=np.int32), B, 1)
+    assert units.tolist() == [[0, 32, 32, 0], [32, 32, 8, 0]]
 
 
 def test_minimum_shared_blocks():
@@ -160,11 +167,12 @@ def test_prefix_order_makes_sharers_consecutive():
             assert pos[-1] - pos[0] + 1 == len(pos)
     units, sr = pkv.prefix_rows(t[order], lens[order], B, 4, 1)
     _check(t[order], lens[order], B, 4, 1, units, sr)
-    # every family of n sequences gives ceil(n / 4) units with its prompt's blocks shared
+    # every family of n sequences gives ceil(n / 8) units with its prompt's blocks shared
+    # (8 members of 4 heads fill the 32 query columns)
     for k in range(5):
         n = int((fam == k).sum())
         got = [u for u in units if fam[order][u[0]] == k]
-        assert len(got) == -(-n // 4)
+        assert len(got) == -(-n // 8)
         assert all(u[1] == len(prompts[k]) * B for u in got if u[2] > 1)
 
 

@@ -414,6 +414,7 @@ CONFIGS: Dict[str, Callable[[], Workload]] = {
     "8b-gqa-bf16": lambda: gqa8b("bf16"),
     "8b-gqa-bf16-b8": lambda: gqa8b("bf16", 8),
     "8b-gqa-bf16-b32": lambda: gqa8b("bf16", 32),
+    "8b-gqa-fp8-b32": lambda: gqa8b("fp8", 32),
     "mqa-16q-bf16": mqa_bf16,
     "shared-prefix-bf16": shared_prefix_bf16,
     "chat-prefix-cache-bf16": chat_prefix_cache_bf16,
