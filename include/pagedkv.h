@@ -196,8 +196,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                 taking the remainder, run in parallel and merged.  MFMA
  *                 kernel: the batch's steps are shared out evenly over the
  *                 persistent workers, each taking at least P tokens (0 = no
- *                 lower bound); contexts that cross a worker boundary are
- *                 merged.
+ *                 lower bound) as long as that leaves at least half the
+ *                 workers some steps; contexts that cross a worker boundary
+ *                 are merged.
  *   workspace     device buffer of >= pkv_decode_workspace_bytes(...) bytes
  * The result does not depend on the split beyond rounding; for given context
  * lengths and partition_size it depends only on the logical order of each
@@ -248,7 +249,8 @@ int pkv_paged_attn_decode_ex(const void* q, int32_t q_dtype,
  *   The vector kernel's pieces are the partitions of partition_size tokens;
  *   the MFMA kernel's pieces are the parts of a context that fall to different
  *   persistent workers (each worker takes an equal share of all 32-token steps
- *   of the batch, and at least partition_size tokens when that is non-zero).
+ *   of the batch, and at least partition_size tokens when that is non-zero and
+ *   leaves at least half the workers some steps).
  * pkv_paged_attn_merge -- combines the pieces of every context that has more
  *   than one, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max m)
  *   (the rescaling of the running softmax, FlashAttention-style tiling,

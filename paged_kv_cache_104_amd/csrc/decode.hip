@@ -61,7 +61,8 @@ struct DecodeArgs {
   int32_t num_blocks;   // pool blocks (block ids outside [0, num_blocks) are skipped)
   int32_t max_ctx;      // contexts are cut at this host-known bound
   int32_t part_tokens;  // vector kernel: partition length (0 = whole context);
-                        // MFMA kernel: least tokens per worker (0 = balance only)
+                        // MFMA kernel: least tokens per worker while at least
+                        // half the workers get steps (0 = balance only)
   int32_t max_parts;    // vector kernel: partitions of the longest context
   int32_t workers;      // MFMA kernel: persistent workers launched
   float qk_scale_log2;  // scale * log2(e) * k_scale
@@ -833,7 +834,12 @@ __device__ __forceinline__ bool find_start(const DecodeArgs& a, const int4* __re
     for (int u = 0; u < 4; ++u) sum += v[u];
   }
   total = __builtin_amdgcn_readfirstlane(wave_sum(sum)) * hkv;
-  q = max(max(1, a.part_tokens >> 5), (total + a.workers - 1) / a.workers);
+  // Steps per worker: an even share, or more when partition_size asks for longer
+  // pieces, but never so many that fewer than half the workers get steps (a short
+  // stream over a few workers runs at their latency, not at the memory's rate).
+  const int q_even = (total + a.workers - 1) / a.workers;
+  const int q_half = (2 * total + a.workers - 1) / a.workers;
+  q = max(q_even, min(max(1, a.part_tokens >> 5), q_half));
   if (int64_t(w) * q >= total) return false;
   const int target = w * q;
   int base = 0;  // steps of one KV head of the units before the chunk
