@@ -159,12 +159,14 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     # forked samples share blocks: read them once for all sharers (shared-prefix units), or
     # per sequence with the shared blocks kept cached
     if use_rows:
-        rows_d, seq_rows_d = batch.shared_prefix_rows(wl.group, 1)
+        rows_d, seq_rows_d, reread = batch.shared_prefix_rows(wl.group, 1)
         n_rows = int(rows_d.shape[0])
         ws_bytes = pkv.rows_workspace_bytes(desc, n_rows)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         log(f"shared-prefix units: {n_rows} units for {S} sequences, "
-            f"{int((rows_d[:, 2] > 1).sum())} with shared blocks")
+            f"{int((rows_d[:, 2] > 1).sum())} with shared blocks, "
+            f"{int(rows_d[:, 3].sum())} read again by other units"
+            f"{' (cached loads)' if reread else ''}")
     elif shared:
         impl |= pkv.IMPL_SHARED_BLOCKS
     kv_bytes = np.zeros(total)
@@ -196,14 +198,16 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         if use_rows:
             pkv.paged_attn_decode_rows(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                        wl.scale, out, desc, max_ctx, partition_size, rows_d,
-                                       seq_rows_d, workspace=workspace, phases=1)
+                                       seq_rows_d, workspace=workspace, phases=1,
+                                       shared_blocks=reread)
         else:
             pkv.paged_attn_partials(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                     wl.scale, out, desc, max_ctx, partition_size, workspace, impl)
         if use_rows:
             pkv.paged_attn_decode_rows(q, cache.k_pool, cache.v_pool, batch.tables, batch.lens,
                                        wl.scale, out, desc, max_ctx, partition_size, rows_d,
-                                       seq_rows_d, workspace=workspace, phases=2)
+                                       seq_rows_d, workspace=workspace, phases=2,
+                                       shared_blocks=reread)
         else:
             pkv.paged_attn_merge(out, batch.lens, wl.num_kv_heads, max_ctx, partition_size,
                                  workspace)
@@ -262,7 +266,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
                 t_attn_diag=t_attn_diag, host_s=host_s[warmup:warmup + steps],
                 t_attn_flush=t_attn_flush, t_merge_flush=t_merge_flush, kv_flush=kv_flush,
                 max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs, shared=shared,
-                rows=use_rows,
+                rows=use_rows, rows_cached=use_rows and reread,
                 unique_ratio=unique_bytes / float(kvb[-1]))
 
 
@@ -572,7 +576,8 @@ def main() -> int:
             "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
             "mean_context": round(mean_ctx, 1), "partition_size": ps,
-            "kv_loads": ("shared-prefix units" if r["rows"] else
+            "kv_loads": ("shared-prefix units, cached loads" if r["rows_cached"] else
+                         "shared-prefix units" if r["rows"] else
                          "cached (shared blocks)" if r["shared"] else "streaming"),
             "prefix_cache": r["cache_stats"],
             "description": wl.description,

@@ -316,26 +316,32 @@ int pkv_paged_attn_decode_noalloc(const void* q, int32_t q_dtype, const void* k_
  * sharing"; glossary "Sharing blocks between sequences").  The keys and
  * values of those blocks are the same bytes for every sharer, so the decode
  * can read them once and score all the sharers' queries against them: the
- * matrix-core kernel has 16 query columns, of which a head group uses
- * num_q_heads / num_kv_heads.  The result is the same attention as
+ * matrix-core kernel has 32 query columns (two 16-column tiles), of which a
+ * head group uses num_q_heads / num_kv_heads.  The result is the same attention as
  * pkv_paged_attn_decode gives (softmax over each sequence's whole context),
  * up to rounding: a member's running softmax goes on from the shared tokens
  * to its own, and a unit split between workers is merged as a split context
  * is.
  *
  * Units: the decode runs over units instead of sequences.  Unit u is int32
- * [4] {seq0, shared_tokens, members, 0}: the `members` consecutive sequences
- * seq0 .. seq0 + members - 1 (at most 16 / group) hold the same block ids
- * over their first shared_tokens tokens (a multiple of block_size, at most
- * every member's context length).  The kernel reads those tokens once,
- * through seq0's table, scoring every member's queries, then each member's
- * remaining tokens through its own table.  seq_rows[s] = {unit, member index
- * within the unit, 0, 0}.  A unit {s, 0, 1, 0} is a plain sequence.
+ * [4] {seq0, shared_tokens, members, reread}: the `members` consecutive
+ * sequences seq0 .. seq0 + members - 1 (at most 32 / group) hold the same
+ * block ids over their first shared_tokens tokens (a multiple of block_size,
+ * at most every member's context length).  The kernel reads those tokens
+ * once, through seq0's table, scoring every member's queries, then each
+ * member's remaining tokens through its own table.  reread = 1 marks a unit
+ * whose shared blocks other units or sequences of the batch read too (a prompt
+ * with more sharers than one unit holds); the kernel does not read the field,
+ * it tells the caller to pass PKV_IMPL_SHARED_BLOCKS (below).  seq_rows[s] =
+ * {unit, member index within the unit, 0, 0}.  A unit {s, 0, 1, 0} is a plain
+ * sequence.
  */
 
 /* Build the units for a batch on the host: runs of consecutive sequences (at
- * most 16 / group) whose tables start with the same >= min_shared_blocks
- * block ids share those blocks, kept below each member's last block.
+ * most 32 / group) whose tables start with the same >= min_shared_blocks
+ * block ids share those blocks, kept below each member's last block.  A
+ * unit's reread is 1 when sequences outside it start with its first block
+ * too (a prompt with more sharers than one unit holds).
  *   tables   host int32 [num_seqs][max_blocks] (the batch's block tables)
  *   lens     host int32 [num_seqs] context lengths
  *   rows     host int32 [num_seqs][4] out (units); seq_rows host int32 [num_seqs][4] out
@@ -359,13 +365,18 @@ int32_t pkv_prefix_order(const int32_t* tables, const int32_t* lens, int32_t num
 
 /* Workspace bytes of pkv_paged_attn_decode_rows for num_rows units (0 on
  * invalid arguments): a header, one record per (unit, KV head) and the
- * persistent workers' partial-segment slots (two of 16 rows each). */
+ * persistent workers' partial-segment slots (two of 32 rows each). */
 size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows);
 
 /* Decode attention over units (see above); arguments as pkv_paged_attn_decode,
  * plus rows / seq_rows (device int32 [num_rows][4] / [num_seqs][4], 16-byte
  * aligned, e.g. uploaded from pkv_prefix_rows) and phases: 1 the decode
- * kernel, 2 the merge, 3 both (1 then 2 on the same workspace and stream).
+ * kernel, 2 the merge, 3 both (1 then 2 on the same workspace and stream),
+ * optionally or-ed with PKV_IMPL_SHARED_BLOCKS: read K and V with ordinary
+ * loads instead of streaming them, which pays when some unit has reread = 1
+ * (its shared blocks are read again by other units of the launch and then hit
+ * in the Infinity Cache) and costs a few percent otherwise.  The result is the
+ * same either way.
  * bf16 or fp8 pools only (PKV_E_UNSUPPORTED for f32).  Unit fields are
  * trusted only as far as memory safety: out-of-range sequences and members
  * are cut, shared tokens are cut to whole blocks of seq0's context, and a

@@ -555,9 +555,12 @@ def rows_workspace_bytes(desc: CacheDesc, num_rows: int) -> int:
 
 def paged_attn_decode_rows(q, k_pool, v_pool, block_tables, context_lens, scale: float, out,
                            desc: CacheDesc, max_context_len: int, partition_size: int,
-                           rows, seq_rows, workspace=None, phases: int = 3, stream=None):
+                           rows, seq_rows, workspace=None, phases: int = 3, stream=None,
+                           shared_blocks: bool = False):
     """Shared-prefix decode (see include/pagedkv.h): ``rows`` / ``seq_rows`` are device int32
-    tensors [R, 4] / [S, 4] (``prefix_rows`` builds them on the host)."""
+    tensors [R, 4] / [S, 4] (``prefix_rows`` builds them on the host).  ``shared_blocks``
+    adds PKV_IMPL_SHARED_BLOCKS to ``phases`` (cached K/V loads; for batches in which some
+    unit's reread field is set)."""
     torch = _torch()
     S, Hq, D = q.shape
     if rows.dtype != torch.int32 or seq_rows.dtype != torch.int32:
@@ -576,7 +579,8 @@ def paged_attn_decode_rows(q, k_pool, v_pool, block_tables, context_lens, scale:
             _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(desc),
             _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, Hq,
             float(scale), _ptr(out), int(max_context_len), int(partition_size), _ptr(rows), R,
-            _ptr(seq_rows), _ptr(workspace), ws_bytes, _stream(stream), int(phases)))
+            _ptr(seq_rows), _ptr(workspace), ws_bytes, _stream(stream),
+            int(phases) | (IMPL_SHARED_BLOCKS if shared_blocks else 0)))
     return out
 
 

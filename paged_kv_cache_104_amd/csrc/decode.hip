@@ -1507,17 +1507,23 @@ static int64_t rows_workers(const pkv_cache_desc* c) {
                            : rows_workers_d<128>(c->kv_dtype, c->block_size);
 }
 
-// The shared-prefix decode reads each shared block once, so it always streams.
+// `shared`: blocks are read again within the launch (by other sequences of a
+// plain decode, or by other units of a shared-prefix decode), so K and V are read
+// with ordinary loads that leave them in the caches; otherwise they stream.  The
+// choice is per launch: a load whose kind depended on the step would be merged by
+// the compiler into one ordinary load for both cases.
 template <int D, int BS>
 static int dispatch_mfma(const DecodeArgs& a, int kv, bool shared, bool rows, hipStream_t s) {
   if (kv == PKV_BF16)
-    return rows     ? launch_mfma<KV_BF16, D, BS, true, true>(a, s)
-           : shared ? launch_mfma<KV_BF16, D, BS, false, false>(a, s)
-                    : launch_mfma<KV_BF16, D, BS, true, false>(a, s);
+    return rows ? (shared ? launch_mfma<KV_BF16, D, BS, false, true>(a, s)
+                          : launch_mfma<KV_BF16, D, BS, true, true>(a, s))
+                : (shared ? launch_mfma<KV_BF16, D, BS, false, false>(a, s)
+                          : launch_mfma<KV_BF16, D, BS, true, false>(a, s));
   if (kv == PKV_FP8_E4M3)
-    return rows     ? launch_mfma<KV_FP8, D, BS, true, true>(a, s)
-           : shared ? launch_mfma<KV_FP8, D, BS, false, false>(a, s)
-                    : launch_mfma<KV_FP8, D, BS, true, false>(a, s);
+    return rows ? (shared ? launch_mfma<KV_FP8, D, BS, false, true>(a, s)
+                          : launch_mfma<KV_FP8, D, BS, true, true>(a, s))
+                : (shared ? launch_mfma<KV_FP8, D, BS, false, false>(a, s)
+                          : launch_mfma<KV_FP8, D, BS, true, false>(a, s));
   return fail(PKV_E_UNSUPPORTED, "the MFMA kernel needs a bf16 or fp8 pool");
 }
 
@@ -1805,7 +1811,10 @@ extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const 
                                           size_t workspace_bytes, void* stream, int32_t phases) {
   clear_error();
   if (num_rows < 0) return fail(PKV_E_INVAL, "negative num_rows");
-  if (phases < 1 || phases > 3) return fail(PKV_E_INVAL, "phases must be 1, 2 or 3");
+  const bool cached = (phases & PKV_IMPL_SHARED_BLOCKS) != 0;
+  phases &= ~PKV_IMPL_SHARED_BLOCKS;
+  if (phases < 1 || phases > 3)
+    return fail(PKV_E_INVAL, "phases must be 1, 2 or 3 (optionally with PKV_IMPL_SHARED_BLOCKS)");
   int rc = check_desc(c);
   if (rc) return rc;
   if (c->kv_dtype == PKV_F32)
@@ -1828,8 +1837,8 @@ extern "C" int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (phases & 1) {
     rc = c->head_dim == 64
-             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, true, false, true, s)
-             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, true, false, true, s);
+             ? dispatch_bs<64>(a, c->block_size, c->kv_dtype, q_dtype, true, cached, true, s)
+             : dispatch_bs<128>(a, c->block_size, c->kv_dtype, q_dtype, true, cached, true, s);
     if (rc) return rc;
   }
   if (phases & 2) return launch_merge(a, c->head_dim, q_dtype, s, true);

@@ -9,10 +9,15 @@
 // them, the shared-prefix kernel's two 16-column query tiles) whose tables start with the
 // same nb >= min_shared_blocks block ids; nb is also kept below every
 // member's last block, so each member has tokens after the shared part.  A
-// group becomes one unit {first member, nb * B shared tokens, members, 0};
-// any other sequence is a unit of its own {seq, 0, 1, 0}.
+// group becomes one unit {first member, nb * B shared tokens, members, reread};
+// any other sequence is a unit of its own {seq, 0, 1, 0}.  reread is 1 when
+// sequences outside the unit start with the unit's first block too (a prompt
+// with more sharers than one unit holds): other units or sequences of the
+// batch read the unit's shared blocks again, and the kernel then reads them
+// with cached loads.
 #include <algorithm>
 #include <cstdint>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
@@ -59,6 +64,11 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
     }
     ++nr;
   };
+  // readers of each first block: sequences with a context whose table starts with it
+  std::unordered_map<int32_t, int> first_readers;
+  for (int i = 0; i < num_seqs && max_blocks > 0; ++i)
+    if (lens[i] > 0 && tables[int64_t(i) * max_blocks] >= 0)
+      ++first_readers[tables[int64_t(i) * max_blocks]];
   for (int i = 0; i < num_seqs;) {
     int nb = shareable(i);
     int n = 1;
@@ -70,6 +80,7 @@ extern "C" int32_t pkv_prefix_rows(const int32_t* tables, const int32_t* lens, i
     }
     if (n >= 2 && nb >= min_nb) {
       put_unit(i, nb * block_size, n);
+      rows[int64_t(nr - 1) * 4 + 3] = first_readers[tables[int64_t(i) * max_blocks]] > n;
       i += n;
     } else {
       put_unit(i, 0, 1);

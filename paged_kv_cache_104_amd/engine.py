@@ -239,13 +239,16 @@ class DecodeBatch:
 
     def shared_prefix_rows(self, group: int, min_shared_blocks: int = 1):
         """Units of the shared-prefix decode for the batch as it stands, uploaded:
-        ``(rows, seq_rows)`` device int32.  Sequences that share leading blocks must be
-        consecutive in the batch.  The units stay valid while no shared block is replaced
-        (appends only grow the contexts after the shared part)."""
+        ``(rows, seq_rows, reread)``, device int32 tensors and whether some unit's shared
+        blocks are read by other units too (then pass ``shared_blocks=True`` to the decode).
+        Sequences that share leading blocks must be consecutive in the batch.  The units
+        stay valid while no shared block is replaced (appends only grow the contexts after
+        the shared part)."""
         import torch
 
         t, lens = self.cache.bm.block_tables(self.seqs, self.max_blocks)
         rows, seq_rows = prefix_rows(t, lens, self.cache.desc.block_size, group,
                                      min_shared_blocks)
         dev = self.cache.device
-        return (torch.from_numpy(rows).to(dev), torch.from_numpy(seq_rows).to(dev))
+        return (torch.from_numpy(rows).to(dev), torch.from_numpy(seq_rows).to(dev),
+                bool(rows[:, 3].any()))

@@ -133,3 +133,16 @@ def test_timing_hook_validation():
     assert L.pkv_time_next_decode(None, None) == 0
     assert L.pkv_time_next_decode(16, None) == pkv.PKV_E_INVAL
     assert L.pkv_time_next_decode(None, 16) == pkv.PKV_E_INVAL
+
+
+@pytest.mark.parametrize("phases", [0, 4, 0x100, 0x200 | 3, -1])
+def test_shared_prefix_decode_rejects_bad_phases(phases):
+    """phases is 1, 2 or 3, optionally with the cached-loads hint; anything else is refused
+    before any device work."""
+    import paged_kv_cache_104_amd as pkv
+
+    rc = pkv.lib.pkv_paged_attn_decode_rows(None, 1, None, None, None, None, 1, None, 0, 8,
+                                            0.1, None, 16, 0, None, 1, None, None, 0, None,
+                                            phases)
+    assert rc == -1
+    assert b"phases" in pkv.lib.pkv_last_error()

@@ -13,14 +13,15 @@ from test_gpu_cache_ops import _shared_prefix_small
 pytestmark = pytest.mark.gpu
 
 
-def _rows_decode(g, rows, seq_rows, ps, phases=3):
+def _rows_decode(g, rows, seq_rows, ps, shared_blocks=False):
     import paged_kv_cache_104_amd as pkv
 
     torch = torch_mod()
     wl = g.wl
     out = torch.empty_like(g.q)
     pkv.paged_attn_decode_rows(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens, wl.scale,
-                               out, g.desc, wl.max_context_len, ps, rows, seq_rows)
+                               out, g.desc, wl.max_context_len, ps, rows, seq_rows,
+                               shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return out
 
@@ -75,6 +76,26 @@ def test_rows_match_oracle_and_plain_decode(case):
         err = np.abs(out - ref).max()
         assert err <= tol, (ps, err)
         assert np.abs(out - plain).max() <= tol
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prompt_wider_than_a_unit_reread_with_cached_loads(kv):
+    """12 samples of 4 heads per prompt: units of 8 and 4 members share the prompt, both
+    flagged as read again; the decode with cached loads (the launch hint) gives the
+    streaming decode's result bit for bit, within tolerance of the oracle."""
+    torch = torch_mod()
+    wl = _shared_prefix_small(415, prompts=2, n=12, prefix=200, D=128, Hkv=2, g=4,
+                              kv_dtype=kv)
+    print(f"rows reread case {kv}", flush=True)
+    g = GpuState(wl)
+    ref = oracle_decode(oracle_run(wl))
+    rows, seq_rows, rows_d, sr_d = _rows(g, 4)
+    assert rows[:, 2].tolist() == [8, 4, 8, 4] and (rows[:, 3] == 1).all(), rows
+    for ps in (0, 128):
+        a = _rows_decode(g, rows_d, sr_d, ps)
+        b = _rows_decode(g, rows_d, sr_d, ps, shared_blocks=True)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), ps
+        assert np.abs(out_host(b) - ref).max() <= TOL[kv], ps
 
 
 def test_no_shared_run_is_the_plain_decode_bit_for_bit():

@@ -15,13 +15,17 @@ def _check(tables, lens, B, g, min_blocks, units, seq_rows):
     """Units tile the batch in order; a unit's members hold the same block ids over its
     shared tokens (whole blocks, at least min_blocks of them, short of every member's last
     token); member counts obey the 32-column limit; seq_rows maps each sequence to its
-    unit and position."""
+    unit and position; a unit's reread flag says whether sequences outside it start with
+    its first block too."""
     tables = np.asarray(tables)
+    lens = np.asarray(lens)
     S = len(lens)
     assert seq_rows.shape == (S, 4) and (seq_rows[:, 2:] == 0).all()
-    assert (units[:, 3] == 0).all()
+    firsts = tables[:, 0] if tables.shape[1] else np.full(S, -1)
     nxt = 0
-    for u, (s0, T, M, _) in enumerate(units):
+    for u, (s0, T, M, reread) in enumerate(units):
+        readers = int(((lens > 0) & (firsts >= 0) & (firsts == firsts[s0])).sum()) if S else 0
+        assert reread == (1 if T > 0 and readers > M else 0)
         assert s0 == nxt and 1 <= M <= max(1, 32 // g)
         nxt += M
         assert T % B == 0
@@ -69,7 +73,9 @@ def test_member_limit_splits_large_families():
     t[:, 2] = np.arange(S)
     lens = np.full(S, 40, dtype=np.int32)
     units, sr = _units(t, lens, B, g)
-    assert units.tolist() == [[0, 32, 8, 0], [8, 32, 8, 0], [16, 32, 3, 0]]
+    # the prompt has more sharers than a unit holds: every unit flags its shared blocks
+    # as read again
+    assert units.tolist() == [[0, 32, 8, 1], [8, 32, 8, 1], [16, 32, 3, 1]]
     _check(t, lens, B, g, 1, units, sr)
     # groups of 16 heads: two members per unit (the two 16-column tiles)
     units, sr = _units(t, lens, B, 16)
@@ -80,7 +86,25 @@ def test_member_limit_splits_large_families():
     t2[:, :2] = [7, 9]
     t2[:, 2] = np.arange(100, 140)
     units, sr = _units(t2, np.full(40, 33, dtype=np.int32), B, 1)
-    assert units.tolist() == [[0, 32, 32, 0], [32, 32, 8, 0]]
+    assert units.tolist() == [[0, 32, 32, 1], [32, 32, 8, 1]]
+    # all sharers in one unit: nothing else reads the prompt
+    units, sr = _units(t2[:32], np.full(32, 33, dtype=np.int32), B, 1)
+    assert units.tolist() == [[0, 32, 32, 0]]
+
+
+def test_reread_flag_counts_sharers_outside_the_unit():
+    B = 4
+    # sequences 0-1 share blocks 5, 6; sequence 2 starts with block 5 too but has a single
+    # full block before its last token, below the two-block minimum; sequence 3 is alone
+    t = np.array([[5, 6, 1, -1], [5, 6, 2, -1], [5, 3, -1, -1], [8, 9, -1, -1]], dtype=np.int32)
+    lens = np.array([12, 11, 6, 7], dtype=np.int32)
+    units, sr = _units(t, lens, B, 2, 2)
+    assert units.tolist() == [[0, 8, 2, 1], [2, 0, 1, 0], [3, 0, 1, 0]]
+    _check(t, lens, B, 2, 2, units, sr)
+    # an empty context reads nothing
+    lens[2] = 0
+    units, sr = _units(t, lens, B, 2, 2)
+    assert units.tolist() == [[0, 8, 2, 0], [2, 0, 1, 0], [3, 0, 1, 0]]
 
 
 def test_minimum_shared_blocks():
