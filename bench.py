@@ -338,11 +338,15 @@ def cpu_baseline(wl, seconds: float, seconds_one: float = 5.0):
     }
 
 
-def read_reference(tile_bytes: int, total_bytes: int = READ_REF_BYTES, reps: int = 5):
+def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF_BYTES,
+                   reps: int = 5):
     """The library's plain read probe over a buffer far larger than the last-level cache:
     a sequential stream, and tiles of the workload's (block, KV head) tile size read in a
     random order (as the decode reads its blocks).  Best of a few launch widths, median of
-    ``reps`` launches each (GB/s)."""
+    ``reps`` launches each (GB/s).  ``same_bytes``: random tiles adding up to the decode's
+    own KV bytes per launch, each launch on tiles no earlier launch of that width read
+    (while the buffer holds enough), so that a short launch is set against a read of its
+    own size from HBM, ramp and tail included."""
     import torch
 
     import paged_kv_cache_104_amd as pkv
@@ -367,6 +371,23 @@ def read_reference(tile_bytes: int, total_bytes: int = READ_REF_BYTES, reps: int
                     ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
             best = max(best, n * tile_bytes / float(np.median(ts)) / 1e9)
         res[name] = round(best, 1)
+    m = max(1, min(n, -(-same_bytes // tile_bytes)))
+    best_t = None
+    for wgs in (1024, 2048, 4096, 8192):
+        ts = []
+        for r in range(reps + 1):
+            lo = (r * m) % max(1, n - m + 1)
+            ids = perm[lo:lo + m]
+            ev[0].record()
+            pkv.read_probe(buf, tile_bytes, ids, m, sink, wgs)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if r:
+                ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        t = float(np.median(ts))
+        best_t = t if best_t is None else min(best_t, t)
+    res["same_bytes"] = {"bytes": int(m * tile_bytes), "us": round(best_t * 1e6, 2),
+                         "GBps": round(m * tile_bytes / best_t / 1e9, 1)}
     del buf, perm, sink
     return res
 
@@ -624,10 +645,13 @@ def main() -> int:
     if not args.no_read_reference:
         log("timing the read probe")
         tile = wl.block_size * wl.head_dim * {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
-        ref = read_reference(tile)
+        ref = read_reference(tile, result["roofline"]["algorithmic_bytes_per_launch"])
         result["roofline"]["read_probe_GBps"] = {"tile_bytes": tile, **ref}
         result["roofline"]["stream_frac"] = round(result["roofline"]["achieved"]
                                                   / ref["sequential"], 4)
+        # the flushed decode against a probe launch reading as many bytes from HBM
+        result["roofline"]["same_bytes_frac"] = round(
+            result["roofline"]["achieved_flushed"] / ref["same_bytes"]["GBps"], 4)
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
