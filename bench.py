@@ -630,6 +630,8 @@ def main() -> int:
     }
     flush_gbs = float((r["kv_flush"] / r["t_attn_flush"]).mean()) / 1e9
     result["roofline"]["achieved_flushed"] = round(flush_gbs, 1)
+    # the attention kernels together: the decode and the merge of split contexts
+    merged_gbs = float(r["kv_attn"].mean()) / (float(r["t_attn"].mean()) + float(r["t_merge"].mean())) / 1e9
     if r["shared"]:
         # blocks read by several sequences: the HBM roofline is judged on distinct bytes
         ub = attn_gbs * r["unique_ratio"]
@@ -640,8 +642,11 @@ def main() -> int:
         result["roofline"]["algorithmic_bytes_per_launch"] = int(r["kv_attn"].mean()
                                                                  * r["unique_ratio"])
         result["roofline"]["achieved_flushed"] = round(flush_gbs * r["unique_ratio"], 1)
+        merged_gbs *= r["unique_ratio"]
     result["roofline"]["frac_flushed"] = round(result["roofline"]["achieved_flushed"]
                                                / HBM_PEAK_GBS, 4)
+    result["roofline"]["achieved_decode_and_merge"] = round(merged_gbs, 1)
+    result["roofline"]["frac_decode_and_merge"] = round(merged_gbs / HBM_PEAK_GBS, 4)
     if not args.no_read_reference:
         log("timing the read probe")
         tile = wl.block_size * wl.head_dim * {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
