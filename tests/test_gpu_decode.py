@@ -302,6 +302,22 @@ def test_many_pairs_per_worker(case):
         assert err <= tol, (ps, err)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_batch_of_more_than_256_sequences(kv):
+    """700 short contexts: the matrix-core workers find their start with the chunked scan
+    (each lane's context lengths re-read chunk by chunk), which batches of at most 256
+    sequences never take; ranges start anywhere among the three chunks."""
+    wl = workloads.random_small(333, S=700, Hq=8, Hkv=2, D=128, B=16, max_ctx=90,
+                                kv_dtype=kv, in_dtype="bf16")
+    print(f"700 sequences {kv}", flush=True)
+    ref = oracle_decode(oracle_run(wl))
+    g = GpuState(wl)
+    for ps in (0, 64, 2048):
+        out = out_host(g.decode(ps, IMPLS["mfma"]))
+        err = np.abs(out - ref).max()
+        assert err <= TOL[kv], (ps, err)
+
+
 @pytest.mark.parametrize("impl", [1, 2])
 def test_timing_events_hold_the_kernel(impl):
     """With the timing hook the decode launch records its own start and end: the pair's

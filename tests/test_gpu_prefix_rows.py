@@ -98,6 +98,22 @@ def test_prompt_wider_than_a_unit_reread_with_cached_loads(kv):
         assert np.abs(out_host(b) - ref).max() <= TOL[kv], ps
 
 
+def test_more_than_256_units():
+    """300 prompts of two samples each: 300 units, so the workers find their start with the
+    chunked scan over the unit descriptors (more than one group of 256)."""
+    wl = _shared_prefix_small(416, prompts=300, n=2, prefix=40, D=64, Hkv=2, g=2, max_tail=20)
+    print("300 units", flush=True)
+    g = GpuState(wl)
+    ref = oracle_decode(oracle_run(wl))
+    rows, seq_rows, rows_d, sr_d = _rows(g, 2)
+    assert len(rows) == 300 and (rows[:, 2] == 2).all(), rows[:4]
+    plain = out_host(g.decode(0, 2))
+    for ps in (0, 64):
+        out = out_host(_rows_decode(g, rows_d, sr_d, ps))
+        assert np.abs(out - ref).max() <= TOL[wl.kv_dtype], ps
+        assert np.abs(out - plain).max() <= TOL[wl.kv_dtype], ps
+
+
 def test_no_shared_run_is_the_plain_decode_bit_for_bit():
     torch = torch_mod()
     wl = _shared_prefix_small(410, prompts=2, n=4, prefix=100, D=128, Hkv=2, g=4)
