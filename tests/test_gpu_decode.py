@@ -34,6 +34,11 @@ def _cases():
                     in_dtype="bf16"))
     out.append(dict(seed=292, S=3, Hq=6, Hkv=2, D=128, B=16, max_ctx=100, kv_dtype="bf16",
                     in_dtype="bf16"))
+    # the widest group at the narrow head size, and a two-KV-head 16-group
+    out.append(dict(seed=293, S=3, Hq=16, Hkv=1, D=64, B=32, max_ctx=150, kv_dtype="fp8",
+                    in_dtype="bf16"))
+    out.append(dict(seed=294, S=3, Hq=32, Hkv=2, D=64, B=8, max_ctx=150, kv_dtype="bf16",
+                    in_dtype="bf16"))
     return out
 
 
@@ -316,6 +321,30 @@ def test_batch_of_more_than_256_sequences(kv):
         out = out_host(g.decode(ps, IMPLS["mfma"]))
         err = np.abs(out - ref).max()
         assert err <= TOL[kv], (ps, err)
+
+
+@pytest.mark.parametrize("kv,impl", [("bf16", 2), ("fp8", 2), ("bf16", 1)])
+def test_contexts_cut_at_max_context_len(kv, impl):
+    """A max_context_len below some context lengths cuts those contexts at it: the result is
+    the attention over their first max_context_len tokens (the oracle on the cut lengths)."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
+    wl = workloads.random_small(334, S=6, Hq=8, Hkv=2, D=128, B=16, max_ctx=900, min_ctx=300,
+                                kv_dtype=kv, in_dtype="bf16")
+    print(f"cut contexts {kv} impl {impl}", flush=True)
+    st = oracle_run(wl)
+    g = GpuState(wl)
+    for cut in (500, 256, 17):
+        st_cut = dataclasses.replace(st, ctx=np.minimum(st.ctx, cut))
+        ref = oracle_decode(st_cut)
+        for ps in (0, 128):
+            out = torch.empty_like(g.q)
+            pkv.paged_attn_decode(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens,
+                                  wl.scale, out, g.desc, cut, ps, impl=impl)
+            torch.cuda.synchronize()
+            err = np.abs(out_host(out) - ref).max()
+            assert err <= TOL[kv], (cut, ps, err)
 
 
 @pytest.mark.parametrize("impl", [1, 2])
