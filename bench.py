@@ -45,11 +45,37 @@ EVENT_EVERY = 2        # timed steps between two whose decode kernel records its
 READ_REF_BYTES = 4 << 30
 
 
+def _code_only(src: str) -> str:
+    """C++ source without its comments and blank space, so that editing a comment does not
+    count as a change of the kernel.  String and character literals are kept."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code of the sources the decode kernel is built from (decode.hip,
+    device_common.h), comments and blank space left out."""
     h = hashlib.sha256()
     for f in ("decode.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_104_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_104_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -588,9 +588,9 @@ __device__ __forceinline__ int row_seq(const DecodeArgs& a, int4 d) {
   return (d.x >= 0 && d.x < a.num_seqs) ? d.x : 0;
 }
 
-// Unit of descriptor d {first sequence, shared tokens, members, 0} given the
-// first sequence's context length len0: members cut to the 16 query columns
-// and to the batch, shared tokens to whole blocks of the first member's
+// Unit of descriptor d {first sequence, shared tokens, members, reread} given
+// the first sequence's context length len0: members cut to the kUnitCols query
+// columns and to the batch, shared tokens to whole blocks of the first member's
 // context.  An out-of-range first sequence gives a unit without members.
 __device__ __forceinline__ void unit_of(const DecodeArgs& a, int4 d, int len0, int& seq0, int& M,
                                         int& T) {
@@ -1246,7 +1246,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(DecodeArgs a) {
   int64_t first0 = 0, head_step = 0, stride = 0, fix = 0;
   if constexpr (ROWS) {
     // shared-prefix decode: the segments of the sequence's unit, in its member's columns
-    // (16-row slots); a sequence outside every unit is left alone
+    // (kUnitCols-row slots); a sequence outside every unit is left alone
     const int4 sr = a.seq_rows[s];
     const int u = sr.x, mem = sr.y;
     if (u < 0 || u >= a.num_rows || mem < 0 || (mem + 1) * g > kUnitCols) return;
