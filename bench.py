@@ -414,6 +414,24 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
         best_t = t if best_t is None else min(best_t, t)
     res["same_bytes"] = {"bytes": int(m * tile_bytes), "us": round(best_t * 1e6, 2),
                          "GBps": round(m * tile_bytes / best_t / 1e9, 1)}
+    # the same bytes as one sequential stream (after a read of other tiles, so not cached):
+    # no tile ids to wait for, the upper bound for a read of this size
+    best_t = None
+    for wgs in (1024, 2048, 4096, 8192):
+        ts = []
+        for r in range(reps + 1):
+            pkv.read_probe(buf[n * tile_bytes // 2:], tile_bytes, None, min(m, n // 2), sink,
+                           2048)
+            ev[0].record()
+            pkv.read_probe(buf, tile_bytes, None, m, sink, wgs)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if r:
+                ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        t = float(np.median(ts))
+        best_t = t if best_t is None else min(best_t, t)
+    res["same_bytes_sequential"] = {"bytes": int(m * tile_bytes), "us": round(best_t * 1e6, 2),
+                                    "GBps": round(m * tile_bytes / best_t / 1e9, 1)}
     del buf, perm, sink
     return res
 
@@ -683,6 +701,8 @@ def main() -> int:
         # the flushed decode against a probe launch reading as many bytes from HBM
         result["roofline"]["same_bytes_frac"] = round(
             result["roofline"]["achieved_flushed"] / ref["same_bytes"]["GBps"], 4)
+        result["roofline"]["same_bytes_sequential_frac"] = round(
+            result["roofline"]["achieved_flushed"] / ref["same_bytes_sequential"]["GBps"], 4)
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
