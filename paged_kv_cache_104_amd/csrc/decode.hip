@@ -1863,30 +1863,25 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[kScratchMaxDevices] = {};
 
-// Device address of the current device's scratch (nullptr and a message on failure).
-static void* scratch_ptr() {
+// Device address of the current device's scratch in *out; PKV_OK, or the status and a
+// message on failure.
+static int scratch_ptr(void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    fail(PKV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    return nullptr;
-  }
-  if (dev < 0 || dev >= kScratchMaxDevices) {
-    fail(PKV_E_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
-         kScratchMaxDevices);
-    return nullptr;
-  }
+  if (e != hipSuccess) return fail(PKV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(PKV_E_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kScratchMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess || !p) {
-      fail(PKV_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
-      return nullptr;
-    }
+    if (e != hipSuccess || !p)
+      return fail(PKV_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
     g_scratch_ptr[dev] = p;
   }
-  return g_scratch_ptr[dev];
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
 }
 
 // Scratch layout of one call: header | records of the (sequence, head) pairs | partial
@@ -1941,8 +1936,9 @@ extern "C" int pkv_paged_attn_decode_noalloc(const void* q, int32_t q_dtype, con
                 "the batch needs %zu bytes of scratch, more than the %zu the no-allocation "
                 "decode holds (use pkv_paged_attn_decode with a workspace)",
                 lay.total, kScratchBytes);
-  void* ws = scratch_ptr();
-  if (!ws) return PKV_E_HIP;
+  void* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc) return rc;
   DecodeArgs a;
   WsLayout got;
   rc = prepare(q, q_dtype, k_pool, v_pool, c, block_tables, max_blocks_per_seq, context_lens,
