@@ -39,7 +39,7 @@ DEFAULT_CONFIG = "8b-gqa-bf16"
 DOMINANT_KERNEL = "decode_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DIAG_STEPS = 10        # untimed steps after the timed ones, with every kernel bracketed
-FLUSH_STEPS = 10       # untimed steps after those, each after a read that evicts the KV
+FLUSH_STEPS = 10       # untimed steps after those, each after a write that evicts the KV
 FLUSH_BYTES = 512 << 20
 EVENT_EVERY = 2        # timed steps between two whose decode kernel records its own events
 READ_REF_BYTES = 4 << 30
@@ -136,7 +136,8 @@ def build_gpu_state(wl, workers: int):
 
 
 def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers: int,
-            event_every: int = EVENT_EVERY, rows_mode: str = "auto"):
+            event_every: int = EVENT_EVERY, rows_mode: str = "auto",
+            cached_loads: bool = False):
     import torch
 
     import paged_kv_cache_104_amd as pkv
@@ -175,15 +176,17 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     # holds the kernel alone; separate event records around it would add the idle time
     # they leave on the device (about 6 us each).  The diagnostic steps after the timed
     # ones also time the cache write and the merge; the flushed steps after those first
-    # read a 512 MB scratch buffer (untimed), so that no KV line is left in the 256 MB
-    # last-level cache or the L2s when the decode starts.  Every event is recorded once
-    # here so none is created inside the timed loop.
+    # write a 512 MB scratch buffer (untimed), so that no KV line is left in the 256 MB
+    # last-level cache or the L2s when the decode starts, and the cache holds dirty lines
+    # of other data instead, as after the rest of a model's layer.  Every event is
+    # recorded once here so none is created inside the timed loop.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
     for e in [x for row in ev for x in row]:
         e.record(stream)
     torch.cuda.synchronize()
     # forked samples share blocks: read them once for all sharers (shared-prefix units), or
-    # per sequence with the shared blocks kept cached
+    # per sequence; with cached_loads the K/V loads are ordinary ones that leave lines in the
+    # caches for other readers (the shared-blocks hint) instead of streaming
     if use_rows:
         rows_d, seq_rows_d, reread = batch.shared_prefix_rows(wl.group, 1)
         n_rows = int(rows_d.shape[0])
@@ -191,19 +194,17 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         log(f"shared-prefix units: {n_rows} units for {S} sequences, "
             f"{int((rows_d[:, 2] > 1).sum())} with shared blocks, "
-            f"{int(rows_d[:, 3].sum())} read again by other units"
-            f"{' (cached loads)' if reread else ''}")
-    elif shared:
+            f"{int(rows_d[:, 3].sum())} read again by other units")
+        reread = reread and cached_loads
+    elif shared and cached_loads:
         impl |= pkv.IMPL_SHARED_BLOCKS
     kv_bytes = np.zeros(total)
     host_s = np.zeros(total)
     n_pairs = 0
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    flush_buf.fill_(1)
-    flush_sink = torch.empty(2048 * 64, dtype=torch.int32, device=dev)
 
-    def flush():
-        pkv.read_probe(flush_buf, 4096, None, FLUSH_BYTES // 4096, flush_sink, 2048)
+    def flush(i):
+        flush_buf.fill_(i % 251 + 1)
 
     def sampled(i):
         return i >= warmup + steps or (i - warmup) % event_every == 0
@@ -254,7 +255,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
     for i in range(warmup + steps, warmup + steps + DIAG_STEPS):
         step(i, all_events=True)
     for i in range(warmup + steps + DIAG_STEPS, total):
-        flush()
+        flush(i)
         step(i, all_events=True)
     torch.cuda.synchronize()
     gc.enable()
@@ -293,6 +294,7 @@ def run_gpu(wl, steps: int, warmup: int, partition_size: int, impl: int, workers
                 t_attn_flush=t_attn_flush, t_merge_flush=t_merge_flush, kv_flush=kv_flush,
                 max_ctx=max_ctx, ws_bytes=ws_bytes, n_pairs=n_pairs, shared=shared,
                 rows=use_rows, rows_cached=use_rows and reread,
+                cached_loads=bool(shared and cached_loads),
                 unique_ratio=unique_bytes / float(kvb[-1]))
 
 
@@ -371,8 +373,9 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
     random order (as the decode reads its blocks).  Best of a few launch widths, median of
     ``reps`` launches each (GB/s).  ``same_bytes``: random tiles adding up to the decode's
     own KV bytes per launch, each launch on tiles no earlier launch of that width read
-    (while the buffer holds enough), so that a short launch is set against a read of its
-    own size from HBM, ramp and tail included."""
+    (while the buffer holds enough) and after the same 512 MB write as the flushed decode
+    steps, so that a short launch is set against a read of its own size from HBM, ramp and
+    tail included."""
     import torch
 
     import paged_kv_cache_104_amd as pkv
@@ -382,6 +385,7 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
     n = total_bytes // tile_bytes
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(0)).to("cuda")
     sink = torch.empty(8192 * 64, dtype=torch.int32, device="cuda")
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     res = {}
     for name, ids in (("sequential", None), ("random_tiles", perm)):
@@ -404,6 +408,7 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
         for r in range(reps + 1):
             lo = (r * m) % max(1, n - m + 1)
             ids = perm[lo:lo + m]
+            flush_buf.fill_(r + 1)
             ev[0].record()
             pkv.read_probe(buf, tile_bytes, ids, m, sink, wgs)
             ev[1].record()
@@ -414,14 +419,13 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
         best_t = t if best_t is None else min(best_t, t)
     res["same_bytes"] = {"bytes": int(m * tile_bytes), "us": round(best_t * 1e6, 2),
                          "GBps": round(m * tile_bytes / best_t / 1e9, 1)}
-    # the same bytes as one sequential stream (after a read of other tiles, so not cached):
-    # no tile ids to wait for, the upper bound for a read of this size
+    # the same bytes as one sequential stream, after the same write: no tile ids to wait
+    # for, the upper bound for a read of this size
     best_t = None
     for wgs in (1024, 2048, 4096, 8192):
         ts = []
         for r in range(reps + 1):
-            pkv.read_probe(buf[n * tile_bytes // 2:], tile_bytes, None, min(m, n // 2), sink,
-                           2048)
+            flush_buf.fill_(r + 1)
             ev[0].record()
             pkv.read_probe(buf, tile_bytes, None, m, sink, wgs)
             ev[1].record()
@@ -432,7 +436,7 @@ def read_reference(tile_bytes: int, same_bytes: int, total_bytes: int = READ_REF
         best_t = t if best_t is None else min(best_t, t)
     res["same_bytes_sequential"] = {"bytes": int(m * tile_bytes), "us": round(best_t * 1e6, 2),
                                     "GBps": round(m * tile_bytes / best_t / 1e9, 1)}
-    del buf, perm, sink
+    del buf, perm, sink, flush_buf
     return res
 
 
@@ -579,6 +583,9 @@ def main() -> int:
     ap.add_argument("--rows", choices=("auto", "off"), default="auto",
                     help="shared-prefix (unit) decode for batches whose sequences share blocks "
                          "(auto), or the per-sequence decode (off)")
+    ap.add_argument("--cached-loads", action="store_true",
+                    help="batches that share blocks: read K/V with ordinary loads (the "
+                         "shared-blocks hint) instead of streaming them")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-reference", action="store_true",
@@ -616,7 +623,8 @@ def main() -> int:
     wl.cache_sequences = True          # keep the drawn inputs for the oracle's sample
     ps = wl.partition_size if args.partition_size is None else args.partition_size
     r = run_gpu(wl, args.steps, args.warmup, ps, args.impl, args.workers,
-                event_every=max(1, args.event_every), rows_mode=args.rows)
+                event_every=max(1, args.event_every), rows_mode=args.rows,
+                cached_loads=args.cached_loads)
     wall = r["wall"]
     total_bytes = float(r["kv_bytes"].sum())
     value = total_bytes / wall / 1e9
@@ -643,7 +651,7 @@ def main() -> int:
             "mean_context": round(mean_ctx, 1), "partition_size": ps,
             "kv_loads": ("shared-prefix units, cached loads" if r["rows_cached"] else
                          "shared-prefix units" if r["rows"] else
-                         "cached (shared blocks)" if r["shared"] else "streaming"),
+                         "cached (shared blocks)" if r["cached_loads"] else "streaming"),
             "prefix_cache": r["cache_stats"],
             "description": wl.description,
         },

@@ -223,7 +223,10 @@ typedef enum {
    * samples, beam search).  The MFMA kernel then reads K/V with ordinary
    * cached loads so the other readers hit in L2 / Infinity Cache; without the
    * hint it streams them (non-temporal loads), which is faster when every
-   * block is read once.  The result is the same either way. */
+   * block is read once.  The cached loads allocate lines in the last-level
+   * cache: when it holds dirty lines of earlier work (a large write just
+   * before the decode) they pay for writing those back and can be slower than
+   * streaming even with sharing.  The result is the same either way. */
   PKV_IMPL_SHARED_BLOCKS = 0x100
 } pkv_decode_impl;
 
@@ -373,10 +376,11 @@ size_t pkv_rows_workspace_bytes(const pkv_cache_desc* c, int32_t num_rows);
  * aligned, e.g. uploaded from pkv_prefix_rows) and phases: 1 the decode
  * kernel, 2 the merge, 3 both (1 then 2 on the same workspace and stream),
  * optionally or-ed with PKV_IMPL_SHARED_BLOCKS: read K and V with ordinary
- * loads instead of streaming them, which pays when some unit has reread = 1
+ * loads instead of streaming them, which can pay when some unit has reread = 1
  * (its shared blocks are read again by other units of the launch and then hit
- * in the Infinity Cache) and costs a few percent otherwise.  The result is the
- * same either way.
+ * in the Infinity Cache) if the cache holds no dirty lines of earlier work,
+ * and costs a few percent when no unit has it, much more after a large write
+ * (see PKV_IMPL_SHARED_BLOCKS).  The result is the same either way.
  * bf16 or fp8 pools only (PKV_E_UNSUPPORTED for f32).  Unit fields are
  * trusted only as far as memory safety: out-of-range sequences and members
  * are cut, shared tokens are cut to whole blocks of seq0's context, and a

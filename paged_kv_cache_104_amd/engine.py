@@ -186,7 +186,12 @@ class PagedKVCache:
 
     def decode(self, q, out, tables, lens, scale: float, max_context_len: int,
                partition_size: int = 0, workspace=None, impl: int = IMPL_AUTO,
-               hint_sharing: bool = True):
+               hint_sharing: bool = False):
+        """Decode over the cache's pools.  ``hint_sharing``: when some block is held by
+        several sequences, read K/V with ordinary cached loads (PKV_IMPL_SHARED_BLOCKS)
+        instead of streaming them.  Off by default: the cached loads gain only when the last
+        level cache holds no dirty lines of other work when the decode starts; after a large
+        write they pay for writing those lines back."""
         if hint_sharing and self.shares_blocks():
             impl |= IMPL_SHARED_BLOCKS
         return paged_attn_decode(q, self.k_pool, self.v_pool, tables, lens, scale, out, self.desc,
@@ -240,7 +245,8 @@ class DecodeBatch:
     def shared_prefix_rows(self, group: int, min_shared_blocks: int = 1):
         """Units of the shared-prefix decode for the batch as it stands, uploaded:
         ``(rows, seq_rows, reread)``, device int32 tensors and whether some unit's shared
-        blocks are read by other units too (then pass ``shared_blocks=True`` to the decode).
+        blocks are read by other units too (then ``shared_blocks=True`` for the decode can
+        pay, when the last-level cache holds no dirty lines of other work).
         Sequences that share leading blocks must be consecutive in the batch.  The units
         stay valid while no shared block is replaced (appends only grow the contexts after
         the shared part)."""
