@@ -665,6 +665,8 @@ def main() -> int:
             "decode_attention_p10_p50_p90": [round(float(np.percentile(r["t_attn"], p)) * 1e3, 4)
                                              for p in (10, 50, 90)],
             "decode_attention_flushed": round(float(r["t_attn_flush"].mean()) * 1e3, 4),
+            "decode_attention_flushed_p10_p50_p90": [
+                round(float(np.percentile(r["t_attn_flush"], p)) * 1e3, 4) for p in (10, 50, 90)],
             "merge_flushed": round(float(r["t_merge_flush"].mean()) * 1e3, 4),
         },
         "host_ms_per_step": round(float(r["host_s"].mean()) * 1e3, 4),
