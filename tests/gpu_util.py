@@ -69,13 +69,14 @@ class GpuState:
         self.q = to_device(wl.q_input(), wl.in_dtype, "cuda")
         torch.cuda.synchronize()
 
-    def decode(self, partition_size=None, impl=0, out=None):
+    def decode(self, partition_size=None, impl=0, out=None, scale=None):
         torch = torch_mod()
         wl = self.wl
         ps = wl.partition_size if partition_size is None else partition_size
         out = torch.empty_like(self.q) if out is None else out
-        self.cache.decode(self.q, out, self.tables, self.lens, wl.scale, wl.max_context_len,
-                          ps, impl=impl)
+        self.cache.decode(self.q, out, self.tables, self.lens,
+                          wl.scale if scale is None else scale, wl.max_context_len, ps,
+                          impl=impl)
         torch.cuda.synchronize()
         return out
 
@@ -97,6 +98,49 @@ def out_host(t) -> np.ndarray:
 
 
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 3e-2}
+
+# Softmax scale factor of the peaked-attention checks: q.k / sqrt(D) of unit normal draws is
+# about N(0, 1), times 16 the largest score of a context beats the next by a wide margin, so
+# each output is close to the V row of one token anywhere in the context (and the kernel's
+# running maximum is raised again and again along the context).
+PEAK = 16.0
+
+# Unit roundoff of bf16 (8 significant bits).
+U_BF16 = 2.0 ** -8
+
+
+def peaked_tol(kv_dtype: str, ref: np.ndarray) -> np.ndarray:
+    """The dtype's tolerance plus the rounding of the output itself (bf16 for bf16 and fp8
+    pools, f32 for f32 pools): a peaked softmax gives outputs as large as single value
+    entries, and at |out| >= 4 a correctly rounded bf16 output is already up to 0.0156 away
+    from the exact one, beyond the absolute 1.5e-2."""
+    u = 2.0 ** -24 if kv_dtype == "f32" else U_BF16
+    return TOL[kv_dtype] + u * np.abs(ref)
+
+
+def abs_values(v_pool: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """The value pool in the oracle's storage format with every sign cleared."""
+    if kv_dtype == "bf16":
+        return v_pool & np.uint16(0x7FFF)
+    if kv_dtype == "fp8":
+        return v_pool & np.uint8(0x7F)
+    return np.abs(v_pool)
+
+
+def rounding_bound(st, ref: np.ndarray, scale=None, seqs=None) -> np.ndarray:
+    """Per-element bound on |out - ref| for the bf16 and fp8 pools' decode, from its
+    arithmetic: the kernel rounds each softmax weight p_i to bf16 (relative error <= u) and
+    normalises by the sum of the same rounded weights, so to first order
+    |out - ref| <= u * (sum_i w_i |v_i| + |ref|), and the bf16 output adds u * |ref|.  The
+    weighted mean of |v| is the oracle's own decode over the value pool with signs cleared.
+    Twice that, plus 1e-4 for the fp32 scores, sums and exponentials."""
+    from oracle import attention as oattn
+
+    wl = st.wl
+    absv = oattn.paged_decode(st.q64(), st.k_pool, abs_values(st.v_pool, wl.kv_dtype),
+                              st.tables, st.ctx, wl.scale if scale is None else scale,
+                              wl.kv_dtype, st.k_scale, st.v_scale, seqs=seqs)
+    return 2.0 * U_BF16 * (absv + 2.0 * np.abs(ref)) + 1e-4
 
 
 def pools_equal_bits(a: np.ndarray, b: np.ndarray) -> bool:

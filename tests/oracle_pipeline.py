@@ -115,7 +115,8 @@ def new_token_inputs(wl, positions, get=None):
     return np.stack(ks), np.stack(vs)
 
 
-def decode(st: OracleState, seqs=None) -> np.ndarray:
+def decode(st: OracleState, seqs=None, scale=None) -> np.ndarray:
     wl = st.wl
-    return oattn.paged_decode(st.q64(), st.k_pool, st.v_pool, st.tables, st.ctx, wl.scale,
-                              wl.kv_dtype, st.k_scale, st.v_scale, seqs=seqs)
+    return oattn.paged_decode(st.q64(), st.k_pool, st.v_pool, st.tables, st.ctx,
+                              wl.scale if scale is None else scale, wl.kv_dtype, st.k_scale,
+                              st.v_scale, seqs=seqs)

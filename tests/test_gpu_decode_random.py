@@ -1,11 +1,13 @@
 """Seeded random sweep of the decode against the fp64 oracle: batch size, head group, head
 size, block size, pool dtype, context lengths and partition size drawn per case, both kernel
-families.  Each case is small enough for the oracle to finish in well under a second."""
+families, at the workload's softmax scale and at a 16 times larger one.  Errors are held to
+the dtype's tolerance and to the per-element bound of the kernel's rounding.  Each case is
+small enough for the oracle to finish in well under a second."""
 import numpy as np
 import pytest
 
 import workloads
-from gpu_util import TOL, GpuState, out_host
+from gpu_util import PEAK, TOL, GpuState, out_host, peaked_tol, rounding_bound
 from oracle_pipeline import decode as oracle_decode
 from oracle_pipeline import run as oracle_run
 
@@ -34,10 +36,15 @@ def test_random_shape(case):
     ps = case.pop("ps")
     wl = workloads.random_small(**case)
     print(f"random case {case} ps {ps}", flush=True)
-    ref = oracle_decode(oracle_run(wl))
+    st = oracle_run(wl)
     g = GpuState(wl)
-    for impl in (2, 1):
-        for p in (ps, 0):
-            out = out_host(g.decode(p, impl))
-            err = np.abs(out - ref).max()
-            assert err <= TOL[wl.kv_dtype], (impl, p, err)
+    # the workload's scale, then a peaked softmax whose outputs are single tokens' values
+    for scale in (wl.scale, PEAK * wl.scale):
+        ref = oracle_decode(st, scale=scale)
+        bound = rounding_bound(st, ref, scale)
+        tol = TOL[wl.kv_dtype] if scale == wl.scale else peaked_tol(wl.kv_dtype, ref)
+        for impl in (2, 1):
+            for p in (ps, 0):
+                err = np.abs(out_host(g.decode(p, impl, scale=scale)) - ref)
+                assert (err <= tol).all(), (scale, impl, p, err.max())
+                assert (err <= bound).all(), (scale, impl, p, (err / bound).max())
