@@ -110,12 +110,12 @@ U_BF16 = 2.0 ** -8
 
 
 def peaked_tol(kv_dtype: str, ref: np.ndarray) -> np.ndarray:
-    """The dtype's tolerance plus the rounding of the output itself (bf16 for bf16 and fp8
-    pools, f32 for f32 pools): a peaked softmax gives outputs as large as single value
-    entries, and at |out| >= 4 a correctly rounded bf16 output is already up to 0.0156 away
-    from the exact one, beyond the absolute 1.5e-2."""
-    u = 2.0 ** -24 if kv_dtype == "f32" else U_BF16
-    return TOL[kv_dtype] + u * np.abs(ref)
+    """The dtype's tolerance plus the rounding of the bf16 output itself (bf16 and fp8
+    pools): a peaked softmax gives outputs as large as single value entries, and at
+    |out| >= 4 a correctly rounded bf16 output is already up to 0.0156 away from the exact
+    one, beyond the absolute 1.5e-2."""
+    assert kv_dtype in ("bf16", "fp8"), kv_dtype
+    return TOL[kv_dtype] + U_BF16 * np.abs(ref)
 
 
 def abs_values(v_pool: np.ndarray, kv_dtype: str) -> np.ndarray:

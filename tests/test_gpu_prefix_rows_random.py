@@ -1,10 +1,12 @@
 """Seeded random sweep of the shared-prefix decode against the fp64 oracle: prompts, samples
 per prompt (families wider than one unit included), prefix length, tails, head group, head
-size, block size and pool dtype drawn per case, with and without the cached-load hint."""
+size, block size and pool dtype drawn per case, with and without the cached-load hint, at the
+workload's softmax scale and at a 16 times larger one; errors held to the tolerance and to
+the per-element rounding bound of the kernel's arithmetic."""
 import numpy as np
 import pytest
 
-from gpu_util import TOL, GpuState, out_host, torch_mod
+from gpu_util import PEAK, TOL, GpuState, out_host, peaked_tol, rounding_bound, torch_mod
 from oracle_pipeline import decode as oracle_decode
 from oracle_pipeline import run as oracle_run
 from test_gpu_cache_ops import _shared_prefix_small
@@ -34,15 +36,20 @@ def test_random_families(case):
     wl = _shared_prefix_small(**kw)
     print(f"random families {kw} cached {cached} ps {ps}", flush=True)
     g = GpuState(wl)
-    ref = oracle_decode(oracle_run(wl))
+    st = oracle_run(wl)
     group = wl.num_q_heads // wl.num_kv_heads
     rows, seq_rows = pkv.prefix_rows(g.tables.cpu().numpy(), g.lens.cpu().numpy(),
                                      wl.block_size, group, 1)
-    out = torch.empty_like(g.q)
-    pkv.paged_attn_decode_rows(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens, wl.scale,
-                               out, g.desc, wl.max_context_len, ps,
-                               torch.from_numpy(rows).cuda(), torch.from_numpy(seq_rows).cuda(),
-                               shared_blocks=cached)
-    torch.cuda.synchronize()
-    err = np.abs(out_host(out) - ref).max()
-    assert err <= TOL[wl.kv_dtype], err
+    rows_d, seq_rows_d = torch.from_numpy(rows).cuda(), torch.from_numpy(seq_rows).cuda()
+    for scale in (wl.scale, PEAK * wl.scale):
+        ref = oracle_decode(st, scale=scale)
+        tol = TOL[wl.kv_dtype] if scale == wl.scale else peaked_tol(wl.kv_dtype, ref)
+        out = torch.empty_like(g.q)
+        pkv.paged_attn_decode_rows(g.q, g.cache.k_pool, g.cache.v_pool, g.tables, g.lens, scale,
+                                   out, g.desc, wl.max_context_len, ps, rows_d, seq_rows_d,
+                                   shared_blocks=cached)
+        torch.cuda.synchronize()
+        err = np.abs(out_host(out) - ref)
+        assert (err <= tol).all(), (scale, err.max())
+        bound = rounding_bound(st, ref, scale)
+        assert (err <= bound).all(), (scale, (err / bound).max())

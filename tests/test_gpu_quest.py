@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import TOL, GpuState, out_host, torch_mod
+from gpu_util import PEAK, TOL, GpuState, out_host, peaked_tol, torch_mod
 from oracle import allocator as oalloc
 from oracle import attention as oattn
 from oracle import cache as ocache
@@ -244,16 +244,20 @@ def test_quest_decode_matches_oracle(kv, impl):
     sel_t, sel_l = _pkv().quest_select(st.q, st.cache.quest_meta, st.desc, st.gt, st.gl,
                                     int(max(lens)), budget)
     ch = gpu_chosen(sel_t, sel_l, st.tables, st.ctx, H, B, budget)
-    scale = D ** -0.5
-    ref = quest.quest_decode(st.q64, st.kp, st.vp, st.tables, st.ctx, scale, H, budget, kv,
-                             st.k_scale, st.v_scale, chosen=ch)
-    for ps in (0, 64, 256):
-        out = torch.empty_like(st.q)
-        st.cache.quest_decode(st.q, out, st.gt, st.gl, scale, int(max(lens)), budget, ps,
-                              impl=impl)
-        torch.cuda.synchronize()
-        err = np.abs(out_host(out) - ref).max()
-        assert err <= TOL[kv], (ps, err)
+    # the selection does not depend on a positive scale; the peaked one makes each output
+    # close to one chosen token's value row (bf16 and fp8 pools: with f32 weights the fp32
+    # rounding of scores near 60 alone moves outputs by more than the f32 tolerance)
+    for scale in (D ** -0.5,) + (() if kv == "f32" else (PEAK * D ** -0.5,)):
+        ref = quest.quest_decode(st.q64, st.kp, st.vp, st.tables, st.ctx, scale, H, budget, kv,
+                                 st.k_scale, st.v_scale, chosen=ch)
+        tol = TOL[kv] if scale == D ** -0.5 else peaked_tol(kv, ref)
+        for ps in (0, 64, 256):
+            out = torch.empty_like(st.q)
+            st.cache.quest_decode(st.q, out, st.gt, st.gl, scale, int(max(lens)), budget, ps,
+                                  impl=impl)
+            torch.cuda.synchronize()
+            err = np.abs(out_host(out) - ref)
+            assert (err <= tol).all(), (scale, ps, err.max())
 
 
 @pytest.mark.parametrize("impl", [2, 1])
