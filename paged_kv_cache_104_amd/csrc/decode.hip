@@ -505,8 +505,10 @@ __device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* 
   const int last = (t1 + BS - 1) / BS - 1;
 #pragma unroll
   for (int b = 0; b < 32 / BS; ++b) {
+    // a block past the context's last one holds only masked tokens: read block 0 instead,
+    // which every worker's dead loads share, so it comes from L2 and not from memory
     const int pb = table[min(tt / BS + b, last)];
-    pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
+    pbs[b] = (tt / BS + b <= last && pb >= 0 && pb < num_blocks) ? pb : 0;
   }
 }
 
@@ -1147,6 +1149,9 @@ __global__ __launch_bounds__(64, (MfmaTuning<KV, ROWS ? 2 : 1>::waves)) void dec
       step_blocks<BS>(la_pbs, tables + int64_t(la.seq) * a.max_blocks,                         \
                       ROWS ? la.tb + 32 * (la.x - la.x0) : 32 * la.x,                          \
                       ROWS ? la.tb + la.ctx : la.ctx, a.num_blocks);                           \
+    } else {                                                                                   \
+      /* the range is loaded: the round's remaining issues read block 0 */                     \
+      for (int b = 0; b < NB; ++b) la_pbs[b] = 0;                                              \
     }                                                                                          \
   } while (0)
 
@@ -1156,8 +1161,10 @@ __global__ __launch_bounds__(64, (MfmaTuning<KV, ROWS ? 2 : 1>::waves)) void dec
   // from inside the unrolled round would give the loop header a second
   // incoming path on which the round's fresh loads are pending, and the
   // compiler would then wait for them before reusing any of their registers.
-  // Steps of the last round past the range are skipped (their loads still
-  // issue, repeating the last step).
+  // Steps of the last round past the range are skipped, but their loads still
+  // issue (one or two steps per worker).  They read block 0, the same for every
+  // worker: streamed again from the worker's last step they cost 16-32 KB of
+  // memory reads each, 30 MB per launch (10% of a multi-query layer's bytes).
   do {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
