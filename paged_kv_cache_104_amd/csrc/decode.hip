@@ -505,10 +505,10 @@ __device__ __forceinline__ void step_blocks(int (&pbs)[32 / BS], const int32_t* 
   const int last = (t1 + BS - 1) / BS - 1;
 #pragma unroll
   for (int b = 0; b < 32 / BS; ++b) {
-    // a block past the context's last one holds only masked tokens: read block 0 instead,
-    // which every worker's dead loads share, so it comes from L2 and not from memory
+    // a block past the context's last one holds only masked tokens: it repeats the last
+    // block, whose lines the same step loads anyway
     const int pb = table[min(tt / BS + b, last)];
-    pbs[b] = (tt / BS + b <= last && pb >= 0 && pb < num_blocks) ? pb : 0;
+    pbs[b] = (pb >= 0 && pb < num_blocks) ? pb : 0;
   }
 }
 
