@@ -1472,8 +1472,29 @@ static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
   DecodeArgs a = a0;
   // a preset count (the no-allocation entry point sized its scratch for it) is a cap
   const int64_t resident = std::min<int64_t>(kMaxWorkers, resident_workers(kernel));
-  a.workers = int32_t(a0.workers > 0 ? std::min<int64_t>(a0.workers, resident) : resident);
-  return launch_decode(kernel, dim3(static_cast<unsigned>(a.workers)), dim3(64), s, a,
+  int64_t w = a0.workers > 0 ? std::min<int64_t>(a0.workers, resident) : resident;
+  // Few long pairs (eight or more workers' shares each, as in a multi-query layer): two bf16
+  // workers per CU instead of four.  Each worker's share doubles, so the fixed cost of
+  // finding its start and of the pieces it writes and the merge reads weighs half as much,
+  // and two steps of loads in flight per worker still keep the memory busy (multi-query
+  // layer 55.3 -> 52.1 us; with many pairs four workers per CU stay ahead).
+  if (!ROWS && KV == KV_BF16 && int64_t(a.num_seqs) * a.num_kv_heads * 8 <= w && w >= 2)
+    w /= 2;
+  a.workers = int32_t(w);
+  // Only the workers that can get steps are launched.  With a partition size each share is
+  // at least part_tokens / 32 steps (unless that would leave fewer than half the workers
+  // busy), so at most max(ceil(steps / share), ceil(w / 2)) workers have any, where steps is
+  // the most the contexts can hold.  The split itself is computed for all w workers, so the
+  // result is the same; the workers left out would only have started, scanned the context
+  // lengths and left (one 32k-token context in partitions of 512: 513 of 1024 launched).
+  int64_t grid = w;
+  if (!ROWS && a.part_tokens > 0) {
+    const int64_t share = std::max(1, a.part_tokens >> 5);
+    const int64_t steps =
+        int64_t(a.num_seqs) * a.num_kv_heads * ((int64_t(a.max_ctx) + 31) / 32);
+    grid = std::min<int64_t>(w, std::max<int64_t>((steps + share - 1) / share, (w + 1) / 2));
+  }
+  return launch_decode(kernel, dim3(static_cast<unsigned>(grid)), dim3(64), s, a,
                        a.context_lens, a.block_tables, a.rows);
 }
 
