@@ -1473,14 +1473,18 @@ static int launch_mfma(const DecodeArgs& a0, hipStream_t s) {
   // a preset count (the no-allocation entry point sized its scratch for it) is a cap
   const int64_t resident = std::min<int64_t>(kMaxWorkers, resident_workers(kernel));
   int64_t w = a0.workers > 0 ? std::min<int64_t>(a0.workers, resident) : resident;
-  // Few long pairs (four or more workers' shares each, as in a multi-query layer): two bf16
-  // workers per CU instead of four.  Each worker's share doubles, so the fixed cost of
-  // finding its start and of the pieces it writes and the merge reads weighs half as much,
-  // and two steps of loads in flight per worker still keep the memory busy (multi-query
-  // layers of 32 to 256 sequences 12% to 1.4% faster, GQA layers of 64 to 256 pairs up to 2%;
-  // with thousands of pairs four workers per CU stay ahead by about 2%).
-  if (!ROWS && KV == KV_BF16 && int64_t(a.num_seqs) * a.num_kv_heads * 4 <= w && w >= 2)
-    w /= 2;
+  // Few long pairs: half the workers.  Each worker's share doubles, so the fixed cost of
+  // finding its start and of the pieces it writes and the merge reads weighs half as much.
+  // bf16, four or more workers' shares per pair: two workers per CU instead of four, whose
+  // two steps of loads in flight still keep the memory busy (multi-query layers of 32 to 256
+  // sequences 12% to 1.4% faster, GQA layers of 64 to 256 pairs up to 3%; with thousands of
+  // pairs four workers per CU stay ahead by about 2%).  fp8 (two waves per SIMD), eight or
+  // more shares per pair of a group of 16: one wave per SIMD (multi-query layers of 32 to 256
+  // sequences 13% to 2% faster).  With smaller groups the pieces weigh less and fp8 loses
+  // more from halving the loads in flight (group 4: up to 5% slower from 128 pairs on).
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
+  const bool few_pairs = KV == KV_BF16 ? pairs * 4 <= w : (a.group >= 16 && pairs * 8 <= w);
+  if (!ROWS && few_pairs && w >= 2) w /= 2;
   a.workers = int32_t(w);
   // Only the workers that can get steps are launched.  With a partition size each share is
   // at least part_tokens / 32 steps (unless that would leave fewer than half the workers
