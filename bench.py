@@ -495,6 +495,76 @@ def swap_sweep(total_bytes: int, reps: int, methods=("kernel", "dma")) -> None:
     print(json.dumps({"swap_sweep": rows, "bytes_per_direction": total_bytes, "reps": reps}))
 
 
+def cache_ops_bench(tokens: int, reps: int) -> None:
+    """The cache write and the copy-on-write block copy at scale, against the HBM roofline:
+    ``tokens`` new tokens (a prefill's worth, 8 KV heads, D = 128, 16-token blocks) written
+    through ``pkv_reshape_and_cache`` into whole blocks placed at random in the pool (bf16,
+    and fp8 encoded from bf16), and ``pkv_copy_blocks`` over as many blocks' worth of random
+    (src, dst) pairs.  Bytes are the algorithmic ones, read plus written; a plain device copy
+    of the same bytes (torch ``copy_``) is timed beside them.  Median of ``reps`` launches."""
+    import torch
+
+    import paged_kv_cache_104_amd as pkv
+
+    H, D, B = 8, 128, 16
+    n_blk = tokens // B
+    rng = np.random.default_rng(11)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        return float(np.median(ts))
+
+    rows = []
+    for kv in ("bf16", "fp8"):
+        scale = 0.05 if kv == "fp8" else 1.0
+        desc = pkv.cache_desc(2 * n_blk + 1, H, B, D, kv, scale, scale)
+        kp, vp = pkv.alloc_pools(desc, poison=False)
+        elem = 2 if kv == "bf16" else 1
+        # reshape_and_cache: whole blocks at random places
+        blocks = rng.permutation(2 * n_blk + 1)[:n_blk]
+        t = np.arange(tokens)
+        slots = torch.from_numpy(blocks[t // B] * B + t % B).cuda()
+        k = torch.randn(tokens, H, D, device="cuda").to(torch.bfloat16)
+        v = torch.randn(tokens, H, D, device="cuda").to(torch.bfloat16)
+        sec = timed(lambda: pkv.reshape_and_cache(k, v, slots, kp, vp, desc))
+        nbytes = tokens * H * D * (2 + elem) * 2
+        rows.append({"op": "reshape_and_cache", "kv_dtype": kv, "tokens": tokens,
+                     "bytes": nbytes, "us": round(sec * 1e6, 1),
+                     "GBps": round(nbytes / sec / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
+        # copy_blocks: n_blk pairs, sources and destinations disjoint, random
+        perm = rng.permutation(2 * n_blk)
+        pairs = torch.from_numpy(np.stack([perm[:n_blk], perm[n_blk:]], 1).astype(np.int64)).cuda()
+        sec = timed(lambda: pkv.copy_blocks(kp, vp, pairs, desc))
+        nbytes = n_blk * H * B * D * elem * 2 * 2
+        rows.append({"op": "copy_blocks", "kv_dtype": kv, "pairs": n_blk,
+                     "block_bytes": H * B * D * elem, "bytes": nbytes, "us": round(sec * 1e6, 1),
+                     "GBps": round(nbytes / sec / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
+        del kp, vp, k, v
+    # a plain device copy of the bf16 write's bytes (half read, half written)
+    src = torch.empty(tokens * H * D * 2 * 2, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    sec = timed(lambda: dst.copy_(src))
+    nbytes = 2 * src.numel()
+    rows.append({"op": "torch_copy", "bytes": nbytes, "us": round(sec * 1e6, 1),
+                 "GBps": round(nbytes / sec / 1e9, 1),
+                 "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
+    for r in rows:
+        log(json.dumps(r))
+    print(json.dumps({"cache_ops": rows, "reps": reps}), flush=True)
+
+
 def quest_bench(wl, budget: int, steps: int, warmup: int, partition_size: int, impl: int,
                 workers: int) -> None:
     """QUEST decode against the dense decode on the same decode steps.
@@ -594,6 +664,9 @@ def main() -> int:
     ap.add_argument("--swap-sweep", type=int, default=0, metavar="BYTES",
                     help="measure swapping rates moving BYTES of K+V each way, then exit")
     ap.add_argument("--swap-methods", default="kernel,dma")
+    ap.add_argument("--cache-ops", type=int, default=0, metavar="TOKENS",
+                    help="time the cache write and the block copy at scale (TOKENS new tokens "
+                         "and as many blocks' worth of copies), then exit")
     ap.add_argument("--quest-budget", type=int, default=0, metavar="BLOCKS",
                     help="time the QUEST decode with this budget against the dense decode "
                          "on --config, then exit")
@@ -608,6 +681,9 @@ def main() -> int:
         return 0
     if args.swap_sweep:
         swap_sweep(args.swap_sweep, 5, tuple(args.swap_methods.split(",")))
+        return 0
+    if args.cache_ops:
+        cache_ops_bench(args.cache_ops, 10)
         return 0
 
     import torch

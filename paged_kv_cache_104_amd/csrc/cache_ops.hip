@@ -19,6 +19,58 @@
 
 namespace pkv {
 
+// 8 consecutive dimensions of one (token, head) key row, from the input segment ks to
+// the pool segment kd (fp8: divided by k_scale and encoded, as every cache write does).
+template <int KV, typename In>
+__device__ __forceinline__ void write_key_segment(const In* __restrict__ ks,
+                                                  typename KvTraits<KV>::T* __restrict__ kd,
+                                                  float k_scale) {
+  if constexpr (KV == KV_BF16) {
+    *reinterpret_cast<uint4*>(kd) = *reinterpret_cast<const uint4*>(ks);
+  } else {
+    float kf[8];
+    if constexpr (sizeof(In) == 2) {
+      const uint4 ku = *reinterpret_cast<const uint4*>(ks);
+      const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kf[2 * i] = bf16_to_f32(kw[i] & 0xffffu);
+        kf[2 * i + 1] = bf16_to_f32(kw[i] >> 16);
+      }
+    } else {
+      const float4 k0 = reinterpret_cast<const float4*>(ks)[0];
+      const float4 k1 = reinterpret_cast<const float4*>(ks)[1];
+      kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
+      kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
+    }
+    if constexpr (KV == KV_FP8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_encode(__fdiv_rn(kf[i], k_scale)) << (8 * i);
+        hi |= e4m3_encode(__fdiv_rn(kf[i + 4], k_scale)) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
+    } else {
+      reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
+      reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
+    }
+  }
+}
+
+// One value element in the pool's storage format (fp8: divided by v_scale and encoded).
+template <int KV, typename In>
+__device__ __forceinline__ typename KvTraits<KV>::T encode_value(In x, float v_scale) {
+  if constexpr (KV == KV_BF16) {
+    return x;
+  } else {
+    float f;
+    if constexpr (sizeof(In) == 2) f = bf16_to_f32(x); else f = x;
+    if constexpr (KV == KV_FP8) return uint8_t(e4m3_encode(__fdiv_rn(f, v_scale)));
+    else return f;
+  }
+}
+
 // One token of k / v ([tokens][heads][D]) into slot `slot` of the pools, by one
 // workgroup.  Keys: each thread moves 8 consecutive dimensions of one head, a
 // contiguous row segment of the key tile.  Values: the token is one column of
@@ -45,54 +97,16 @@ __device__ __forceinline__ void write_token(
   for (int ch = threadIdx.x; ch < n / 8; ch += blockDim.x) {
     const int h = (ch * 8) / head_dim;
     const int d0 = ch * 8 - h * head_dim;
-    const In* ks = k + tok * n + ch * 8;
-    T* kd = k_pool + tile0 + h * head_stride + int64_t(pos) * head_dim + d0;
-    if constexpr (KV == KV_BF16) {
-      *reinterpret_cast<uint4*>(kd) = *reinterpret_cast<const uint4*>(ks);
-    } else {
-      float kf[8];
-      if constexpr (sizeof(In) == 2) {
-        const uint4 ku = *reinterpret_cast<const uint4*>(ks);
-        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kf[2 * i] = bf16_to_f32(kw[i] & 0xffffu);
-          kf[2 * i + 1] = bf16_to_f32(kw[i] >> 16);
-        }
-      } else {
-        const float4 k0 = reinterpret_cast<const float4*>(ks)[0];
-        const float4 k1 = reinterpret_cast<const float4*>(ks)[1];
-        kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w;
-        kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
-      }
-      if constexpr (KV == KV_FP8) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo |= e4m3_encode(__fdiv_rn(kf[i], k_scale)) << (8 * i);
-          hi |= e4m3_encode(__fdiv_rn(kf[i + 4], k_scale)) << (8 * i);
-        }
-        *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
-      } else {
-        reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
-        reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
-      }
-    }
+    write_key_segment<KV, In>(k + tok * n + ch * 8,
+                              k_pool + tile0 + h * head_stride + int64_t(pos) * head_dim + d0,
+                              k_scale);
   }
   // values: one element per thread, consecutive threads on consecutive dimensions, so
   // the lanes that write one line of the dimension-major tile do it in one instruction
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int h = e / head_dim, d = e - h * head_dim;
     T* vd = v_pool + tile0 + h * head_stride + int64_t(d) * block_size + pos;
-    const In x = v[tok * n + e];
-    if constexpr (KV == KV_BF16) {
-      __builtin_nontemporal_store(x, vd);
-    } else {
-      float f;
-      if constexpr (sizeof(In) == 2) f = bf16_to_f32(x); else f = x;
-      if constexpr (KV == KV_FP8) __builtin_nontemporal_store(uint8_t(e4m3_encode(__fdiv_rn(f, v_scale))), vd);
-      else __builtin_nontemporal_store(f, vd);
-    }
+    __builtin_nontemporal_store(encode_value<KV, In>(v[tok * n + e], v_scale), vd);
   }
 }
 
@@ -107,6 +121,115 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(
   if (slot < 0 || slot >= num_slots) return;             // skip (negative) / never write outside
   write_token<KV, In>(k, v, tok, slot, k_pool, v_pool, num_kv_heads, head_dim, block_size,
                       k_scale, v_scale);
+}
+
+// Writes of many tokens at once (a prompt's prefill): the value tile of a (block, head)
+// is dimension-major, so one token writes one element in each of its D rows, a few bytes
+// of every line; one store per element held such writes near 0.5 TB/s.  Here one
+// workgroup takes B consecutive tokens.  Keys go out as contiguous row segments as above.
+// For the values, each thread owns one (head, dimension) row at a time and gathers that
+// element of every token of the chunk into registers.  When the chunk's tokens fill one
+// block in order (the usual prefill: every block of a prompt but its last), the row is
+// written whole, B elements with 16-byte stores (8 bytes for an fp8 pool of 8-token
+// blocks); otherwise each token's element is stored alone: through the caches when a
+// neighbouring token of the chunk shares its block, so that the parts of a line meet in
+// L2, and streamed when it is alone in its block (a decode step's token, whose partial
+// lines would otherwise sit dirty in L2 when the decode reads that block).
+constexpr int kRunsThreads = 256;
+constexpr int64_t kRunsMinTokens = 512;    // fewer: the per-token kernel (decode steps)
+
+template <typename T>
+__device__ __forceinline__ uint32_t storage_bits(T x) {
+  if constexpr (sizeof(T) == 4) return __builtin_bit_cast(uint32_t, x);
+  else return uint32_t(x);
+}
+
+// B elements of one row of the dimension-major value tile, as whole 16-byte (or 8-byte)
+// stores; dst is the row's start (aligned: a row is B elements, 8 B at least).
+template <int KV, int B>
+__device__ __forceinline__ void store_value_row(typename KvTraits<KV>::T* __restrict__ dst,
+                                                const typename KvTraits<KV>::T (&x)[B]) {
+  constexpr int bytes = KvTraits<KV>::bytes, per_word = 4 / bytes, words = B * bytes / 4;
+  uint32_t w[words];
+#pragma unroll
+  for (int i = 0; i < words; ++i) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int b = 0; b < per_word; ++b) u |= storage_bits(x[i * per_word + b]) << (8 * bytes * b);
+    w[i] = u;
+  }
+  if constexpr (words % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < words / 4; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else {
+    static_assert(words == 2, "rows of 8 bytes or a multiple of 16");
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+}
+
+template <int KV, typename In, int B>
+__global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
+    const In* __restrict__ k, const In* __restrict__ v, const int64_t* __restrict__ slots,
+    typename KvTraits<KV>::T* __restrict__ k_pool, typename KvTraits<KV>::T* __restrict__ v_pool,
+    int num_kv_heads, int head_dim, int64_t num_tokens, int64_t num_slots, float k_scale,
+    float v_scale) {
+  typedef typename KvTraits<KV>::T T;
+  __shared__ int64_t s_blk[B];   // block of the chunk's token j, or -1: skipped
+  __shared__ int s_off[B];
+  const int64_t i0 = int64_t(blockIdx.x) * B;
+  const int n_tok = int(min<int64_t>(B, num_tokens - i0));
+  const int H = num_kv_heads, D = head_dim, n = H * D;
+  if (int(threadIdx.x) < B) {
+    int64_t blk = -1;
+    int off = 0;
+    if (int(threadIdx.x) < n_tok) {
+      const int64_t sl = slots[i0 + threadIdx.x];
+      if (sl >= 0 && sl < num_slots) {
+        blk = sl / B;
+        off = int(sl - blk * B);
+      }
+    }
+    s_blk[threadIdx.x] = blk;
+    s_off[threadIdx.x] = off;
+  }
+  __syncthreads();
+  // one whole block, its tokens in order: every value row is written whole
+  bool whole = n_tok == B && s_blk[0] >= 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) whole = whole && s_blk[j] == s_blk[0] && s_off[j] == j;
+  // keys
+  for (int e = threadIdx.x; e < n_tok * (n / 8); e += kRunsThreads) {
+    const int j = e / (n / 8), ch = e - j * (n / 8);
+    const int64_t blk = s_blk[j];
+    if (blk < 0) continue;
+    const int h = (ch * 8) / D, d0 = ch * 8 - h * D;
+    write_key_segment<KV, In>(k + (i0 + j) * n + ch * 8,
+                              k_pool + (blk * H + h) * int64_t(B) * D + int64_t(s_off[j]) * D + d0,
+                              k_scale);
+  }
+  // values: row e = h * D + d of every token of the chunk
+  for (int e = threadIdx.x; e < n; e += kRunsThreads) {
+    const int h = e / D, d = e - h * D;
+    T x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      x[j] = j < n_tok ? encode_value<KV, In>(v[(i0 + j) * n + e], v_scale) : T(0);
+    if (whole) {
+      store_value_row<KV, B>(v_pool + ((s_blk[0] * H + h) * int64_t(D) + d) * B, x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int64_t blk = j < n_tok ? s_blk[j] : -1;
+        if (blk < 0) continue;
+        T* dst = v_pool + ((blk * H + h) * int64_t(D) + d) * B + s_off[j];
+        const bool alone = (j == 0 || s_blk[j > 0 ? j - 1 : 0] != blk) &&
+                           (j + 1 >= n_tok || s_blk[j + 1 < B ? j + 1 : B - 1] != blk);
+        if (alone) __builtin_nontemporal_store(x[j], dst);
+        else *dst = x[j];
+      }
+    }
+  }
 }
 
 // The decode step's append for up to kAppendMax tokens, with the host's slots and
@@ -175,6 +298,33 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+template <int KV, typename In>
+static int launch_runs(const In* k, const In* v, const int64_t* slots,
+                       typename KvTraits<KV>::T* k_pool, typename KvTraits<KV>::T* v_pool,
+                       const pkv_cache_desc* c, int64_t num_tokens, int64_t num_slots,
+                       hipStream_t s) {
+  const int64_t chunks = (num_tokens + c->block_size - 1) / c->block_size;
+  if (chunks > 0x7fffffff) return fail(PKV_E_INVAL, "too many tokens for one call");
+  const dim3 grid(static_cast<unsigned>(chunks)), block(kRunsThreads);
+  const float ks = KV == KV_FP8 ? c->k_scale : 1.f, vs = KV == KV_FP8 ? c->v_scale : 1.f;
+  const int H = c->num_kv_heads, D = c->head_dim;
+  switch (c->block_size) {
+    case 8:
+      reshape_and_cache_runs_kernel<KV, In, 8><<<grid, block, 0, s>>>(
+          k, v, slots, k_pool, v_pool, H, D, num_tokens, num_slots, ks, vs);
+      return PKV_OK;
+    case 16:
+      reshape_and_cache_runs_kernel<KV, In, 16><<<grid, block, 0, s>>>(
+          k, v, slots, k_pool, v_pool, H, D, num_tokens, num_slots, ks, vs);
+      return PKV_OK;
+    case 32:
+      reshape_and_cache_runs_kernel<KV, In, 32><<<grid, block, 0, s>>>(
+          k, v, slots, k_pool, v_pool, H, D, num_tokens, num_slots, ks, vs);
+      return PKV_OK;
+  }
+  return fail(PKV_E_UNSUPPORTED, "block_size %d", c->block_size);
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -201,8 +351,32 @@ extern "C" int pkv_reshape_and_cache(const void* k, const void* v, int32_t in_dt
                 dtype_name(c->kv_dtype));
   const int64_t num_slots = int64_t(c->num_blocks) * c->block_size;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(num_tokens)), block(128);
   const int H = c->num_kv_heads, D = c->head_dim, B = c->block_size;
+  if (num_tokens >= kRunsMinTokens) {
+    int rc;
+    if (c->kv_dtype == PKV_F32)
+      rc = launch_runs<KV_F32>(static_cast<const float*>(k), static_cast<const float*>(v),
+                               slot_mapping, static_cast<float*>(k_pool),
+                               static_cast<float*>(v_pool), c, num_tokens, num_slots, s);
+    else if (c->kv_dtype == PKV_BF16)
+      rc = launch_runs<KV_BF16>(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                slot_mapping, static_cast<uint16_t*>(k_pool),
+                                static_cast<uint16_t*>(v_pool), c, num_tokens, num_slots, s);
+    else if (in_dtype == PKV_BF16)
+      rc = launch_runs<KV_FP8>(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                               slot_mapping, static_cast<uint8_t*>(k_pool),
+                               static_cast<uint8_t*>(v_pool), c, num_tokens, num_slots, s);
+    else
+      rc = launch_runs<KV_FP8>(static_cast<const float*>(k), static_cast<const float*>(v),
+                               slot_mapping, static_cast<uint8_t*>(k_pool),
+                               static_cast<uint8_t*>(v_pool), c, num_tokens, num_slots, s);
+    if (rc) return rc;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PKV_E_HIP, "reshape_and_cache launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
+  const dim3 grid(static_cast<unsigned>(num_tokens)), block(128);
   if (c->kv_dtype == PKV_F32) {
     reshape_and_cache_kernel<KV_F32, float><<<grid, block, 0, s>>>(
         static_cast<const float*>(k), static_cast<const float*>(v), slot_mapping,
