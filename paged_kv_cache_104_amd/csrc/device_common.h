@@ -42,23 +42,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 }
 
 // float -> OCP FP8 E4M3FN code: round to nearest, ties to even, saturate at +-448,
-// NaN -> 0x7F, sign kept (negative values that round to zero give 0x80).
+// NaN -> 0x7F, sign kept (negative values that round to zero give 0x80).  Both
+// rounding paths are computed and the result selected, without branches: a cache
+// write encodes every element, and per-element branches cost more than the paths.
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   const uint32_t u = __float_as_uint(y);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;                     // NaN
   const float af = __uint_as_float(a);
-  if (af > 448.0f) return sign | 0x7eu;                  // saturate (incl. inf)
-  if (af < 0.015625f) {                                  // below 2^-6: steps of 2^-9
-    // af * 512 is exact; rint rounds half to even; 8 gives code 0x08 = 2^-6
-    return sign | uint32_t(__builtin_rintf(af * 512.0f));
-  }
-  // normal: keep 3 of 23 mantissa bits, rounding at bit 20 to nearest even;
-  // a carry into the exponent is the correct next binade
-  uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-  r -= 120u << 3;                                        // exponent bias 127 -> 7
-  return sign | r;
+  // below 2^-6: steps of 2^-9; af * 512 is exact, rint rounds half to even, and 8
+  // gives code 0x08 = 2^-6
+  const uint32_t sub = uint32_t(__builtin_rintf(fminf(af, 0.015625f) * 512.0f));
+  // normal: keep 3 of 23 mantissa bits, rounding at bit 20 to nearest even (a carry
+  // into the exponent is the correct next binade), exponent bias 127 -> 7
+  const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t r = af < 0.015625f ? sub : nrm;
+  r = af > 448.0f ? 0x7eu : r;                           // saturate (incl. inf)
+  return a > 0x7f800000u ? 0x7fu : (sign | r);           // NaN
 }
 
 template <int KV>
