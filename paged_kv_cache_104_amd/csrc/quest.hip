@@ -79,11 +79,19 @@ __device__ __forceinline__ void slab_minmax(const typename KvTraits<KV>::T* __re
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     T lo = slab[d], hi = lo;
     float flo = kv_to_f32<KV>(lo), fhi = flo;
-    for (int r = 1; r < count; ++r) {
-      const T x = slab[int64_t(r) * D + d];
-      const float f = kv_to_f32<KV>(x);
-      if (f < flo) { flo = f; lo = x; }
-      if (f > fhi) { fhi = f; hi = x; }
+    for (int r0 = 1; r0 < count; r0 += 8) {
+      // eight rows' loads issued together, then compared in row order (a compare between
+      // two loads made each load wait for the one before); rows past count repeat the
+      // last one, which changes neither extreme
+      T x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = slab[int64_t(min(r0 + i, count - 1)) * D + d];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float f = kv_to_f32<KV>(x[i]);
+        if (f < flo) { flo = f; lo = x[i]; }
+        if (f > fhi) { fhi = f; hi = x[i]; }
+      }
     }
     meta[d] = lo;
     meta[D + d] = hi;
