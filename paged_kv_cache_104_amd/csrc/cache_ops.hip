@@ -117,11 +117,23 @@ __device__ __forceinline__ void write_token(
                               k_inv);
   }
   // values: one element per thread, consecutive threads on consecutive dimensions, so
-  // the lanes that write one line of the dimension-major tile do it in one instruction
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int h = e / head_dim, d = e - h * head_dim;
-    T* vd = v_pool + tile0 + h * head_stride + int64_t(d) * block_size + pos;
-    __builtin_nontemporal_store(encode_value<KV, In>(v[tok * n + e], v_inv), vd);
+  // the lanes that write one line of the dimension-major tile do it in one instruction;
+  // eight elements' loads are requested before any is stored
+  for (int e0 = threadIdx.x; e0 < n; e0 += 8 * blockDim.x) {
+    In raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * int(blockDim.x);
+      raw[i] = v[tok * n + min(e, n - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * int(blockDim.x);
+      if (e >= n) break;
+      const int h = e / head_dim, d = e - h * head_dim;
+      T* vd = v_pool + tile0 + h * head_stride + int64_t(d) * block_size + pos;
+      __builtin_nontemporal_store(encode_value<KV, In>(raw[i], v_inv), vd);
+    }
   }
 }
 
