@@ -27,7 +27,21 @@ def _draw(seed):
                 ps=int(rng.choice([0, B, 2 * B, 256, 1024])))
 
 
-CASES = [_draw(i) for i in range(24)]
+def _draw_wide(seed):
+    """Batches of 100 to 400 sequences: more (sequence, KV head) pairs than a quarter of the
+    workers, so the bf16 decode runs all of them (the small draws above run half)."""
+    rng = np.random.default_rng(9500 + seed)
+    hkv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    B = int(rng.choice([8, 16, 32]))
+    max_ctx = int(rng.choice([33, 200, 700]))
+    return dict(seed=5500 + seed, S=int(rng.integers(100, 401)), Hq=g * hkv, Hkv=hkv,
+                D=int(rng.choice([64, 128])), B=B, max_ctx=max_ctx, min_ctx=1,
+                kv_dtype=str(rng.choice(["bf16", "fp8"])), in_dtype="bf16",
+                ps=int(rng.choice([0, B, 256])))
+
+
+CASES = [_draw(i) for i in range(24)] + [_draw_wide(i) for i in range(12)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c['seed']}")
