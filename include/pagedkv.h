@@ -198,7 +198,10 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                 max(1, ctx / P) partitions of P tokens, the last one also
  *                 taking the remainder, run in parallel and merged.  MFMA
  *                 kernel: the batch's steps are shared out evenly over the
- *                 persistent workers, each taking at least P tokens (0 = no
+ *                 persistent workers (as many as fit on the device, half as
+ *                 many for a batch of few long (sequence, head) pairs; only
+ *                 those that can get steps are launched), each taking at
+ *                 least P tokens (0 = no
  *                 lower bound) as long as that leaves at least half the
  *                 workers some steps; contexts that cross a worker boundary
  *                 are merged.
