@@ -156,8 +156,9 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(
 // workgroup takes B consecutive tokens.  Keys go out as contiguous row segments as above.
 // For the values, each thread owns one (head, dimension) row at a time and gathers that
 // element of every token of the chunk into registers.  When the chunk's tokens fill one
-// block in order (the usual prefill: every block of a prompt but its last), the row is
-// written whole, B elements with 16-byte stores (8 bytes for an fp8 pool of 8-token
+// block in order (every block but the last of a prompt whose first token is a multiple of
+// B tokens into the call), the row is written whole, B elements with 16-byte stores (8
+// bytes for an fp8 pool of 8-token
 // blocks); otherwise each token's element is stored alone: through the caches when a
 // neighbouring token of the chunk shares its block, so that the parts of a line meet in
 // L2, and streamed when it is alone in its block (a decode step's token, whose partial
