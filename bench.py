@@ -529,18 +529,33 @@ def cache_ops_bench(tokens: int, reps: int) -> None:
         desc = pkv.cache_desc(2 * n_blk + 1, H, B, D, kv, scale, scale)
         kp, vp = pkv.alloc_pools(desc, poison=False)
         elem = 2 if kv == "bf16" else 1
-        # reshape_and_cache: whole blocks at random places
-        blocks = rng.permutation(2 * n_blk + 1)[:n_blk]
-        t = np.arange(tokens)
-        slots = torch.from_numpy(blocks[t // B] * B + t % B).cuda()
+        # reshape_and_cache: one prompt in whole blocks at random places, a batch of prompts
+        # of random lengths laid end to end (each in its own random blocks, so most chunks of
+        # B tokens straddle two blocks), and distinct random slots (about half the rows of
+        # the blocks they touch)
         k = torch.randn(tokens, H, D, device="cuda").to(torch.bfloat16)
         v = torch.randn(tokens, H, D, device="cuda").to(torch.bfloat16)
-        sec = timed(lambda: pkv.reshape_and_cache(k, v, slots, kp, vp, desc))
-        nbytes = tokens * H * D * (2 + elem) * 2
-        rows.append({"op": "reshape_and_cache", "kv_dtype": kv, "tokens": tokens,
-                     "bytes": nbytes, "us": round(sec * 1e6, 1),
-                     "GBps": round(nbytes / sec / 1e9, 1),
-                     "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
+        blocks = rng.permutation(2 * n_blk + 1)
+        t = np.arange(tokens)
+        lens = []
+        while sum(lens) < tokens:
+            lens.append(int(min(rng.integers(1, 2001), tokens - sum(lens))))
+        batch, used = [], 0
+        for n in lens:
+            p = np.arange(n)
+            batch.append(blocks[used + p // B] * B + p % B)
+            used += -(-n // B)
+        scattered = rng.permutation(len(blocks) * B)[:tokens]
+        for layout, sl in (("one prompt", blocks[t // B] * B + t % B),
+                           (f"{len(lens)} prompts", np.concatenate(batch)),
+                           ("scattered slots", scattered)):
+            slots = torch.from_numpy(sl.astype(np.int64)).cuda()
+            sec = timed(lambda: pkv.reshape_and_cache(k, v, slots, kp, vp, desc))
+            nbytes = tokens * H * D * (2 + elem) * 2
+            rows.append({"op": "reshape_and_cache", "kv_dtype": kv, "tokens": tokens,
+                         "layout": layout, "bytes": nbytes, "us": round(sec * 1e6, 1),
+                         "GBps": round(nbytes / sec / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
         # copy_blocks: n_blk pairs, sources and destinations disjoint, random
         perm = rng.permutation(2 * n_blk)
         pairs = torch.from_numpy(np.stack([perm[:n_blk], perm[n_blk:]], 1).astype(np.int64)).cuda()

@@ -154,15 +154,18 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(
 // is dimension-major, so one token writes one element in each of its D rows, a few bytes
 // of every line; one store per element held such writes near 0.5 TB/s.  Here one
 // workgroup takes B consecutive tokens.  Keys go out as contiguous row segments as above.
-// For the values, each thread owns one (head, dimension) row at a time and gathers that
-// element of every token of the chunk into registers.  When the chunk's tokens fill one
-// block in order (every block but the last of a prompt whose first token is a multiple of
-// B tokens into the call), the row is written whole, B elements with 16-byte stores (8
-// bytes for an fp8 pool of 8-token
-// blocks); otherwise each token's element is stored alone: through the caches when a
-// neighbouring token of the chunk shares its block, so that the parts of a line meet in
-// L2, and streamed when it is alone in its block (a decode step's token, whose partial
-// lines would otherwise sit dirty in L2 when the decode reads that block).
+// For the values the call's tokens fall into runs: maximal sequences of consecutive
+// tokens whose slots are consecutive within one block.  A run holds at most B tokens and
+// belongs to the workgroup of the chunk its first token is in (it may reach into the next
+// chunk), so every token is written once.  A run of B tokens fills its block: each thread
+// owns one (head, dimension) row at a time, gathers that element of the run's tokens into
+// registers and writes the row whole, with 16-byte stores (8 bytes for an fp8 pool of
+// 8-token blocks).  Prompts laid end to end in one call are such runs in every block but
+// the last of each prompt, wherever the prompts start in the call.  The tokens of shorter
+// runs are stored one element at a time: through the caches when a neighbouring token
+// shares its block, so that the parts of a line meet in L2, and streamed when it is alone
+// in its block (a decode step's token, whose partial lines would otherwise sit dirty in L2
+// when the decode reads that block).
 constexpr int kRunsThreads = 256;
 constexpr int64_t kRunsMinTokens = 512;    // fewer: the per-token kernel (decode steps)
 
@@ -203,67 +206,106 @@ __global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
     int num_kv_heads, int head_dim, int64_t num_tokens, int64_t num_slots, double k_inv,
     double v_inv) {
   typedef typename KvTraits<KV>::T T;
-  __shared__ int64_t s_blk[B];   // block of the chunk's token j, or -1: skipped
-  __shared__ int s_off[B];
+  static_assert(2 * B <= 64 && 2 * B + 1 <= kRunsThreads,
+                "the window fits the workgroup, its bit masks one wavefront");
+  // the window: tokens i0 - 1 .. i0 + 2B - 1 at index t = token - i0 + 1
+  __shared__ int64_t s_blk[2 * B + 1];   // block of the token, or -1: skipped / outside the call
+  __shared__ int s_off[2 * B + 1];
+  __shared__ int s_part[2 * B];          // token i0 + j is in a shorter run this chunk owns
+  __shared__ int s_whole;                // first token (minus i0) of the run of B tokens, or -1
+  __shared__ uint64_t s_mask[2];         // bit j: s_part[j]; of those, stored streamed
   const int64_t i0 = int64_t(blockIdx.x) * B;
   const int n_tok = int(min<int64_t>(B, num_tokens - i0));
   const int H = num_kv_heads, D = head_dim, n = H * D;
-  if (int(threadIdx.x) < B) {
+  const int tid = threadIdx.x;
+  if (tid < 2 * B + 1) {
+    const int64_t tok = i0 - 1 + tid;
     int64_t blk = -1;
     int off = 0;
-    if (int(threadIdx.x) < n_tok) {
-      const int64_t sl = slots[i0 + threadIdx.x];
+    if (tok >= 0 && tok < num_tokens) {
+      const int64_t sl = slots[tok];
       if (sl >= 0 && sl < num_slots) {
         blk = sl / B;
         off = int(sl - blk * B);
       }
     }
-    s_blk[threadIdx.x] = blk;
-    s_off[threadIdx.x] = off;
+    s_blk[tid] = blk;
+    s_off[tid] = off;
+  }
+  if (tid < 2 * B) s_part[tid] = 0;
+  if (tid == 0) s_whole = -1;
+  __syncthreads();
+  if (tid < B) {
+    // does a run start at token i0 + tid, and how long is it
+    const int t = tid + 1;
+    const int64_t blk = s_blk[t];
+    if (blk >= 0 && !(s_blk[t - 1] == blk && s_off[t - 1] + 1 == s_off[t])) {
+      int len = 1;
+      while (len < B && s_blk[t + len] == blk && s_off[t + len] == s_off[t] + len) ++len;
+      if (len == B) s_whole = tid;   // at most one: a second would start B tokens later
+      else
+        for (int j = tid; j < tid + len; ++j) s_part[j] = 1;
+    }
   }
   __syncthreads();
-  // one whole block, its tokens in order: every value row is written whole
-  bool whole = n_tok == B && s_blk[0] >= 0;
-#pragma unroll
-  for (int j = 0; j < B; ++j) whole = whole && s_blk[j] == s_blk[0] && s_off[j] == j;
-  // keys
-  for (int e = threadIdx.x; e < n_tok * (n / 8); e += kRunsThreads) {
+  if (tid < 64) {
+    // the first wavefront gathers the shorter runs' tokens into two bit masks
+    const int t = tid + 1;
+    const bool part = tid < 2 * B && s_part[tid] != 0;
+    const bool alone = part && s_blk[t - 1] != s_blk[t] && s_blk[min(t + 1, 2 * B)] != s_blk[t];
+    const uint64_t pm = __ballot(part), am = __ballot(alone);
+    if (tid == 0) {
+      s_mask[0] = pm;
+      s_mask[1] = am;
+    }
+  }
+  __syncthreads();
+  // keys: every token of the chunk
+  for (int e = tid; e < n_tok * (n / 8); e += kRunsThreads) {
     const int j = e / (n / 8), ch = e - j * (n / 8);
-    const int64_t blk = s_blk[j];
+    const int64_t blk = s_blk[j + 1];
     if (blk < 0) continue;
     const int h = (ch * 8) / D, d0 = ch * 8 - h * D;
     write_key_segment<KV, In>(k + (i0 + j) * n + ch * 8,
-                              k_pool + (blk * H + h) * int64_t(B) * D + int64_t(s_off[j]) * D + d0,
+                              k_pool + (blk * H + h) * int64_t(B) * D + int64_t(s_off[j + 1]) * D + d0,
                               k_inv);
   }
-  // values: row e = h * D + d of every token of the chunk
-  for (int e = threadIdx.x; e < n; e += kRunsThreads) {
-    const int h = e / D, d = e - h * D;
-    // all B loads first, then the encodes: an encode between two loads would make each
-    // load wait for the one before it (fp8: 221 against 117 us for 65 536 tokens)
-    In raw[B];
-    if (n_tok == B) {
+  // values: row e = h * D + d of the value tiles, at element e * B of the (block, 0) tile
+  // (the tiles of one block's heads follow one another).  All of a pass's loads are issued
+  // before its encodes: an encode between two loads would make each load wait for the one
+  // before it (fp8: 221 against 117 us for 65 536 tokens).
+  const int whole = s_whole;
+  const uint64_t part_mask = s_mask[0], alone_mask = s_mask[1];
+  if (whole >= 0) {
+    const int64_t s0 = i0 + whole;
+    T* const tile = v_pool + s_blk[whole + 1] * n * int64_t(B);
+    for (int e = tid; e < n; e += kRunsThreads) {
+      In raw[B];
 #pragma unroll
-      for (int j = 0; j < B; ++j) raw[j] = v[(i0 + j) * n + e];
-    } else {
+      for (int j = 0; j < B; ++j) raw[j] = v[(s0 + j) * n + e];
+      T x[B];
 #pragma unroll
-      for (int j = 0; j < B; ++j) raw[j] = j < n_tok ? v[(i0 + j) * n + e] : In(0);
+      for (int j = 0; j < B; ++j) x[j] = encode_value<KV, In>(raw[j], v_inv);
+      store_value_row<KV, B>(tile + int64_t(e) * B, x);
     }
-    T x[B];
+  }
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t pm = uint32_t(part_mask >> (half * B)), am = uint32_t(alone_mask >> (half * B));
+    if (pm == 0) continue;
+    const int j0 = half * B;
+    for (int e = tid; e < n; e += kRunsThreads) {
+      In raw[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) x[j] = encode_value<KV, In>(raw[j], v_inv);
-    if (whole) {
-      store_value_row<KV, B>(v_pool + ((s_blk[0] * H + h) * int64_t(D) + d) * B, x);
-    } else {
+      for (int j = 0; j < B; ++j) raw[j] = (pm >> j) & 1u ? v[(i0 + j0 + j) * n + e] : In(0);
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        const int64_t blk = j < n_tok ? s_blk[j] : -1;
-        if (blk < 0) continue;
-        T* dst = v_pool + ((blk * H + h) * int64_t(D) + d) * B + s_off[j];
-        const bool alone = (j == 0 || s_blk[j > 0 ? j - 1 : 0] != blk) &&
-                           (j + 1 >= n_tok || s_blk[j + 1 < B ? j + 1 : B - 1] != blk);
-        if (alone) __builtin_nontemporal_store(x[j], dst);
-        else *dst = x[j];
+        if (!((pm >> j) & 1u)) continue;
+        const int t = j0 + j + 1;
+        T* dst = v_pool + s_blk[t] * n * int64_t(B) + int64_t(e) * B + s_off[t];
+        const T x = encode_value<KV, In>(raw[j], v_inv);
+        if ((am >> j) & 1u) __builtin_nontemporal_store(x, dst);
+        else *dst = x;
       }
     }
   }
