@@ -58,13 +58,11 @@ __device__ __forceinline__ void write_key_segment(const In* __restrict__ ks,
       kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
     }
     if constexpr (KV == KV_FP8) {
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_encode(div_by_scale(kf[i], k_inv)) << (8 * i);
-        hi |= e4m3_encode(div_by_scale(kf[i + 4], k_inv)) << (8 * i);
-      }
-      *reinterpret_cast<uint2*>(kd) = make_uint2(lo, hi);
+      for (int i = 0; i < 8; ++i) q[i] = div_by_scale(kf[i], k_inv);
+      *reinterpret_cast<uint2*>(kd) = make_uint2(e4m3_encode4(q[0], q[1], q[2], q[3]),
+                                                 e4m3_encode4(q[4], q[5], q[6], q[7]));
     } else {
       reinterpret_cast<float4*>(kd)[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
       reinterpret_cast<float4*>(kd)[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
@@ -175,19 +173,36 @@ __device__ __forceinline__ uint32_t storage_bits(T x) {
   else return uint32_t(x);
 }
 
-// B elements of one row of the dimension-major value tile, as whole 16-byte (or 8-byte)
-// stores; dst is the row's start (aligned: a row is B elements, 8 B at least).
-template <int KV, int B>
+// B input elements as one row of the dimension-major value tile, encoded and written
+// with whole 16-byte (or 8-byte) stores; dst is the row's start (aligned: a row is B
+// elements, 8 bytes at least).
+template <int KV, typename In, int B>
 __device__ __forceinline__ void store_value_row(typename KvTraits<KV>::T* __restrict__ dst,
-                                                const typename KvTraits<KV>::T (&x)[B]) {
-  constexpr int bytes = KvTraits<KV>::bytes, per_word = 4 / bytes, words = B * bytes / 4;
+                                                const In (&raw)[B], double v_inv) {
+  constexpr int words = B * KvTraits<KV>::bytes / 4;
   uint32_t w[words];
+  if constexpr (KV == KV_FP8) {
+    float q[B];
 #pragma unroll
-  for (int i = 0; i < words; ++i) {
-    uint32_t u = 0;
+    for (int j = 0; j < B; ++j) {
+      float f;
+      if constexpr (sizeof(In) == 2) f = bf16_to_f32(raw[j]); else f = raw[j];
+      q[j] = div_by_scale(f, v_inv);
+    }
 #pragma unroll
-    for (int b = 0; b < per_word; ++b) u |= storage_bits(x[i * per_word + b]) << (8 * bytes * b);
-    w[i] = u;
+    for (int i = 0; i < words; ++i)
+      w[i] = e4m3_encode4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+  } else {
+    constexpr int per_word = 4 / KvTraits<KV>::bytes;
+#pragma unroll
+    for (int i = 0; i < words; ++i) {
+      uint32_t u = 0;
+#pragma unroll
+      for (int b = 0; b < per_word; ++b)
+        u |= storage_bits(encode_value<KV, In>(raw[i * per_word + b], v_inv))
+             << (8 * KvTraits<KV>::bytes * b);
+      w[i] = u;
+    }
   }
   if constexpr (words % 4 == 0) {
 #pragma unroll
@@ -283,10 +298,7 @@ __global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
       In raw[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) raw[j] = v[(s0 + j) * n + e];
-      T x[B];
-#pragma unroll
-      for (int j = 0; j < B; ++j) x[j] = encode_value<KV, In>(raw[j], v_inv);
-      store_value_row<KV, B>(tile + int64_t(e) * B, x);
+      store_value_row<KV, In, B>(tile + int64_t(e) * B, raw, v_inv);
     }
   }
 #pragma unroll 1

@@ -41,24 +41,27 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __uint_as_float(__float_as_uint(mag) | sign);
 }
 
-// float -> OCP FP8 E4M3FN code: round to nearest, ties to even, saturate at +-448,
-// NaN -> 0x7F, sign kept (negative values that round to zero give 0x80).  Both
-// rounding paths are computed and the result selected, without branches: a cache
-// write encodes every element, and per-element branches cost more than the paths.
+// float -> OCP FP8 E4M3FN code: round to nearest, ties to even (subnormals in steps of
+// 2^-9), saturate at +-448, NaN -> 0x7F, sign kept (negative values that round to zero
+// give 0x80).  The conversion instruction rounds the same way but codes magnitudes past
+// 448 (infinities too) as NaN and every NaN as 0xFF, so its input is first clamped to
+// +-448, and a NaN enters as +inf, which it codes 0x7F.  A cache write encodes every
+// element; three instructions per element (and one per pair for the conversion) keep
+// that write bound by memory rather than by the encode.
+__device__ __forceinline__ float e4m3_saturate(float y) {
+  return y != y ? __builtin_inff() : __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f);
+}
+
 __device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const float af = __uint_as_float(a);
-  // below 2^-6: steps of 2^-9; af * 512 is exact, rint rounds half to even, and 8
-  // gives code 0x08 = 2^-6
-  const uint32_t sub = uint32_t(__builtin_rintf(fminf(af, 0.015625f) * 512.0f));
-  // normal: keep 3 of 23 mantissa bits, rounding at bit 20 to nearest even (a carry
-  // into the exponent is the correct next binade), exponent bias 127 -> 7
-  const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  uint32_t r = af < 0.015625f ? sub : nrm;
-  r = af > 448.0f ? 0x7eu : r;                           // saturate (incl. inf)
-  return a > 0x7f800000u ? 0x7fu : (sign | r);           // NaN
+  const float c = e4m3_saturate(y);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xffu;
+}
+
+// The codes of a, b, c, d in bytes 0, 1, 2, 3 of one word.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), w, true);
+  return uint32_t(w);
 }
 
 template <int KV>

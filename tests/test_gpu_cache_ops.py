@@ -156,8 +156,12 @@ def test_fp8_encode_sweep_f32_input(scale):
     assert np.array_equal(gv, want)
 
 
-def test_fp8_encode_every_bf16_input():
-    """Every bf16 input (65536 patterns) through the bf16 -> fp8 cache write."""
+@pytest.mark.parametrize("layout", ["in order", "reversed", "small calls"])
+def test_fp8_encode_every_bf16_input(layout):
+    """Every bf16 input (65536 patterns) through the bf16 -> fp8 cache write, keys and
+    values, by each of the write's encode paths: whole value rows (tokens in order, one
+    call), single value elements (slots in reverse order, so no two neighbouring tokens
+    share a row run) and the per-token kernel (calls of fewer than 512 tokens)."""
     import paged_kv_cache_104_amd as pkv
 
     torch = torch_mod()
@@ -165,15 +169,20 @@ def test_fp8_encode_every_bf16_input():
     H, D, B = 2, 64, 16
     T = bits.size // (H * D)
     N = T // B
+    order = np.arange(T)[::-1].copy() if layout == "reversed" else np.arange(T)
+    calls = [(0, 200), (200, 400), (400, T)] if layout == "small calls" else [(0, T)]
     for scale in (1.0, 0.0078125, 0.37):
         desc = pkv.cache_desc(N, H, B, D, "fp8", scale, scale)
         kp, vp = pkv.alloc_pools(desc)
         xt = torch.from_numpy(bits.view(np.int16).reshape(T, H, D)).view(torch.bfloat16).cuda()
-        slots = torch.arange(T, dtype=torch.int64, device="cuda")
-        pkv.reshape_and_cache(xt, xt, slots, kp, vp, desc)
-        got = kp.cpu().numpy().reshape(N, H, B, D).transpose(0, 2, 1, 3).reshape(-1)
-        want = codec.e4m3_quantize(codec.bf16_to_f32(bits), scale)
-        assert np.array_equal(got, want), scale
+        slots = torch.from_numpy(order.astype(np.int64)).cuda()
+        for a, b in calls:
+            pkv.reshape_and_cache(xt[a:b], xt[a:b], slots[a:b], kp, vp, desc)
+        want = codec.e4m3_quantize(codec.bf16_to_f32(bits), scale).reshape(T, H, D)[np.argsort(order)]
+        got_k = kp.cpu().numpy().reshape(N, H, B, D).transpose(0, 2, 1, 3).reshape(T, H, D)
+        got_v = vp.cpu().numpy().reshape(N, H, D, B).transpose(0, 3, 1, 2).reshape(T, H, D)
+        assert np.array_equal(got_k, want), scale
+        assert np.array_equal(got_v, want), scale
 
 
 def test_negative_slots_are_skipped():
