@@ -425,8 +425,10 @@ int pkv_paged_attn_decode_rows(const void* q, int32_t q_dtype,
  * Metadata: device [num_blocks][num_kv_heads][2][head_dim] of the pool's
  * kv_dtype, pkv_quest_meta_bytes(c) bytes; row 0 the minimum, row 1 the
  * maximum (stored codes, exact: min / max of values of a type are values of
- * it).  The caller keeps it current after writing keys: a block's entry
- * covers its first `count` slots as of the last update.
+ * it).  For an fp8 pool a channel holding both zeros stores -0 as its minimum
+ * and +0 as its maximum, and a NaN key becomes its channel's maximum (code
+ * 0x7F) or minimum (0xFF).  The caller keeps it current after writing keys: a
+ * block's entry covers its first `count` slots as of the last update.
  */
 size_t pkv_quest_meta_bytes(const pkv_cache_desc* c);
 

@@ -98,6 +98,78 @@ __device__ __forceinline__ void slab_minmax(const typename KvTraits<KV>::T* __re
   }
 }
 
+// fp8 keys: the codes are sign and magnitude, so their values order as the bytes
+// c ^ 0x80 (c >= 0) and c ^ 0xFF (c < 0) do as unsigned numbers (-0 just below +0; the
+// NaN codes 0x7F and 0xFF at the top and the bottom).  A thread owns four channels (one
+// 32-bit word of a row) and every kQuestFp8RowGroups-th row of the slab; the minimum and
+// maximum of each byte are taken on two 16-bit halves (even and odd bytes) with packed
+// 16-bit integer min / max, the row groups are combined through LDS, and the order map,
+// its own inverse up to the top bit's test, is undone before the store.  Two or three
+// integer instructions per key, against a decode to fp32 and two float compares: the fp32
+// path held the whole-pool update near 3 TB/s, bound by arithmetic.  A 128-thread
+// workgroup.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t fp8_order(uint32_t u) {   // four codes at once
+  const uint32_t neg = (u >> 7) & 0x01010101u;
+  return u ^ ((neg << 7) - neg) ^ 0x80808080u;                 // 0xFF where negative, else 0x80
+}
+__device__ __forceinline__ uint32_t fp8_unorder(uint32_t k) {
+  const uint32_t pos = (k >> 7) & 0x01010101u;                 // top bit set: a code >= 0
+  return k ^ ((pos << 7) - pos) ^ 0xFFFFFFFFu;                 // 0x80 where it was >= 0, else 0xFF
+}
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+__device__ __forceinline__ void slab_minmax_fp8(const uint8_t* __restrict__ slab,
+                                                uint8_t* __restrict__ meta, int count, int D) {
+  constexpr int kThreads = 128;
+  __shared__ uint32_t s_m[4][kThreads];    // min even, min odd, max even, max odd
+  const int groups = D / 4, row_groups = kThreads / groups;
+  const int cg = threadIdx.x % groups, rg = threadIdx.x / groups;
+  uint32_t mn_e = 0x00ff00ffu, mn_o = 0x00ff00ffu, mx_e = 0, mx_o = 0;
+  for (int r0 = rg; r0 < count; r0 += 4 * row_groups) {
+    // four rows' words requested together; rows past count repeat the last one
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = *reinterpret_cast<const uint32_t*>(slab + int64_t(min(r0 + i * row_groups, count - 1)) * D + cg * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k = fp8_order(w[i]);
+      const uint32_t e = k & 0x00ff00ffu, o = (k >> 8) & 0x00ff00ffu;
+      mn_e = as_u32(__builtin_elementwise_min(as_u16x2(mn_e), as_u16x2(e)));
+      mn_o = as_u32(__builtin_elementwise_min(as_u16x2(mn_o), as_u16x2(o)));
+      mx_e = as_u32(__builtin_elementwise_max(as_u16x2(mx_e), as_u16x2(e)));
+      mx_o = as_u32(__builtin_elementwise_max(as_u16x2(mx_o), as_u16x2(o)));
+    }
+  }
+  s_m[0][threadIdx.x] = mn_e;
+  s_m[1][threadIdx.x] = mn_o;
+  s_m[2][threadIdx.x] = mx_e;
+  s_m[3][threadIdx.x] = mx_o;
+  __syncthreads();
+  if (rg == 0) {
+    for (int g = 1; g < row_groups; ++g) {
+      const int t = g * groups + cg;
+      mn_e = as_u32(__builtin_elementwise_min(as_u16x2(mn_e), as_u16x2(s_m[0][t])));
+      mn_o = as_u32(__builtin_elementwise_min(as_u16x2(mn_o), as_u16x2(s_m[1][t])));
+      mx_e = as_u32(__builtin_elementwise_max(as_u16x2(mx_e), as_u16x2(s_m[2][t])));
+      mx_o = as_u32(__builtin_elementwise_max(as_u16x2(mx_o), as_u16x2(s_m[3][t])));
+    }
+    *reinterpret_cast<uint32_t*>(meta + cg * 4) = fp8_unorder(mn_e | (mn_o << 8));
+    *reinterpret_cast<uint32_t*>(meta + D + cg * 4) = fp8_unorder(mx_e | (mx_o << 8));
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ void slab_update(const typename KvTraits<KV>::T* __restrict__ slab,
+                                            typename KvTraits<KV>::T* __restrict__ meta,
+                                            int count, int D) {
+  if constexpr (KV == KV_FP8) slab_minmax_fp8(slab, meta, count, D);
+  else slab_minmax<KV>(slab, meta, count, D);
+}
+
 // Entry i: block blocks[i] over its first counts[i] slots, for head blockIdx.y.
 template <int KV>
 __global__ __launch_bounds__(128) void quest_update_blocks_kernel(
@@ -107,7 +179,7 @@ __global__ __launch_bounds__(128) void quest_update_blocks_kernel(
   const int b = blocks[blockIdx.x], cnt = counts[blockIdx.x], h = blockIdx.y;
   if (b < 0 || b >= N || cnt < 1 || cnt > B) return;
   const int64_t slab = int64_t(b) * H + h;
-  slab_minmax<KV>(k_pool + slab * B * D, meta + slab * 2 * D, cnt, D);
+  slab_update<KV>(k_pool + slab * B * D, meta + slab * 2 * D, cnt, D);
 }
 
 // Row blockIdx.x: the block that holds its last token (context_lens - 1).
@@ -123,7 +195,7 @@ __global__ __launch_bounds__(128) void quest_update_tails_kernel(
   const int b = tables[int64_t(blockIdx.x) * max_blocks + j];
   if (b < 0 || b >= N) return;
   const int64_t slab = int64_t(b) * H + h;
-  slab_minmax<KV>(k_pool + slab * B * D, meta + slab * 2 * D, (len - 1) % B + 1, D);
+  slab_update<KV>(k_pool + slab * B * D, meta + slab * 2 * D, (len - 1) % B + 1, D);
 }
 
 // ------------------------------------------------------------------------ scores
@@ -165,11 +237,16 @@ __device__ __forceinline__ void unpack8(const Raw8<KV_BF16>& r, float (&f)[8]) {
     f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
 }
+// fp8: the conversion instruction, two codes at a time (exact: every E4M3 value is an
+// fp32 value).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void unpack8(const Raw8<KV_FP8>& r, float (&f)[8]) {
+  const uint32_t w[2] = {r.a.x, r.a.y};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = e4m3_to_f32((r.a.x >> (8 * i)) & 0xffu);
-    f[4 + i] = e4m3_to_f32((r.a.y >> (8 * i)) & 0xffu);
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), true);
+    f[4 * i] = lo.x; f[4 * i + 1] = lo.y; f[4 * i + 2] = hi.x; f[4 * i + 3] = hi.y;
   }
 }
 
