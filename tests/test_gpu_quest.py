@@ -170,6 +170,57 @@ def test_metadata_matches_oracle(kv):
                 assert np.array_equal(oattn.dequant(meta[pb, kvh, 1], kv), maxs[j]), (s, j)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_metadata_zeros_nan_and_counts(D):
+    """fp8 metadata over codes drawn from the whole code range, for every fill count of a
+    block: each channel's minimum and maximum are the codes of its smallest and largest
+    values; a channel whose smallest (largest) value is zero and that holds both zero codes
+    stores -0 = 0x80 (+0 = 0x00); a NaN code is its channel's maximum (0x7F) or minimum
+    (0xFF); rows past the count do not count."""
+    pkv = _pkv()
+    torch = torch_mod()
+    H, B = 2, 16
+    N = B + 1
+    desc = pkv.cache_desc(N, H, B, D, "fp8", 1.0, 1.0)
+    kp, _ = pkv.alloc_pools(desc)
+    rng = np.random.default_rng(D)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = rng.choice(finite, size=(N, H, B, D)).astype(np.uint8)
+    zeros = rng.random((N, H, B, D)) < 0.25                  # many signed zeros
+    codes[zeros] = rng.choice(np.array([0x00, 0x80], np.uint8), size=int(zeros.sum()))
+    nan = rng.random((N, H, B, D)) < 0.01
+    codes[nan] = rng.choice(np.array([0x7F, 0xFF], np.uint8), size=int(nan.sum()))
+    codes[0, :, :, :4] = rng.choice(np.array([0x00, 0x80], np.uint8), size=(H, B, 4))
+    kp.copy_(torch.from_numpy(codes).to(kp.device))
+    counts = np.array(list(range(1, B + 1)) + [B], np.int32)      # block b holds counts[b] rows
+    meta = pkv.alloc_quest_meta(desc)
+    pkv.quest_update_blocks(kp, meta, np.arange(N, dtype=np.int32), counts, desc)
+    torch.cuda.synchronize()
+    got = meta.cpu().numpy().reshape(N, H, 2, D)
+    vals = codec.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+
+    def extreme(col, use_min):
+        if (col == (0xFF if use_min else 0x7F)).any():
+            return 0xFF if use_min else 0x7F
+        col = col[(col != 0x7F) & (col != 0xFF)]
+        if col.size == 0:                      # only the other NaN code
+            return 0x7F if use_min else 0xFF
+        v = vals[col]
+        x = v.min() if use_min else v.max()
+        if x == 0:
+            present = set(col[v == 0].tolist())
+            return (0x80 if use_min else 0x00) if len(present) == 2 else present.pop()
+        return int(col[v == x][0])
+
+    for b in range(N):
+        for h in range(H):
+            rows = codes[b, h, :counts[b]]
+            want_lo = [extreme(rows[:, d], True) for d in range(D)]
+            want_hi = [extreme(rows[:, d], False) for d in range(D)]
+            assert got[b, h, 0].tolist() == want_lo, (b, h)
+            assert got[b, h, 1].tolist() == want_hi, (b, h)
+
+
 def test_metadata_follows_appends_and_swaps():
     """Engine path: decode-step appends (device tables) and a swap round trip keep the
     metadata equal to a recompute of every live block from the key pool."""
