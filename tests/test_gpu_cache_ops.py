@@ -205,8 +205,10 @@ def _large_write_slots(pattern, T, B, N, rng):
     end to end, each in its own randomly placed blocks, so chunks of B tokens straddle
     sequences), ``continued`` (the same, each sequence starting at a random row of its
     first block, as a prompt does after a cached prefix, with some tokens skipped),
-    ``scattered`` (distinct random slots, some negative or past the pool) or ``aligned``
-    (one prompt starting at a block's first slot)."""
+    ``scattered`` (distinct random slots, some negative or past the pool), ``aligned``
+    (one prompt starting at a block's first slot) or ``mixed`` (a batch that mixes prompt
+    chunks, some starting within a block, with single decode tokens each at a random row of
+    a block of its own)."""
     blocks = rng.permutation(N)
     if pattern == "aligned":
         t = np.arange(T)
@@ -218,8 +220,12 @@ def _large_write_slots(pattern, T, B, N, rng):
         return s
     out, used = [], 0
     while sum(len(x) for x in out) < T:
+        if pattern == "mixed" and rng.random() < 0.7:
+            out.append(np.array([blocks[used] * B + int(rng.integers(0, B))]))
+            used += 1
+            continue
         n = int(min(rng.integers(1, 700), T - sum(len(x) for x in out)))
-        first = int(rng.integers(0, B)) if pattern == "continued" else 0
+        first = int(rng.integers(0, B)) if pattern in ("continued", "mixed") else 0
         nb = -(-(first + n) // B)
         own = blocks[used:used + nb]
         used += nb
@@ -241,8 +247,9 @@ def test_large_writes_bitexact(case):
     """Writes of thousands of tokens (the path for prefills: chunks of one block's worth of
     tokens, whole value rows for a run of tokens that fills a block in order, single
     elements otherwise) leave both pools bit-identical to the oracle's cache write, for
-    prompts laid end to end (starting at a block's first row or within a block), one
-    aligned prompt and scattered slots with skipped ones."""
+    prompts laid end to end (starting at a block's first row or within a block), prompts
+    mixed with single decode tokens, one aligned prompt and scattered slots with skipped
+    ones."""
     import paged_kv_cache_104_amd as pkv
 
     torch = torch_mod()
@@ -252,7 +259,7 @@ def test_large_writes_bitexact(case):
     N = int(1.3 * T / B) + 64
     scale = 0.02 if kv == "fp8" else 1.0
     desc = pkv.cache_desc(N, H, B, D, kv, scale, scale)
-    for pattern in ("prompts", "continued", "aligned", "scattered"):
+    for pattern in ("prompts", "continued", "mixed", "aligned", "scattered"):
         print(f"large write {case} {pattern} T={T}", flush=True)
         slots = _large_write_slots(pattern, T, B, N, rng)
         x = rng.standard_normal((2, T, H, D)).astype(np.float32)
