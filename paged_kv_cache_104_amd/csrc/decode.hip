@@ -1445,7 +1445,7 @@ static int64_t resident_workers(K kernel) {
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
                                                    64, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
-    hipGetLastError();
+    (void)hipGetLastError();   // clear the failed query's error; fall back to a fixed count
     return 1024;
   }
   const int64_t n = int64_t(cus) * per_cu;
