@@ -250,13 +250,32 @@ __device__ __forceinline__ void unpack8(const Raw8<KV_FP8>& r, float (&f)[8]) {
   }
 }
 
+// Sum over the LPB (8 or 16) lanes that share a block, aligned groups inside one row of 16
+// lanes, with DPP lane moves instead of LDS permutes: swap neighbours, swap pairs, mirror
+// each half row (sums of the two quads), and for 16 lanes mirror the row.  Every lane of the
+// group ends with the same sum (each step adds two equal partial sums in either order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int LPB>
+__device__ __forceinline__ float group_sum(float u) {
+  static_assert(LPB == 8 || LPB == 16, "a block's lanes are a half row or a row");
+  u += dpp_move<0xb1>(u);    // quad_perm [1, 0, 3, 2]
+  u += dpp_move<0x4e>(u);    // quad_perm [2, 3, 0, 1]
+  u += dpp_move<0x141>(u);   // row_half_mirror
+  if constexpr (LPB == 16) u += dpp_move<0x140>(u);   // row_mirror
+  return u;
+}
+
 // Workgroup (pair, chunk): bounds of blocks [chunk * 64, chunk * 64 + 64) of
 // the pair's context.  D / 8 lanes share a block, 8 channels each, so a
 // block's minimum and maximum rows are read with coalesced 16-byte loads.
 // Every table entry and then every metadata row of the chunk is requested
 // before any arithmetic, so the workgroup waits for memory twice in all.  The
 // group's queries sit in LDS as fp32.  Each lane sums its 8 channels per head,
-// a butterfly over the block's lanes completes the bound, and the score is the
+// DPP moves over the block's lanes complete the bound, and the score is the
 // largest bound over the group's heads.  Pairs whose context fits the budget
 // are not scored (the selection keeps all their blocks).
 template <int KV, typename QT, int D>
@@ -305,28 +324,33 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(QuestArgs a)
     *reinterpret_cast<float4*>(&q_s[i / D][i % D + 4]) = make_float4(f[4], f[5], f[6], f[7]);
   }
   __syncthreads();
+  // every pass's block at once (a pass past the chunk's end scores block 0 and stores
+  // nothing), heads outer: each head's query segment is read from LDS once
+  float mn[PASSES][8], mx[PASSES][8], best[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    unpack8(rmn[p], mn[p]);
+    unpack8(rmx[p], mx[p]);
+    best[p] = -INFINITY;
+  }
+  for (int h = 0; h < g; ++h) {
+    const float4 qa = *reinterpret_cast<const float4*>(&q_s[h][d0]);
+    const float4 qb = *reinterpret_cast<const float4*>(&q_s[h][d0 + 4]);
+    const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float u = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u = fmaf(qv[i], qv[i] >= 0.f ? mx[p][i] : mn[p][i], u);
+      best[p] = fmaxf(best[p], group_sum<LPB>(u));
+    }
+  }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int j = j0 + slot + p * BPP;
-    if (j0 + p * BPP >= jend) break;          // uniform: no block of this pass is in range
-    float mn[8], mx[8];
-    unpack8(rmn[p], mn);
-    unpack8(rmx[p], mx);
-    float best = -INFINITY;
-    for (int h = 0; h < g; ++h) {
-      const float4 qa = *reinterpret_cast<const float4*>(&q_s[h][d0]);
-      const float4 qb = *reinterpret_cast<const float4*>(&q_s[h][d0 + 4]);
-      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-      float u = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u = fmaf(qv[i], qv[i] >= 0.f ? mx[i] : mn[i], u);
-#pragma unroll
-      for (int o = LPB / 2; o > 0; o >>= 1) u += __shfl_xor(u, o);
-      best = fmaxf(best, u);
-    }
     if (sub == 0 && j < jend)
       a.scores[int64_t(pair) * a.score_stride + j] =
-          (pb[p] >= 0 && pb[p] < a.num_blocks) ? best : -INFINITY;
+          (pb[p] >= 0 && pb[p] < a.num_blocks) ? best[p] : -INFINITY;
   }
 }
 
