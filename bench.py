@@ -501,7 +501,9 @@ def cache_ops_bench(tokens: int, reps: int) -> None:
     through ``pkv_reshape_and_cache`` into whole blocks placed at random in the pool (bf16,
     and fp8 encoded from bf16), and ``pkv_copy_blocks`` over as many blocks' worth of random
     (src, dst) pairs.  Bytes are the algorithmic ones, read plus written; a plain device copy
-    of the same bytes (torch ``copy_``) is timed beside them.  Median of ``reps`` launches."""
+    of the same bytes (torch ``copy_``) is timed beside them.  Then a decode step's write for
+    batches of 1024 to 16384 sequences (each token alone in a block), in one call and in calls
+    of 500 tokens.  Median of ``reps`` launches."""
     import torch
 
     import paged_kv_cache_104_amd as pkv
@@ -566,6 +568,32 @@ def cache_ops_bench(tokens: int, reps: int) -> None:
                      "GBps": round(nbytes / sec / 1e9, 1),
                      "frac_of_hbm_peak": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4)})
         del kp, vp, k, v
+    # a decode step's write for a large batch: every token alone at a random row of a block
+    # of its own; one call (the large-write kernel, its rows split over several workgroups
+    # per chunk) against calls of 500 tokens (the per-token kernel)
+    for kv in ("bf16", "fp8"):
+        scale = 0.05 if kv == "fp8" else 1.0
+        elem = 2 if kv == "bf16" else 1
+        for T in (1024, 4096, 16384):
+            desc = pkv.cache_desc(T + 1, H, B, D, kv, scale, scale)
+            kp, vp = pkv.alloc_pools(desc, poison=False)
+            k = torch.randn(T, H, D, device="cuda").to(torch.bfloat16)
+            v = torch.randn(T, H, D, device="cuda").to(torch.bfloat16)
+            sl = rng.permutation(T + 1)[:T] * B + rng.integers(0, B, T)
+            slots = torch.from_numpy(sl.astype(np.int64)).cuda()
+
+            def calls():
+                for a in range(0, T, 500):
+                    pkv.reshape_and_cache(k[a:a + 500], v[a:a + 500], slots[a:a + 500], kp, vp,
+                                          desc)
+            one = timed(lambda: pkv.reshape_and_cache(k, v, slots, kp, vp, desc))
+            split = timed(calls)
+            nbytes = T * H * D * (2 + elem) * 2
+            rows.append({"op": "reshape_and_cache", "kv_dtype": kv, "tokens": T,
+                         "layout": "decode batch (one token per block)", "bytes": nbytes,
+                         "us": round(one * 1e6, 1), "us_calls_of_500": round(split * 1e6, 1),
+                         "GBps": round(nbytes / one / 1e9, 1)})
+            del kp, vp, k, v
     # a plain device copy of the bf16 write's bytes (half read, half written)
     src = torch.empty(tokens * H * D * 2 * 2, dtype=torch.uint8, device="cuda")
     src.fill_(1)

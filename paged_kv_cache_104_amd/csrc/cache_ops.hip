@@ -165,8 +165,13 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(
 // shares its block, so that the parts of a line meet in L2, and streamed when it is alone
 // in its block (a decode step's token, whose partial lines would otherwise sit dirty in L2
 // when the decode reads that block).
+// A call of few chunks (a large decode batch: single tokens, each alone in its block)
+// splits each chunk's rows over several workgroups (blockIdx.y), up to kRunsTargetGroups
+// workgroups in all and at least kRunsThreads value rows each; a prefill has enough chunks
+// for one workgroup per chunk.
 constexpr int kRunsThreads = 256;
 constexpr int64_t kRunsMinTokens = 512;    // fewer: the per-token kernel (decode steps)
+constexpr int64_t kRunsTargetGroups = 2048;
 
 template <typename T>
 __device__ __forceinline__ uint32_t storage_bits(T x) {
@@ -276,9 +281,14 @@ __global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
     }
   }
   __syncthreads();
+  // this workgroup's share of the chunk's rows (blockIdx.y of gridDim.y): key segments
+  // [k_lo, k_hi) of every token and value rows [v_lo, v_hi)
+  const int parts = gridDim.y, part = blockIdx.y;
+  const int segs = n / 8, k_lo = segs * part / parts, k_hi = segs * (part + 1) / parts;
+  const int v_lo = n * part / parts, v_hi = n * (part + 1) / parts;
   // keys: every token of the chunk
-  for (int e = tid; e < n_tok * (n / 8); e += kRunsThreads) {
-    const int j = e / (n / 8), ch = e - j * (n / 8);
+  for (int e = tid; e < n_tok * (k_hi - k_lo); e += kRunsThreads) {
+    const int j = e / (k_hi - k_lo), ch = k_lo + (e - j * (k_hi - k_lo));
     const int64_t blk = s_blk[j + 1];
     if (blk < 0) continue;
     const int h = (ch * 8) / D, d0 = ch * 8 - h * D;
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
   if (whole >= 0) {
     const int64_t s0 = i0 + whole;
     T* const tile = v_pool + s_blk[whole + 1] * n * int64_t(B);
-    for (int e = tid; e < n; e += kRunsThreads) {
+    for (int e = v_lo + tid; e < v_hi; e += kRunsThreads) {
       In raw[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) raw[j] = v[(s0 + j) * n + e];
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kRunsThreads) void reshape_and_cache_runs_kernel(
     const uint32_t pm = uint32_t(part_mask >> (half * B)), am = uint32_t(alone_mask >> (half * B));
     if (pm == 0) continue;
     const int j0 = half * B;
-    for (int e = tid; e < n; e += kRunsThreads) {
+    for (int e = v_lo + tid; e < v_hi; e += kRunsThreads) {
       In raw[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) raw[j] = (pm >> j) & 1u ? v[(i0 + j0 + j) * n + e] : In(0);
@@ -401,10 +411,12 @@ static int launch_runs(const In* k, const In* v, const int64_t* slots,
                        hipStream_t s) {
   const int64_t chunks = (num_tokens + c->block_size - 1) / c->block_size;
   if (chunks > 0x7fffffff) return fail(PKV_E_INVAL, "too many tokens for one call");
-  const dim3 grid(static_cast<unsigned>(chunks)), block(kRunsThreads);
+  const int H = c->num_kv_heads, D = c->head_dim;
+  const int64_t parts = std::max<int64_t>(
+      1, std::min<int64_t>((kRunsTargetGroups + chunks - 1) / chunks, int64_t(H) * D / kRunsThreads));
+  const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(parts)), block(kRunsThreads);
   const double ks = inv_scale(KV == KV_FP8 ? c->k_scale : 1.f),
                vs = inv_scale(KV == KV_FP8 ? c->v_scale : 1.f);
-  const int H = c->num_kv_heads, D = c->head_dim;
   switch (c->block_size) {
     case 8:
       reshape_and_cache_runs_kernel<KV, In, 8><<<grid, block, 0, s>>>(

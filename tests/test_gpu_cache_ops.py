@@ -205,7 +205,8 @@ def _large_write_slots(pattern, T, B, N, rng):
     end to end, each in its own randomly placed blocks, so chunks of B tokens straddle
     sequences), ``continued`` (the same, each sequence starting at a random row of its
     first block, as a prompt does after a cached prefix, with some tokens skipped),
-    ``scattered`` (distinct random slots, some negative or past the pool), ``aligned``
+    ``scattered`` (distinct random slots, some negative or past the pool), ``singles`` (a
+    decode batch: each token alone at a random row of a block of its own), ``aligned``
     (one prompt starting at a block's first slot) or ``mixed`` (a batch that mixes prompt
     chunks, some starting within a block, with single decode tokens each at a random row of
     a block of its own)."""
@@ -213,6 +214,8 @@ def _large_write_slots(pattern, T, B, N, rng):
     if pattern == "aligned":
         t = np.arange(T)
         return blocks[t // B] * B + t % B
+    if pattern == "singles":        # a decode batch: each token alone in a block of its own
+        return (blocks[:T] * B + rng.integers(0, B, T)).astype(np.int64)
     if pattern == "scattered":
         s = rng.permutation(N * B)[:T].astype(np.int64)
         s[rng.random(T) < 0.05] = -1
@@ -237,9 +240,10 @@ def _large_write_slots(pattern, T, B, N, rng):
     return s
 
 
-LARGE = [(kv, inp, B, D, H) for kv, inp in (("bf16", "bf16"), ("fp8", "bf16"), ("fp8", "f32"),
-                                            ("f32", "f32"))
-         for B in (8, 16, 32) for D, H in ((64, 3), (128, 2))]
+_IO = (("bf16", "bf16"), ("fp8", "bf16"), ("fp8", "f32"), ("f32", "f32"))
+# 8 heads of 128: a chunk's rows split over several workgroups when the call has few chunks
+LARGE = [(kv, inp, B, D, H) for kv, inp in _IO for B in (8, 16, 32) for D, H in ((64, 3), (128, 2))] \
+    + [(kv, inp, 16, 128, 8) for kv, inp in _IO]
 
 
 @pytest.mark.parametrize("case", LARGE, ids=lambda c: f"{c[0]}-{c[1]}-B{c[2]}-D{c[3]}-H{c[4]}")
@@ -248,18 +252,18 @@ def test_large_writes_bitexact(case):
     tokens, whole value rows for a run of tokens that fills a block in order, single
     elements otherwise) leave both pools bit-identical to the oracle's cache write, for
     prompts laid end to end (starting at a block's first row or within a block), prompts
-    mixed with single decode tokens, one aligned prompt and scattered slots with skipped
-    ones."""
+    mixed with single decode tokens, one aligned prompt, scattered slots with skipped ones
+    and a decode batch of single tokens."""
     import paged_kv_cache_104_amd as pkv
 
     torch = torch_mod()
     kv, inp, B, D, H = case
     rng = np.random.default_rng(B * 1000 + D * 10 + H)
     T = (2600 if D == 128 else 700) + int(rng.integers(0, 40))   # both above the per-token path
-    N = int(1.3 * T / B) + 64
+    N = T + 64                     # room for a block per token (the decode-batch pattern)
     scale = 0.02 if kv == "fp8" else 1.0
     desc = pkv.cache_desc(N, H, B, D, kv, scale, scale)
-    for pattern in ("prompts", "continued", "mixed", "aligned", "scattered"):
+    for pattern in ("prompts", "continued", "mixed", "aligned", "scattered", "singles"):
         print(f"large write {case} {pattern} T={T}", flush=True)
         slots = _large_write_slots(pattern, T, B, N, rng)
         x = rng.standard_normal((2, T, H, D)).astype(np.float32)
