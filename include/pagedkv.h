@@ -85,10 +85,12 @@ typedef struct {
  *   k_pool/v_pool device pools described by *c
  * Slots of one call must be distinct (two writes to one slot race).
  * Bytes of the pools outside the written slots are unchanged.  A call of 512
- * tokens or more (a prefill) runs a kernel that writes whole rows of the value
- * tile wherever B consecutive tokens fill a block in order, wherever in the
- * call they stand (so prompts may be laid end to end at any lengths); the
- * pools end the same either way.
+ * tokens or more runs a kernel that writes whole rows of the value tile
+ * wherever B consecutive tokens fill a block in order, wherever in the call
+ * they stand (a prefill's prompts may be laid end to end at any lengths), and
+ * single elements elsewhere (a large decode batch's tokens); fewer tokens go
+ * through a kernel of one workgroup per token.  The pools end the same either
+ * way.
  */
 int pkv_reshape_and_cache(const void* k, const void* v, int32_t in_dtype,
                           const int64_t* slot_mapping, int64_t num_tokens,
