@@ -254,33 +254,69 @@ def test_large_writes_bitexact(case):
     prompts laid end to end (starting at a block's first row or within a block), prompts
     mixed with single decode tokens, one aligned prompt, scattered slots with skipped ones
     and a decode batch of single tokens."""
-    import paged_kv_cache_104_amd as pkv
-
-    torch = torch_mod()
     kv, inp, B, D, H = case
     rng = np.random.default_rng(B * 1000 + D * 10 + H)
     T = (2600 if D == 128 else 700) + int(rng.integers(0, 40))   # both above the per-token path
     N = T + 64                     # room for a block per token (the decode-batch pattern)
+    for pattern in _PATTERNS:
+        _check_large_write(kv, inp, B, D, H, T, N, pattern, rng)
+
+
+def _check_large_write(kv, inp, B, D, H, T, N, pattern, rng):
+    """One reshape_and_cache call of T tokens in the given slot layout into a pool of N blocks,
+    both pools compared bit for bit with the oracle's cache write."""
+    import paged_kv_cache_104_amd as pkv
+
+    torch = torch_mod()
     scale = 0.02 if kv == "fp8" else 1.0
     desc = pkv.cache_desc(N, H, B, D, kv, scale, scale)
-    for pattern in ("prompts", "continued", "mixed", "aligned", "scattered", "singles"):
-        print(f"large write {case} {pattern} T={T}", flush=True)
-        slots = _large_write_slots(pattern, T, B, N, rng)
-        x = rng.standard_normal((2, T, H, D)).astype(np.float32)
-        if inp == "bf16":
-            xt = torch.from_numpy(x).to(torch.bfloat16)
-            bits = xt.view(torch.int16).numpy().view(np.uint16)
-            kin, vin = bits[0], bits[1]
-            kd, vd = xt[0].contiguous().cuda(), xt[1].contiguous().cuda()
-        else:
-            kin, vin = x[0], x[1]
-            kd, vd = torch.from_numpy(x[0]).cuda(), torch.from_numpy(x[1]).cuda()
-        kp, vp = pkv.alloc_pools(desc)
-        pkv.reshape_and_cache(kd, vd, torch.from_numpy(slots).cuda(), kp, vp, desc)
-        ok, ov = ocache.new_pools(N, H, B, D, kv)
-        ocache.reshape_and_cache(ok, ov, kin, vin, np.where(slots < N * B, slots, -1), inp, kv,
-                                 scale, scale)
-        gk = kp.view(torch.int16).cpu().numpy().view(np.uint16) if kv == "bf16" else kp.cpu().numpy()
-        gv = vp.view(torch.int16).cpu().numpy().view(np.uint16) if kv == "bf16" else vp.cpu().numpy()
-        assert pools_equal_bits(gk, ok), pattern
-        assert pools_equal_bits(gv, ov), pattern
+    print(f"large write {kv}/{inp} B={B} D={D} H={H} {pattern} T={T} N={N}", flush=True)
+    slots = _large_write_slots(pattern, T, B, N, rng)
+    x = rng.standard_normal((2, T, H, D)).astype(np.float32)
+    if inp == "bf16":
+        xt = torch.from_numpy(x).to(torch.bfloat16)
+        bits = xt.view(torch.int16).numpy().view(np.uint16)
+        kin, vin = bits[0], bits[1]
+        kd, vd = xt[0].contiguous().cuda(), xt[1].contiguous().cuda()
+    else:
+        kin, vin = x[0], x[1]
+        kd, vd = torch.from_numpy(x[0]).cuda(), torch.from_numpy(x[1]).cuda()
+    kp, vp = pkv.alloc_pools(desc)
+    pkv.reshape_and_cache(kd, vd, torch.from_numpy(slots).cuda(), kp, vp, desc)
+    ok, ov = ocache.new_pools(N, H, B, D, kv)
+    ocache.reshape_and_cache(ok, ov, kin, vin, np.where(slots < N * B, slots, -1), inp, kv,
+                             scale, scale)
+    gk = kp.view(torch.int16).cpu().numpy().view(np.uint16) if kv == "bf16" else kp.cpu().numpy()
+    gv = vp.view(torch.int16).cpu().numpy().view(np.uint16) if kv == "bf16" else vp.cpu().numpy()
+    assert pools_equal_bits(gk, ok), pattern
+    assert pools_equal_bits(gv, ov), pattern
+
+
+_PATTERNS = ("prompts", "continued", "mixed", "aligned", "scattered", "singles")
+
+
+def _draw_large(i):
+    """A random large write: pool and input dtypes, block size, head size, heads (at most
+    1024 elements per token), token count above the per-token path and slot layout."""
+    r = np.random.default_rng(9100 + i)
+    while True:
+        kv, inp = _IO[int(r.integers(0, len(_IO)))]
+        B, D = int(r.choice([8, 16, 32])), int(r.choice([64, 128]))
+        H = int(r.choice([1, 2, 3, 4, 8, 16]))
+        if H * D <= 1024:
+            break
+    T = int(r.integers(512, 2000))
+    pattern = _PATTERNS[int(r.integers(0, len(_PATTERNS)))]
+    N = T + 64 if pattern == "singles" else int(1.3 * T / B) + 64
+    return kv, inp, B, D, H, T, N, pattern, 9200 + i
+
+
+RANDOM_LARGE = [_draw_large(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", RANDOM_LARGE, ids=lambda c: f"s{c[8]}")
+def test_large_writes_random(case):
+    """A seeded random sweep of large writes (shapes where a chunk's rows split over one to
+    four workgroups, every slot layout) bit-identical to the oracle's cache write."""
+    kv, inp, B, D, H, T, N, pattern, seed = case
+    _check_large_write(kv, inp, B, D, H, T, N, pattern, np.random.default_rng(seed))
